@@ -1,0 +1,197 @@
+// C ABI of the QLoRA NF4 library: argument checks, workspace sizing and
+// dispatch to the HIP kernels. Every check runs on the host before anything
+// is launched; a failed check launches nothing.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/qlora_nf4.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return QLORA_OK;
+}
+
+int hip_status(hipError_t e, const char *where) {
+  if (e == hipSuccess) return ok();
+  return fail(QLORA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+int check_weight(const qlora_nf4_weight *w, const char *fn) {
+  if (!w) return fail(QLORA_ERR_NULL, "%s: weight struct is NULL", fn);
+  if (w->rows <= 0 || w->cols <= 0 || w->rows > kMaxElems / w->cols)
+    return fail(QLORA_ERR_SHAPE, "%s: invalid weight shape %lld x %lld", fn,
+                static_cast<long long>(w->rows), static_cast<long long>(w->cols));
+  if (!w->codes || !w->absmax_q || !w->dq_scale || !w->dq_mean)
+    return fail(QLORA_ERR_NULL, "%s: a weight buffer is NULL", fn);
+  if (!aligned16(w->codes) || !aligned16(w->absmax_q) || !aligned16(w->dq_scale) ||
+      !aligned16(w->dq_mean))
+    return fail(QLORA_ERR_ALIGN, "%s: weight buffers must be 16-byte aligned", fn);
+  return QLORA_OK;
+}
+
+int check_linear_common(const char *fn, int64_t M, const qlora_nf4_weight *W, const float *A,
+                        const float *B, int32_t r) {
+  int st = check_weight(W, fn);
+  if (st != QLORA_OK) return st;
+  if (M <= 0 || M > kMaxElems / W->cols || M > kMaxElems / W->rows)
+    return fail(QLORA_ERR_SHAPE, "%s: invalid M = %lld", fn, static_cast<long long>(M));
+  if (W->cols % QLORA_NF4_BLOCK != 0 || W->rows % QLORA_NF4_BLOCK != 0)
+    return fail(QLORA_ERR_SHAPE,
+                "%s: N (%lld) and K (%lld) must be multiples of 64", fn,
+                static_cast<long long>(W->rows), static_cast<long long>(W->cols));
+  if (r < 0 || r > 256) return fail(QLORA_ERR_SHAPE, "%s: r = %d out of [0, 256]", fn, r);
+  if (r > 0 && (!A || !B)) return fail(QLORA_ERR_NULL, "%s: r > 0 needs A and B", fn);
+  if (r == 0 && (A || B)) return fail(QLORA_ERR_SHAPE, "%s: r = 0 needs A = B = NULL", fn);
+  if ((A && !aligned16(A)) || (B && !aligned16(B)))
+    return fail(QLORA_ERR_ALIGN, "%s: A and B must be 16-byte aligned", fn);
+  return QLORA_OK;
+}
+
+qnf4::LinearArgs make_args(int64_t M, const qlora_nf4_weight *W, int32_t r, float scale) {
+  qnf4::LinearArgs a;
+  a.M = M;
+  a.N = W->rows;
+  a.K = W->cols;
+  a.r = r;
+  a.scale = scale;
+  a.codes = W->codes;
+  a.absmax_q = W->absmax_q;
+  a.dq_scale = W->dq_scale;
+  a.dq_mean = W->dq_mean;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qlora_nf4_storage_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || rows > kMaxElems / cols) return 0;
+  const int64_t n = rows * cols;
+  const int64_t nb = qnf4::ceil_div(n, QLORA_NF4_BLOCK);
+  const int64_t nd = qnf4::ceil_div(nb, QLORA_DQ_BLOCK);
+  return static_cast<size_t>((n + 1) / 2 + nb + 4 * nd + 4);
+}
+
+int qlora_nf4_codebook(float *out) {
+  if (!out) return fail(QLORA_ERR_NULL, "qlora_nf4_codebook: out is NULL");
+  const qnf4::Nf4Tables &t = qnf4::nf4_tables();
+  std::memcpy(out, t.lv, sizeof(t.lv));
+  return ok();
+}
+
+size_t qlora_nf4_quantize_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || rows > kMaxElems / cols) return 0;
+  return qnf4::quantize_ws_bytes(rows * cols);
+}
+
+int qlora_nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols,
+                       const qlora_nf4_weight *out, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "qlora_nf4_quantize";
+  if (!W) return fail(QLORA_ERR_NULL, "%s: W is NULL", fn);
+  if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16)
+    return fail(QLORA_ERR_DTYPE, "%s: w_dtype %d is not QLORA_F32 or QLORA_BF16", fn, w_dtype);
+  int st = check_weight(out, fn);
+  if (st != QLORA_OK) return st;
+  if (out->rows != rows || out->cols != cols)
+    return fail(QLORA_ERR_SHAPE, "%s: out is %lld x %lld but W is %lld x %lld", fn,
+                static_cast<long long>(out->rows), static_cast<long long>(out->cols),
+                static_cast<long long>(rows), static_cast<long long>(cols));
+  if (!aligned16(W)) return fail(QLORA_ERR_ALIGN, "%s: W must be 16-byte aligned", fn);
+  const size_t need = qnf4::quantize_ws_bytes(rows * cols);
+  if (!ws || ws_bytes < need)
+    return fail(QLORA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need,
+                ws ? ws_bytes : size_t(0));
+  if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  hipError_t e = qnf4::launch_quantize(W, w_dtype == QLORA_BF16, rows * cols, out->codes,
+                                       out->absmax_q, out->dq_scale, out->dq_mean, ws,
+                                       static_cast<hipStream_t>(stream));
+  return hip_status(e, fn);
+}
+
+int qlora_nf4_dequantize(const qlora_nf4_weight *q, void *out, int out_dtype, void *stream) {
+  const char *fn = "qlora_nf4_dequantize";
+  int st = check_weight(q, fn);
+  if (st != QLORA_OK) return st;
+  if (!out) return fail(QLORA_ERR_NULL, "%s: out is NULL", fn);
+  if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16)
+    return fail(QLORA_ERR_DTYPE, "%s: out_dtype %d is not QLORA_F32 or QLORA_BF16", fn, out_dtype);
+  if (!aligned16(out)) return fail(QLORA_ERR_ALIGN, "%s: out must be 16-byte aligned", fn);
+  hipError_t e = qnf4::launch_dequantize(q->codes, q->absmax_q, q->dq_scale, q->dq_mean,
+                                         q->rows * q->cols, out, out_dtype == QLORA_BF16,
+                                         static_cast<hipStream_t>(stream));
+  return hip_status(e, fn);
+}
+
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > 256) return 0;
+  if (N % QLORA_NF4_BLOCK || K % QLORA_NF4_BLOCK) return 0;
+  if (N > kMaxElems / K || M > kMaxElems / K || M > kMaxElems / N) return 0;
+  return qnf4::linear_ws_bytes(M, N, K, r);
+}
+
+int qlora_linear_fwd(const void *X, int64_t M, const qlora_nf4_weight *W, const float *A,
+                     const float *B, int32_t r, float scale, void *Y, void *ws, size_t ws_bytes,
+                     void *stream) {
+  const char *fn = "qlora_linear_fwd";
+  if (!X || !Y) return fail(QLORA_ERR_NULL, "%s: X and Y must not be NULL", fn);
+  int st = check_linear_common(fn, M, W, A, B, r);
+  if (st != QLORA_OK) return st;
+  if (!aligned16(X) || !aligned16(Y))
+    return fail(QLORA_ERR_ALIGN, "%s: X and Y must be 16-byte aligned", fn);
+  const size_t need = qnf4::linear_ws_bytes(M, W->rows, W->cols, r);
+  if (!ws || ws_bytes < need)
+    return fail(QLORA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need,
+                ws ? ws_bytes : size_t(0));
+  if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  hipError_t e = qnf4::linear_fwd(make_args(M, W, r, scale), X, A, B, Y, ws,
+                                  static_cast<hipStream_t>(stream));
+  return hip_status(e, fn);
+}
+
+int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qlora_nf4_weight *W,
+                     const float *A, const float *B, int32_t r, float scale, void *dX, float *dA,
+                     float *dB, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "qlora_linear_bwd";
+  if (!dY || !X || !dX) return fail(QLORA_ERR_NULL, "%s: dY, X and dX must not be NULL", fn);
+  int st = check_linear_common(fn, M, W, A, B, r);
+  if (st != QLORA_OK) return st;
+  if (r > 0 && (!dA || !dB)) return fail(QLORA_ERR_NULL, "%s: r > 0 needs dA and dB", fn);
+  if (r == 0 && (dA || dB)) return fail(QLORA_ERR_SHAPE, "%s: r = 0 needs dA = dB = NULL", fn);
+  if (!aligned16(dY) || !aligned16(X) || !aligned16(dX) || (dA && !aligned16(dA)) ||
+      (dB && !aligned16(dB)))
+    return fail(QLORA_ERR_ALIGN, "%s: tensors must be 16-byte aligned", fn);
+  const size_t need = qnf4::linear_ws_bytes(M, W->rows, W->cols, r);
+  if (!ws || ws_bytes < need)
+    return fail(QLORA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need,
+                ws ? ws_bytes : size_t(0));
+  if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  hipError_t e = qnf4::linear_bwd(make_args(M, W, r, scale), dY, X, A, B, dX, dA, dB, ws,
+                                  static_cast<hipStream_t>(stream));
+  return hip_status(e, fn);
+}
+
+const char *qlora_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

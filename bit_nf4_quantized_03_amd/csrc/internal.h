@@ -1,0 +1,64 @@
+// Private declarations shared by the C-ABI layer (api.cpp) and the kernel
+// translation units. Nothing here is part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+#include <cstddef>
+
+namespace qnf4 {
+
+constexpr int kBlock = 64;     // weight elements per absmax constant
+constexpr int kDqBlock = 256;  // absmax constants per double-quantization block
+
+// The NF4 levels and the 15 decision thresholds, passed by value to kernels.
+// thr[i] is the largest fp32 <= the exact midpoint (lv[i] + lv[i+1]) / 2, so
+// for any fp32 y: y > thr[i]  <=>  y is nearer to lv[i+1] than to lv[i] (a tie
+// goes to the lower level).
+struct Nf4Tables {
+  float lv[16];
+  float thr[15];
+};
+
+// Derived once on the host (normal quantiles in long double, rounded once to
+// fp32). Thread-safe.
+const Nf4Tables &nf4_tables();
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- quantize
+// Workspace: fp32 absmax [nb] | fp64 tree partial sums, one level after
+// another (nd + ceil(nd/256) + ... entries).
+size_t quantize_ws_bytes(int64_t n);
+hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, uint8_t *codes,
+                           int8_t *absmax_q, float *dq_scale, float *dq_mean,
+                           void *ws, hipStream_t s);
+
+// -------------------------------------------------------------- dequantize
+hipError_t launch_dequantize(const uint8_t *codes, const int8_t *absmax_q,
+                             const float *dq_scale, const float *dq_mean, int64_t n,
+                             void *out, bool out_bf16, hipStream_t s);
+// Per-block scales c_b (fp32 [nb]) of the reconstruction, for the GEMM kernels.
+hipError_t launch_block_scales(const int8_t *absmax_q, const float *dq_scale,
+                               const float *dq_mean, int64_t nb, float *cs, hipStream_t s);
+
+// ------------------------------------------------------------------ linear
+struct LinearArgs {
+  int64_t M, N, K;
+  int r;
+  float scale;
+  const uint8_t *codes;
+  const int8_t *absmax_q;
+  const float *dq_scale;
+  const float *dq_mean;
+};
+
+size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int r);
+hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const float *B,
+                      void *Y, void *ws, hipStream_t s);
+hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const float *A,
+                      const float *B, void *dX, float *dA, float *dB, void *ws,
+                      hipStream_t s);
+
+}  // namespace qnf4

@@ -1,0 +1,175 @@
+/*
+ * qlora_nf4.h - C ABI of the QLoRA NF4 hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The library implements, as hand-written HIP kernels, the data-parallel hot
+ * path of QLoRA:
+ *   - block-wise NF4 quantization of a frozen base weight with absmax scaling
+ *     (QLoRA vs ChatGPT page, capability "NF4 4-bit quantization"; the NF4
+ *     type has an exact zero and uses all 16 values: ai-papercheck review of
+ *     the QLoRA paper, finding on paper p.5 Section 3),
+ *   - double quantization of the absmax constants to 8 bits with their own
+ *     scales (QLoRA vs ChatGPT page, capability "double quantization";
+ *     Guanaco topic page, "Core Architecture & Training"),
+ *   - dequantization, block by block,
+ *   - the QLoRA linear layer: on-the-fly NF4 dequantization of the frozen
+ *     base plus a full-precision low-rank adapter, forward and backward, with
+ *     gradients only for the adapter and the input (QLoRA vs ChatGPT page,
+ *     capability rows "LoRA on the quantized base" and "training pipeline").
+ *
+ * Conventions shared by every entry point
+ *   Layout      Row-major, contiguous, no strides. W is [rows = N, cols = K]
+ *               (out_features x in_features); X is [M, K]; Y and dY are
+ *               [M, N]; A is [r, K]; B is [N, r].
+ *   Pointers    Every tensor pointer is a DEVICE pointer owned by the caller.
+ *               The qlora_nf4_weight struct itself lives in host memory; its
+ *               members are device pointers. Device pointers must be 16-byte
+ *               aligned (any hipMalloc / torch allocation is).
+ *   Memory      The library allocates nothing. Scratch space is a caller-owned
+ *               device workspace sized by the *_workspace_bytes queries.
+ *   Streams     `stream` is a hipStream_t passed as void* (NULL = the default
+ *               stream). Calls only enqueue work; no host synchronization.
+ *   Outputs     Overwritten, never accumulated.
+ *   Errors      Arguments are checked on the host before anything is
+ *               launched; a failed check returns a negative qlora_status and
+ *               launches nothing. A failed launch returns QLORA_ERR_HIP.
+ *               qlora_last_error() gives a message for the calling thread.
+ *   Finiteness  Inputs must be finite; NaN/Inf are not checked on the GPU.
+ *   Threads     Entry points are thread-safe; calls on one stream run in
+ *               order.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLORA_NF4_BLOCK 64   /* weight elements per absmax constant          */
+#define QLORA_DQ_BLOCK 256   /* absmax constants per double-quantization block */
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = -1,       /* a required pointer is NULL                    */
+  QLORA_ERR_SHAPE = -2,      /* a size is out of range or inconsistent        */
+  QLORA_ERR_DTYPE = -3,      /* dtype outside qlora_dtype or not allowed here */
+  QLORA_ERR_WORKSPACE = -4,  /* workspace NULL or smaller than required       */
+  QLORA_ERR_HIP = -5,        /* a HIP call or kernel launch failed            */
+  QLORA_ERR_ALIGN = -6       /* a device pointer is not 16-byte aligned       */
+} qlora_status;
+
+typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
+
+/*
+ * NF4 + double-quantized weight of `rows x cols` elements, n = rows*cols,
+ * flattened row-major. nb = ceil(n/64) blocks, nd = ceil(nb/256) DQ blocks.
+ *   codes     ceil(n/2) bytes; element 2j is the high nibble of byte j,
+ *             element 2j+1 the low nibble; an odd n leaves the last low
+ *             nibble 0. A code is the index of an NF4 level (0..15, ascending;
+ *             7 is the exact 0.0 level).
+ *   absmax_q  nb int8 codes in [-127, 127] of the block absmax constants.
+ *   dq_scale  nd fp32: per DQ block, the largest |absmax - mean|.
+ *   dq_mean   1 fp32 (device): the mean of the nb absmax constants.
+ * Reconstruction of element i in block b = i/64, DQ block d = b/256:
+ *   k_d = fp32(dq_scale[d] / 127); c_b = fp32(fp32(absmax_q[b] * k_d) + mean);
+ *   w_i = fp32(level[code_i] * c_b), all round-to-nearest-even, no FMA.
+ */
+typedef struct {
+  int64_t rows, cols;
+  uint8_t *codes;
+  int8_t *absmax_q;
+  float *dq_scale;
+  float *dq_mean;
+} qlora_nf4_weight;
+
+/* Bytes of the stored format: ceil(n/2) + nb + 4*nd + 4. Returns 0 if
+ * rows or cols <= 0. Host-only, touches no device. */
+size_t qlora_nf4_storage_bytes(int64_t rows, int64_t cols);
+
+/* The library's 16 NF4 levels (fp32, ascending) written to out[16]. The
+ * levels are normal quantiles at equally spaced probabilities with an exact
+ * zero, scaled to [-1, 1] (Guanaco topic page, "Technical Innovations:
+ * NormalFloat4"; QLoRA review, finding on paper p.5 Section 3). Host-only.
+ * Returns QLORA_OK or QLORA_ERR_NULL. */
+int qlora_nf4_codebook(float *out);
+
+/* Workspace bytes needed by qlora_nf4_quantize for this shape (0 if the shape
+ * is invalid). */
+size_t qlora_nf4_quantize_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * Quantize W [rows, cols] (fp32 or bf16, device) to NF4 + DQ into `out`,
+ * whose rows/cols must equal the arguments and whose four buffers must be
+ * allocated by the caller with the sizes given above.
+ * Blocks of 64 consecutive flattened elements; absmax a_b = max|x|; each
+ * element is coded as the level nearest to fp32(x / a_b) (ties to the lower
+ * level; a zero block gets code 7 and a_b = 0). The constants a_b are then
+ * double-quantized: mean over all nb constants (fp64 binary-tree sum,
+ * adjacent pairs, leaves in index order, zero padded to a power of two, then
+ * fp32(sum/nb)); per 256-block scale s = max|fp32(a - mean)|; code
+ * q = clamp(rint(fp32(fp32((a - mean)/s) * 127)), -127, 127), 0 if s = 0.
+ * (QLoRA vs ChatGPT page, capabilities "NF4 4-bit quantization" and "double
+ * quantization".) Results are bit-identical to that definition.
+ * ws: device workspace of at least qlora_nf4_quantize_workspace_bytes().
+ */
+int qlora_nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols,
+                       const qlora_nf4_weight *out, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/*
+ * Dequantize `q` to out [rows, cols] (device) as fp32 (bit-exact
+ * reconstruction above) or bf16 (round-to-nearest-even of that fp32).
+ * Block-wise dequantization: QLoRA vs ChatGPT page, capability "training
+ * pipeline". No workspace.
+ */
+int qlora_nf4_dequantize(const qlora_nf4_weight *q, void *out, int out_dtype, void *stream);
+
+/* Workspace bytes needed by qlora_linear_fwd and qlora_linear_bwd for these
+ * sizes (the larger of the two; 0 if the sizes are invalid). */
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
+
+/*
+ * QLoRA linear forward (QLoRA vs ChatGPT page, capabilities "LoRA on the
+ * quantized base" and "training pipeline"):
+ *     Y = X W^T + scale * (X A^T) B^T
+ * with W the NF4 + DQ weight [N, K] dequantized block by block on the fly.
+ *   X      bf16 [M, K] (device)
+ *   W      NF4 weight with rows = N, cols = K; K must be a multiple of 64
+ *   A      fp32 [r, K], B fp32 [N, r] (device); r = 0 with A = B = NULL
+ *          means no adapter; 0 <= r <= 256
+ *   scale  the LoRA scale s (alpha / r in the usual convention)
+ *   Y      bf16 [M, N] (device), overwritten
+ * Products run on bf16 matrix cores with fp32 accumulation; A, B and the
+ * adapter activations enter them rounded to bf16. M >= 1.
+ */
+int qlora_linear_fwd(const void *X, int64_t M, const qlora_nf4_weight *W,
+                     const float *A, const float *B, int32_t r, float scale,
+                     void *Y, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * QLoRA linear backward with the base frozen (gradients for the adapter
+ * and the input only; QLoRA vs ChatGPT page, capability "training
+ * pipeline"):
+ *     dH = scale * dY B                  [M, r]
+ *     dX = dY W + dH A                   bf16 [M, K]
+ *     dA = dH^T X                        fp32 [r, K]
+ *     dB = scale * dY^T (X A^T)          fp32 [N, r]
+ * Arguments as in qlora_linear_fwd; dY is bf16 [M, N]. With r = 0, dA and
+ * dB must be NULL and only dX is computed.
+ */
+int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qlora_nf4_weight *W,
+                     const float *A, const float *B, int32_t r, float scale,
+                     void *dX, float *dA, float *dB, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Message for the last non-OK status returned on the calling thread
+ * ("" if none). The pointer stays valid until the thread's next call. */
+const char *qlora_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

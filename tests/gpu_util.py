@@ -1,0 +1,45 @@
+"""Helpers for the GPU parity tests: host <-> device copies of the synthetic
+inputs (bf16 travels as its uint16 bit pattern) and the error measures."""
+import numpy as np
+
+import synth
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def dev_bf16(bits: np.ndarray):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(t.bfloat16).cuda()
+
+
+def dev_f32(x: np.ndarray):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def host_bf16_bits(x) -> np.ndarray:
+    t = torch()
+    return x.detach().contiguous().view(t.int16).cpu().numpy().view(np.uint16)
+
+
+def host_bf16_f32(x) -> np.ndarray:
+    return synth.bf16_to_f32(host_bf16_bits(x))
+
+
+def host(x) -> np.ndarray:
+    return x.detach().cpu().numpy()
+
+
+def rel_fro(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / den) if den > 0 else float(np.linalg.norm(got))
+
+
+def announce(msg: str):
+    """Name the case before a GPU step, flushed, so a crash log shows it."""
+    print(f"[gpu case] {msg}", flush=True)
