@@ -81,7 +81,7 @@ def test_near_threshold_values(qb, cb):
     x[:, 0] = a
     pick = rng.integers(0, 15, size=(nblk, 63))
     target = (thr[pick] * a[:, None].astype(np.float64)).astype(np.float32)
-    steps = rng.integers(-3, 4, size=(nblk, 63))
+    steps = rng.integers(-3, 4, size=(nblk, 63)).astype(np.int32)
     bits = target.view(np.int32) + steps
     x[:, 1:] = bits.view(np.float32)
     x = np.clip(x, -a[:, None], a[:, None]).astype(np.float32)
