@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA NF4 hot path on one MI355X.
+
+One step is one pass of the whole hot path over one batch of the Llama-7B
+attention-projection workload (W 4096 x 4096 bf16 N(0, 0.02), X [4 x 1024
+tokens, 4096] bf16 N(0, 1), dY N(0, 1), LoRA r = 64, alpha = 16, s = 0.25):
+
+    quantize W to NF4 + DQ  ->  dequantize to bf16  ->  fused forward  ->  backward (dX, dA, dB)
+
+Inputs are resident in HBM before the timed region. ``value`` is the
+algorithmic forward + backward flops of the step divided by the step time
+(quantize and dequantize carry no flops but their time counts).
+
+The JSON line also carries
+  roofline      the dominant kernel's achieved rate against the MI355X peak,
+                timed live with HIP events recorded by the library on the
+                launch stream;
+  rows          per-kernel figures of the step (quantize and dequantize in
+                GB/s with buffer rotation past the 256 MB last-level cache);
+  decode        the skinny-M forward (GEMV) at the 7B MLP shapes in GB/s,
+                with rotation over > 512 MB of distinct weights;
+  cpu_baseline  the CPU oracle timed on this host for whole steps of the
+                same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QLoRA linear fwd+bwd TFLOP/s & NF4 dequant/GEMV GB/s vs roofline, 7B/65B"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+ROTATE_BYTES = 640 << 20       # > 2 x (256 MB last-level cache + L2)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources; traffic counters are only reported while
+    the sources they were taken on are unchanged."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_nf4_quantized_03_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the path runs on a single MI355X; see the design notes on sharding).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import bit_nf4_quantized_03_amd as qb
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def d_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def d_f32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+    # ------------------------------------------------------------ workload
+    wl = synth.workload("attn7b")
+    M, N, K, r, s = wl.M, wl.N, wl.K, wl.r, wl.s
+    log(f"workload attn7b M={M} N={N} K={K} r={r} s={s}")
+    W, X, A, B, dY = d_bf16(wl.W), d_bf16(wl.X), d_f32(wl.A), d_f32(wl.B), d_bf16(wl.dY)
+    q = qb.NF4Weight.empty(N, K, dev)
+    ws_q = torch.empty(qb.qlora_nf4_quantize_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+    ws_l = torch.empty(qb.qlora_linear_workspace_bytes(M, N, K, r), dtype=torch.uint8, device=dev)
+    Wdq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dA = torch.empty((r, K), dtype=torch.float32, device=dev)
+    dB = torch.empty((N, r), dtype=torch.float32, device=dev)
+
+    def step():
+        qb.qlora_nf4_quantize(W, out=q, ws=ws_q)
+        qb.qlora_nf4_dequantize(q, torch.bfloat16, out=Wdq)
+        qb.qlora_linear_fwd(X, q, A, B, s, ws=ws_l, out=Y)
+        qb.qlora_linear_bwd(dY, X, q, A, B, s, ws=ws_l, outs=(dX, dA, dB))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    qb.qlora_profile_reset()
+    qb.qlora_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    qb.qlora_profile_enable(False)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    fwd_flops = 2.0 * M * N * K + 2.0 * M * r * (K + N)
+    bwd_flops = 2.0 * M * N * K + 4.0 * M * r * (N + K)
+    value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms -> {value:.1f} TFLOP/s (fwd+bwd algorithmic)")
+
+    kinds = {"fwd_gemm": qb.QLORA_PROF_FWD_GEMM, "bwd_dx_gemm": qb.QLORA_PROF_BWD_DX,
+             "quantize_codes": qb.QLORA_PROF_QUANTIZE, "dequantize": qb.QLORA_PROF_DEQUANTIZE}
+    kt = {}
+    for name, kind in kinds.items():
+        tot, cnt = qb.qlora_profile_read(kind)
+        kt[name] = tot / cnt if cnt else None
+    qb.qlora_profile_reset()
+
+    n = N * K
+    nb, nd = n // 64, n // 64 // 256
+    stored = n // 2 + nb + 4 * nd + 4
+    # Algorithmic work of the two GEMM kernels (the adapter's up projection is
+    # folded into the forward kernel, the dH A term into the dX kernel).
+    fwd_kernel_flops = 2.0 * M * N * (K + r)
+    dx_kernel_flops = 2.0 * M * K * (N + r)
+    rows = {
+        "fwd_gemm": {"us": kt["fwd_gemm"] * 1e3, "flops": fwd_kernel_flops,
+                     "tflops": fwd_kernel_flops / (kt["fwd_gemm"] * 1e-3) / 1e12},
+        "bwd_dx_gemm": {"us": kt["bwd_dx_gemm"] * 1e3, "flops": dx_kernel_flops,
+                        "tflops": dx_kernel_flops / (kt["bwd_dx_gemm"] * 1e-3) / 1e12},
+    }
+    for k in rows:
+        rows[k]["frac_of_bf16_peak"] = rows[k]["tflops"] / BF16_PEAK_TFLOPS
+    dom = max(("fwd_gemm", "bwd_dx_gemm"), key=lambda k: rows[k]["us"])
+
+    # ------------------------------- quantize / dequantize with rotation
+    R = max(2, ROTATE_BYTES // (2 * n + stored))
+    Ws = [W] + [W.clone() for _ in range(R - 1)]
+    qs = [qb.NF4Weight.empty(N, K, dev) for _ in range(R)]
+    outs = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+
+    def timed(fn, reps=3):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(R):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            for i in range(R):
+                fn(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / (reps * R)
+
+    qms = timed(lambda i: qb.qlora_nf4_quantize(Ws[i], out=qs[i], ws=ws_q))
+    dms = timed(lambda i: qb.qlora_nf4_dequantize(qs[i], torch.bfloat16, out=outs[i]))
+    q_bytes = 2 * n + stored
+    d_bytes = stored + 2 * n
+    rows["quantize"] = {"us": qms * 1e3, "bytes": q_bytes, "gbs": q_bytes / (qms * 1e-3) / 1e9}
+    rows["dequantize_bf16"] = {"us": dms * 1e3, "bytes": d_bytes, "gbs": d_bytes / (dms * 1e-3) / 1e9}
+    for k in ("quantize", "dequantize_bf16"):
+        rows[k]["frac_of_hbm_peak"] = rows[k]["gbs"] / HBM_PEAK_GBS
+    rows["quantize"]["rotation"] = R
+    del Ws, qs, outs
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------- decode (skinny M) GEMV
+    decode = {}
+    if not args.no_decode:
+        for name in ("gate7b_m1", "gate7b_m4", "gate7b_m16", "down7b_m1", "down7b_m4", "down7b_m16"):
+            w2 = synth.workload(name)
+            Mx, Nx, Kx = w2.M, w2.N, w2.K
+            st = qb.qlora_nf4_storage_bytes(Nx, Kx)
+            per_set = st + 4 * r * (Kx + Nx)
+            Rd = max(2, ROTATE_BYTES // per_set + 1)
+            Wd = d_bf16(w2.W)
+            qd = [qb.qlora_nf4_quantize(Wd) for _ in range(Rd)]
+            Ad = [d_f32(w2.A) for _ in range(Rd)]
+            Bd = [d_f32(w2.B) for _ in range(Rd)]
+            Xd = d_bf16(w2.X)
+            Yd = torch.empty((Mx, Nx), dtype=torch.bfloat16, device=dev)
+            wsd = torch.empty(qb.qlora_linear_workspace_bytes(Mx, Nx, Kx, r), dtype=torch.uint8, device=dev)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for i in range(Rd):
+                qb.qlora_linear_fwd(Xd, qd[i], Ad[i], Bd[i], w2.s, ws=wsd, out=Yd)
+            torch.cuda.synchronize()
+            reps = 5
+            ev0.record()
+            for _ in range(reps):
+                for i in range(Rd):
+                    qb.qlora_linear_fwd(Xd, qd[i], Ad[i], Bd[i], w2.s, ws=wsd, out=Yd)
+            ev1.record()
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / (reps * Rd)
+            byts = st + 4 * r * (Kx + Nx) + 2 * Mx * Kx + 2 * Mx * Nx
+            decode[name] = {"M": Mx, "N": Nx, "K": Kx, "us": ms * 1e3, "bytes": byts,
+                            "gbs": byts / (ms * 1e-3) / 1e9,
+                            "frac_of_hbm_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                            "rotation": Rd}
+            log(f"decode {name}: {ms * 1e3:.2f} us, {decode[name]['gbs']:.0f} GB/s")
+            del qd, Ad, Bd, Wd
+            torch.cuda.empty_cache()
+
+    # ------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, fwd_flops + bwd_flops, args.cpu_seconds)
+
+    dom_row = rows[dom]
+    roofline = {
+        "kernel": "k_fwd (fused NF4 dequant-GEMM + LoRA fold)" if dom == "fwd_gemm"
+        else "k_bwd_dx (transposed NF4 dequant-GEMM + dH A fold)",
+        "bound": "mfma",
+        "achieved": dom_row["tflops"],
+        "peak": BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": dom_row["tflops"] / BF16_PEAK_TFLOPS,
+        "traffic": load_traffic(dom),
+        "launch_us": dom_row["us"],
+        "flops_per_launch": dom_row["flops"],
+    }
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations and gradients)",
+        "config": {"workload": "Llama-7B attention projection: W 4096x4096 NF4+DQ, "
+                               "X [4x1024 tokens, 4096] bf16, LoRA r=64 alpha=16; step = "
+                               "quantize + dequantize + fused forward + backward",
+                   "M": M, "N": N, "K": K, "r": r, "scale": s,
+                   "step_flops": fwd_flops + bwd_flops},
+        "roofline": roofline,
+        "rows": rows,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, step_flops, seconds):
+    """Time the oracle (as it stands) for whole steps of the same workload on
+    this host: quantize + dequantize (NumPy, one thread) and the fp64
+    forward / backward matmuls (BLAS thread pool)."""
+    import numpy as np
+    import synth
+    from oracle import linear, nf4
+    try:
+        import threadpoolctl
+        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001 - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    cb = nf4.nf4_codebook()
+    w32 = wl.W_f32()
+    X32, dY32 = synth.bf16_to_f32(wl.X), synth.bf16_to_f32(wl.dY)
+    t0 = time.perf_counter()
+    nsteps = 0
+    while True:
+        q = nf4.quantize(w32, cb)
+        What = nf4.dequantize(q, cb)
+        linear.forward(X32, What, wl.A, wl.B, wl.s)
+        linear.backward(dY32, X32, What, wl.A, wl.B, wl.s)
+        nsteps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / nsteps
+    log(f"cpu oracle: {dt:.2f} s per step on {threads} BLAS threads")
+    return {"value": step_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nsteps} whole oracle step(s) of the same workload (quantize, dequantize, "
+                      f"fp64 fwd+bwd at M=4096), {dt:.2f} s per step",
+            "s_per_step": dt}
+
+
+if __name__ == "__main__":
+    main()

@@ -5,7 +5,7 @@ and only marshal arguments: torch supplies device memory (outputs and
 workspaces are allocated with torch on the input's device) and the current
 HIP stream; every step of the computation runs in the library's kernels.
 Importing this package fails loudly if the library has not been built
-(``python -m bit_nf4_quantized_03_amd.build``).
+(``python bit_nf4_quantized_03_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -19,6 +19,7 @@ __all__ = [
     "qlora_nf4_storage_bytes", "qlora_nf4_codebook", "qlora_nf4_quantize_workspace_bytes",
     "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_workspace_bytes",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_last_error", "EXPORTED_SYMBOLS",
+    "qlora_profile_enable", "qlora_profile_read", "qlora_profile_reset",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora_nf4.so")
@@ -30,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "qlora_nf4_storage_bytes", "qlora_nf4_codebook", "qlora_nf4_quantize_workspace_bytes",
     "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_workspace_bytes",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_last_error",
+    "qlora_profile_enable", "qlora_profile_read", "qlora_profile_reset",
 )
 
 
@@ -50,7 +52,7 @@ class _Weight(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m bit_nf4_quantized_03_amd.build`")
+            f"{LIB_PATH} is missing: build it with `python bit_nf4_quantized_03_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
     i64, sz, vp, i32, f32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
     wp = ctypes.POINTER(_Weight)
@@ -64,6 +66,10 @@ def _load():
         "qlora_linear_fwd": (ctypes.c_int, [vp, i64, wp, vp, vp, i32, f32, vp, vp, sz, vp]),
         "qlora_linear_bwd": (ctypes.c_int, [vp, vp, i64, wp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
         "qlora_last_error": (ctypes.c_char_p, []),
+        "qlora_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+        "qlora_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                              ctypes.POINTER(ctypes.c_int64)]),
+        "qlora_profile_reset": (ctypes.c_int, []),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -101,6 +107,28 @@ def qlora_nf4_quantize_workspace_bytes(rows: int, cols: int) -> int:
 
 def qlora_linear_workspace_bytes(M: int, N: int, K: int, r: int) -> int:
     return int(lib.qlora_linear_workspace_bytes(M, N, K, r))
+
+
+QLORA_PROF_FWD_GEMM = 0
+QLORA_PROF_BWD_DX = 1
+QLORA_PROF_QUANTIZE = 2
+QLORA_PROF_DEQUANTIZE = 3
+
+
+def qlora_profile_enable(on: bool = True) -> None:
+    _check("qlora_profile_enable", lib.qlora_profile_enable(1 if on else 0))
+
+
+def qlora_profile_read(kind: int):
+    """(total milliseconds, launches) recorded for ``kind`` since the last reset."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _check("qlora_profile_read", lib.qlora_profile_read(kind, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def qlora_profile_reset() -> None:
+    _check("qlora_profile_reset", lib.qlora_profile_reset())
 
 
 # ---------------------------------------------------------------- torch side

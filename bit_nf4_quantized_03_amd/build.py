@@ -1,6 +1,8 @@
 """Build the HIP library libqlora_nf4.so in-tree with hipcc for gfx950.
 
-Usage: python -m bit_nf4_quantized_03_amd.build   (or call build())
+Usage: python bit_nf4_quantized_03_amd/build.py   (or call build()). It is
+run as a file, not as a package module, because importing the package loads
+the library this script produces.
 
 Every source is compiled with -ffp-contract=off (the quantizer and the
 dequantizer need exact fp32 round-to-nearest steps) and with the packed-fp32
@@ -22,7 +24,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libqlora_nf4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "codebook.cpp", "nf4_quant.hip", "linear.hip"]
+SOURCES = ["api.cpp", "codebook.cpp", "profile.cpp", "nf4_quant.hip", "linear.hip"]
 ARCH = os.environ.get("QLORA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -192,6 +192,23 @@ int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qlora_nf4_w
   return hip_status(e, fn);
 }
 
+int qlora_profile_enable(int on) {
+  qnf4::prof_set(on != 0);
+  return ok();
+}
+
+int qlora_profile_read(int kind, double *total_ms, int64_t *launches) {
+  if (!total_ms || !launches) return fail(QLORA_ERR_NULL, "qlora_profile_read: NULL output");
+  if (kind < 0 || kind >= qnf4::kProfKinds)
+    return fail(QLORA_ERR_SHAPE, "qlora_profile_read: unknown kind %d", kind);
+  return hip_status(qnf4::prof_read(kind, total_ms, launches), "qlora_profile_read");
+}
+
+int qlora_profile_reset(void) {
+  qnf4::prof_reset();
+  return ok();
+}
+
 const char *qlora_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

@@ -24,6 +24,15 @@ struct Nf4Tables {
 // fp32). Thread-safe.
 const Nf4Tables &nf4_tables();
 
+// ------------------------------------------------------------- profiling
+enum ProfKind { kProfFwdGemm = 0, kProfBwdDx = 1, kProfQuantize = 2, kProfDequantize = 3, kProfKinds = 4 };
+bool prof_enabled();
+void prof_set(bool on);
+void prof_begin(int kind, hipStream_t s);
+void prof_end(int kind, hipStream_t s);
+hipError_t prof_read(int kind, double *total_ms, int64_t *count);
+void prof_reset();
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

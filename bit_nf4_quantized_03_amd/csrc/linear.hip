@@ -370,14 +370,18 @@ hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const 
     fp.steps_per_split = pl.dec.steps_per_split;
     if (pl.dec.splits > 1) fp.Y = b.y_part;
     dim3 g(grid_blocks(a.N, CfgDecode::BN), grid_blocks(a.M, CfgDecode::BM), pl.dec.splits);
+    prof_begin(kProfFwdGemm, s);
     hipLaunchKernelGGL(k_fwd<CfgDecode>, g, dim3(CfgDecode::kThreads), 0, s, fp, tab);
+    prof_end(kProfFwdGemm, s);
     if (pl.dec.splits > 1)
       hipLaunchKernelGGL(k_reduce_out, dim3(grid_blocks(a.M * a.N, 256)), dim3(256), 0, s, b.y_part,
                          pl.dec.splits, a.M * a.N, static_cast<__bf16 *>(Y));
   } else {
     fp.steps_per_split = static_cast<int>(a.K / kBK);
     dim3 g(grid_blocks(a.N, CfgBig::BN), grid_blocks(a.M, CfgBig::BM), 1);
+    prof_begin(kProfFwdGemm, s);
     hipLaunchKernelGGL(k_fwd<CfgBig>, g, dim3(CfgBig::kThreads), 0, s, fp, tab);
+    prof_end(kProfFwdGemm, s);
   }
   return hipGetLastError();
 }
@@ -406,7 +410,9 @@ hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const 
   {
     DxParams dp{dY, a.codes, b.cs, b.dHb, b.Atb, dX, a.M, a.N, a.K, pl.rp};
     dim3 g(grid_blocks(a.K, CfgBig::BN), grid_blocks(a.M, CfgBig::BM), 1);
+    prof_begin(kProfBwdDx, s);
     hipLaunchKernelGGL(k_bwd_dx<CfgBig>, g, dim3(CfgBig::kThreads), 0, s, dp, tab);
+    prof_end(kProfBwdDx, s);
   }
   if (pl.rp > 0) {
     // dA [r, K] = dHb^T X

@@ -364,12 +364,14 @@ hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, uint8_t *codes
   double *part = reinterpret_cast<double *>(static_cast<char *>(ws) +
                                             align_up(static_cast<size_t>(nb) * 4, 256));
   const Nf4Tables &tab = nf4_tables();
+  prof_begin(kProfQuantize, s);
   if (w_bf16)
     hipLaunchKernelGGL(k_absmax_codes<true>, dim3(nd), dim3(kThreads), 0, s,
                        static_cast<const uint8_t *>(W), n, codes, absmax_ws, part, nb, tab);
   else
     hipLaunchKernelGGL(k_absmax_codes<false>, dim3(nd), dim3(kThreads), 0, s,
                        static_cast<const uint8_t *>(W), n, codes, absmax_ws, part, nb, tab);
+  prof_end(kProfQuantize, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // Reduce the per-DQ-block partials 256 at a time until one value is left.
@@ -395,12 +397,14 @@ hipError_t launch_dequantize(const uint8_t *codes, const int8_t *absmax_q, const
   const int64_t nd = ceil_div(ceil_div(n, kBlock), kDqBlock);
   const int64_t grid = nd < 8192 ? nd : 8192;
   const Nf4Tables &tab = nf4_tables();
+  prof_begin(kProfDequantize, s);
   if (out_bf16)
     hipLaunchKernelGGL(k_dequant<true>, dim3(grid), dim3(kThreads), 0, s, codes, absmax_q,
                        dq_scale, dq_mean, n, out, tab);
   else
     hipLaunchKernelGGL(k_dequant<false>, dim3(grid), dim3(kThreads), 0, s, codes, absmax_q,
                        dq_scale, dq_mean, n, out, tab);
+  prof_end(kProfDequantize, s);
   return hipGetLastError();
 }
 

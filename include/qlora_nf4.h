@@ -164,6 +164,25 @@ int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qlora_nf4_w
                      void *dX, float *dA, float *dB, void *ws, size_t ws_bytes,
                      void *stream);
 
+/*
+ * Opt-in kernel timing for benchmarks. While enabled, each call records a
+ * pair of HIP events on its stream around its dominant kernel:
+ *   QLORA_PROF_FWD_GEMM     the fused dequant-GEMM of qlora_linear_fwd
+ *   QLORA_PROF_BWD_DX       the transposed dequant-GEMM (dX) of qlora_linear_bwd
+ *   QLORA_PROF_QUANTIZE     the absmax + NF4 code kernel of qlora_nf4_quantize
+ *   QLORA_PROF_DEQUANTIZE   the kernel of qlora_nf4_dequantize
+ * qlora_profile_read waits for the recorded events of `kind` and returns the
+ * summed elapsed milliseconds and the number of launches; qlora_profile_reset
+ * releases them. Not part of the method: instrumentation only.
+ */
+#define QLORA_PROF_FWD_GEMM 0
+#define QLORA_PROF_BWD_DX 1
+#define QLORA_PROF_QUANTIZE 2
+#define QLORA_PROF_DEQUANTIZE 3
+int qlora_profile_enable(int on);
+int qlora_profile_read(int kind, double *total_ms, int64_t *launches);
+int qlora_profile_reset(void);
+
 /* Message for the last non-OK status returned on the calling thread
  * ("" if none). The pointer stays valid until the thread's next call. */
 const char *qlora_last_error(void);

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(qb.EXPORTED_SYMBOLS) == names
