@@ -9,13 +9,15 @@
 // 16-element slice; the 32x32 fp32 result lands in 16 registers per lane,
 // register v holding row 8*(v/4) + 4*(l/32) + (v%4), column l % 32.
 //
-// Loaders turn a 64-wide reduction step of a source tensor into that LDS
-// layout: plain bf16 rows, fp32 rows rounded to bf16, transposed bf16 or
-// fp32 (reduction along the source's rows), and the NF4 + DQ weight decoded on
-// the fly either along its rows (forward: reduction over in_features) or
-// transposed (input gradient: reduction over out_features). Decoding follows
-// the format's reconstruction w = fp32(level[code] * c_b) and rounds w to bf16
-// (round to nearest even) as the matrix-core operand.
+// LDS layout: a tile row is 64 bf16 = 128 bytes = eight 16-byte chunks, with
+// no padding; logical chunk c of row r is stored at chunk c ^ swz(r),
+// swz(r) = (r & 7) ^ ((r >> 3) & 3). The swizzle depends only on r mod 32, so
+// the fragment reads of one wave (rows 32i + l, i = 0..3) differ by immediate
+// offsets. Eight consecutive rows read at one logical chunk (a fragment read),
+// a row written chunk by chunk, and the transposed 8x8 stores (see
+// TransUnits) all land on eight distinct chunk slots per group of eight lanes,
+// so none of them serializes on LDS banks.
+//
 #pragma once
 
 #include "internal.h"
@@ -23,11 +25,16 @@
 namespace qnf4 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 64;          // reduction elements per pipeline step
-constexpr int kLDK = kBK + 8;    // LDS row length in bf16 (padding vs bank conflicts)
+constexpr int kBK = 64;   // reduction elements per pipeline step
+constexpr int kLDK = 64;  // LDS row length in bf16 (swizzled, unpadded)
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 3); }
+// Offset (in bf16 elements) of logical 16-byte chunk `chunk` of tile row `row`.
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * kLDK + ((chunk ^ swz(row)) << 3);
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -69,21 +76,31 @@ struct Acc {
   }
 };
 
-// One 64-deep step of MFMAs from the LDS tiles sA [BM][kLDK], sB [BN][kLDK].
+// Per-lane LDS offsets (bf16 elements) of the four 16-deep fragment slices of
+// a wave's first fragment row; fragment i adds 32 * 64 * i (an immediate).
+template <int WT>
+struct FragAddr {
+  int off[4];
+  __device__ FragAddr(int row0, int lane) {
+    const int r = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) off[kk] = lds_off(row0 + r, 2 * kk + half);
+  }
+};
+
+// One 64-deep step of MFMAs from the LDS tiles sA [BM][64], sB [BN][64].
 template <class Cfg>
 __device__ __forceinline__ void mma_step(Acc<Cfg> &acc, const __bf16 *sA, const __bf16 *sB,
-                                         int wm, int wn, int lane) {
-  const int r = lane & 31;
-  const int koff = (lane >> 5) * 8;
+                                         const FragAddr<Cfg::WTM> &fa, const FragAddr<Cfg::WTN> &fb) {
 #pragma unroll
   for (int kk = 0; kk < kBK / 16; ++kk) {
     bf16x8 a[Cfg::TM], b[Cfg::TN];
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8 *>(sA + (wm * Cfg::WTM + i * 32 + r) * kLDK + kk * 16 + koff);
+      a[i] = *reinterpret_cast<const bf16x8 *>(sA + fa.off[kk] + i * 32 * kLDK);
 #pragma unroll
     for (int j = 0; j < Cfg::TN; ++j)
-      b[j] = *reinterpret_cast<const bf16x8 *>(sB + (wn * Cfg::WTN + j * 32 + r) * kLDK + kk * 16 + koff);
+      b[j] = *reinterpret_cast<const bf16x8 *>(sB + fb.off[kk] + j * 32 * kLDK);
 #pragma unroll
     for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
@@ -93,69 +110,98 @@ __device__ __forceinline__ void mma_step(Acc<Cfg> &acc, const __bf16 *sA, const 
 }
 
 // Pipelined main loop over `steps` reduction steps starting at `red0`, stride
-// 64. LDS is double buffered; one barrier per step. On entry the caller has
+// 64. smem holds the double-buffered tiles [A0 | A1 | B0 | B1]. One barrier
+// per step; the loop is unrolled by two so both buffers are addressed with
+// immediates, and the last step is peeled. On entry the caller has
 // synchronized (LDS free); on exit all LDS reads are complete.
 template <class Cfg, class LA, class LB>
 __device__ __forceinline__ void mainloop(Acc<Cfg> &acc, LA &la, LB &lb, int64_t red0, int steps,
-                                         __bf16 *sA0, __bf16 *sA1, __bf16 *sB0, __bf16 *sB1) {
+                                         __bf16 *smem) {
   if (steps <= 0) return;
+  __bf16 *sA0 = smem, *sA1 = smem + Cfg::kLdsA;
+  __bf16 *sB0 = smem + 2 * Cfg::kLdsA, *sB1 = sB0 + Cfg::kLdsB;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int wm = w / Cfg::WAVES_N, wn = w % Cfg::WAVES_N;
+  const FragAddr<Cfg::WTM> fa(wm * Cfg::WTM, lane);
+  const FragAddr<Cfg::WTN> fb(wn * Cfg::WTN, lane);
   la.load(red0);
   lb.load(red0);
   la.store(sA0);
   lb.store(sB0);
   __syncthreads();
-  for (int s = 0; s < steps; ++s) {
-    __bf16 *cA = (s & 1) ? sA1 : sA0;
-    __bf16 *cB = (s & 1) ? sB1 : sB0;
-    __bf16 *nA = (s & 1) ? sA0 : sA1;
-    __bf16 *nB = (s & 1) ? sB0 : sB1;
-    const bool more = s + 1 < steps;
-    if (more) {
-      la.load(red0 + static_cast<int64_t>(s + 1) * kBK);
-      lb.load(red0 + static_cast<int64_t>(s + 1) * kBK);
-    }
-    mma_step<Cfg>(acc, cA, cB, wm, wn, lane);
-    if (more) {
-      la.store(nA);
-      lb.store(nB);
-    }
+  int s = 0;
+  for (; s + 2 < steps; s += 2) {
+    la.load(red0 + static_cast<int64_t>(s + 1) * kBK);
+    lb.load(red0 + static_cast<int64_t>(s + 1) * kBK);
+    mma_step<Cfg>(acc, sA0, sB0, fa, fb);
+    la.store(sA1);
+    lb.store(sB1);
+    __syncthreads();
+    la.load(red0 + static_cast<int64_t>(s + 2) * kBK);
+    lb.load(red0 + static_cast<int64_t>(s + 2) * kBK);
+    mma_step<Cfg>(acc, sA1, sB1, fa, fb);
+    la.store(sA0);
+    lb.store(sB0);
     __syncthreads();
   }
+  if (s + 1 < steps) {  // two steps left: the last one is in buffer 1
+    la.load(red0 + static_cast<int64_t>(s + 1) * kBK);
+    lb.load(red0 + static_cast<int64_t>(s + 1) * kBK);
+    mma_step<Cfg>(acc, sA0, sB0, fa, fb);
+    la.store(sA1);
+    lb.store(sB1);
+    __syncthreads();
+    mma_step<Cfg>(acc, sA1, sB1, fa, fb);
+  } else {
+    mma_step<Cfg>(acc, sA0, sB0, fa, fb);
+  }
+  __syncthreads();
 }
 
 // ----------------------------------------------------------------- loaders
 // Each loader covers ROWS output rows of one operand and a 64-deep reduction
 // step. load() issues the global reads into registers, store() writes the
-// LDS tile [ROWS][kLDK].
+// LDS tile [ROWS][64].
 
-// bf16 source S[row][t] (t contiguous), row stride ld, rows >= nrows read as 0.
-template <int ROWS, int T>
+// bf16 source S[row][t] (t contiguous), row stride ld, rows >= nrows read as 0
+// (GUARD = false: the caller guarantees every row of the tile exists). The
+// per-lane part of each address is a 32-bit byte offset computed once; a step
+// only moves the uniform base pointer.
+template <int ROWS, int T, bool GUARD = true>
 struct RowBf16 {
   static constexpr int CH = ROWS * 8 / T;
   static_assert(ROWS * 8 % T == 0, "tile/threads mismatch");
-  const __bf16 *src;
-  int64_t ld, nrows, row0;
+  const char *base;
+  uint32_t off[CH];
+  bool ok[CH];
   uint4 reg[CH];
-  __device__ RowBf16(const void *s, int64_t ld_, int64_t nrows_, int64_t row0_)
-      : src(static_cast<const __bf16 *>(s)), ld(ld_), nrows(nrows_), row0(row0_) {}
-  __device__ __forceinline__ void load(int64_t red0) {
+  __device__ RowBf16(const void *s, int64_t ld, int64_t nrows, int64_t row0)
+      : base(static_cast<const char *>(s) + row0 * ld * 2) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int idx = threadIdx.x + i * T;
       const int64_t r = row0 + (idx >> 3);
-      reg[i] = (r < nrows) ? *reinterpret_cast<const uint4 *>(src + r * ld + red0 + (idx & 7) * 8)
-                           : make_uint4(0, 0, 0, 0);
+      ok[i] = !GUARD || r < nrows;
+      const int64_t rc = (!GUARD || r < nrows) ? r : nrows - 1;   // clamped: always safe to read
+      off[i] = static_cast<uint32_t>(((rc - row0) * ld + (idx & 7) * 8) * 2);
+    }
+  }
+  __device__ __forceinline__ void load(int64_t red0) {
+    const char *p = base + red0 * 2;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      uint4 v = *reinterpret_cast<const uint4 *>(p + off[i]);
+      if (GUARD) v = make_uint4(ok[i] ? v.x : 0u, ok[i] ? v.y : 0u, ok[i] ? v.z : 0u, ok[i] ? v.w : 0u);
+      reg[i] = v;
     }
   }
   __device__ __forceinline__ void store(__bf16 *lds) const {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int idx = threadIdx.x + i * T;
-      *reinterpret_cast<uint4 *>(lds + (idx >> 3) * kLDK + (idx & 7) * 8) = reg[i];
+      *reinterpret_cast<uint4 *>(lds + lds_off(idx >> 3, idx & 7)) = reg[i];
     }
   }
 };
@@ -163,56 +209,76 @@ struct RowBf16 {
 // fp32 source S[row][t], row stride ld (multiple of 4), rows >= nrows read as 0.
 template <int ROWS, int T>
 struct RowF32 {
-  static constexpr int CH = ROWS * 16 / T;
-  static_assert(ROWS * 16 % T == 0, "tile/threads mismatch");
+  static constexpr int CH = ROWS * 8 / T;       // 8-element (two float4) chunks
+  static_assert(ROWS * 8 % T == 0, "tile/threads mismatch");
   const float *src;
   int64_t ld, nrows, row0;
-  float4 reg[CH];
+  float4 reg[CH][2];
   __device__ RowF32(const void *s, int64_t ld_, int64_t nrows_, int64_t row0_)
       : src(static_cast<const float *>(s)), ld(ld_), nrows(nrows_), row0(row0_) {}
   __device__ __forceinline__ void load(int64_t red0) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int idx = threadIdx.x + i * T;
-      const int64_t r = row0 + (idx >> 4);
-      reg[i] = (r < nrows) ? *reinterpret_cast<const float4 *>(src + r * ld + red0 + (idx & 15) * 4)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int64_t r = row0 + (idx >> 3);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        reg[i][h] = (r < nrows)
+                        ? *reinterpret_cast<const float4 *>(src + r * ld + red0 + (idx & 7) * 8 + 4 * h)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   __device__ __forceinline__ void store(__bf16 *lds) const {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int idx = threadIdx.x + i * T;
-      uint2 v = make_uint2(pack_bf16x2(reg[i].x, reg[i].y), pack_bf16x2(reg[i].z, reg[i].w));
-      *reinterpret_cast<uint2 *>(lds + (idx >> 4) * kLDK + (idx & 15) * 4) = v;
+      uint4 v = make_uint4(pack_bf16x2(reg[i][0].x, reg[i][0].y), pack_bf16x2(reg[i][0].z, reg[i][0].w),
+                           pack_bf16x2(reg[i][1].x, reg[i][1].y), pack_bf16x2(reg[i][1].z, reg[i][1].w));
+      *reinterpret_cast<uint4 *>(lds + lds_off(idx >> 3, idx & 7)) = v;
     }
   }
 };
 
+// Units of the transposed loaders: 8 reduction rows x 8 output rows. For a
+// tile of ROWS output rows there are UPR = ROWS / 8 column groups cc and 8
+// reduction-row groups rg per 64-deep step. A unit is written as eight 16-byte
+// LDS stores (output rows 8 cc + j, logical chunk rg). Thread t takes cc from
+// bits 0-1 and 3.. of t and rg from bit 2 and the bits above, so each group of
+// eight lanes holds four consecutive cc and two rg four apart: with the
+// swizzle above, its eight stores hit eight distinct chunk slots.
+template <int ROWS, int T>
+struct TransUnits {
+  static constexpr int UPR = ROWS / 8;
+  static constexpr int UNITS = UPR * 8;
+  static constexpr int CH = (UNITS + T - 1) / T;
+  static constexpr int kHiBits = (UPR == 4) ? 0 : (UPR == 8) ? 1 : (UPR == 16) ? 2 : (UPR == 32) ? 3 : 4;
+  static_assert(UPR >= 4 && UPR <= 64 && (UPR & (UPR - 1)) == 0, "unsupported tile height");
+  __device__ static bool active(int idx) { return UNITS % T == 0 || idx < UNITS; }
+  __device__ static int cc(int idx) { return (idx & 3) | (((idx >> 3) & (UPR / 4 - 1)) << 2); }
+  __device__ static int rg(int idx) { return (((idx >> 2) & 1) << 2) | ((idx >> (3 + kHiBits)) & 3); }
+};
+
 // Transposed bf16 source S[t][col] (reduction along the source's rows, cols
-// contiguous, ld multiple of 8): output row = col. Units of 4 reduction rows x
-// 8 columns; reduction rows >= nred and columns >= ncols read as 0 (ncols is
-// a multiple of 8).
+// contiguous, ld and ncols multiples of 8): output row = col. Reduction rows
+// >= nred and columns >= ncols read as 0.
 template <int ROWS, int T>
 struct TransBf16 {
-  static constexpr int UPR = ROWS / 8;           // units per reduction-row group
-  static constexpr int UNITS = 16 * UPR;
-  static constexpr int CH = (UNITS + T - 1) / T;
+  using U = TransUnits<ROWS, T>;
   const __bf16 *src;
   int64_t ld, nred, ncols, col0;
-  uint4 reg[CH][4];
+  uint4 reg[U::CH][8];
   __device__ TransBf16(const void *s, int64_t ld_, int64_t nred_, int64_t ncols_, int64_t col0_)
       : src(static_cast<const __bf16 *>(s)), ld(ld_), nred(nred_), ncols(ncols_), col0(col0_) {}
   __device__ __forceinline__ void load(int64_t red0) {
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {
+    for (int u = 0; u < U::CH; ++u) {
       const int idx = threadIdx.x + u * T;
-      if (UNITS % T != 0 && idx >= UNITS) continue;
-      const int cc = idx % UPR, rg = idx / UPR;
+      if (!U::active(idx)) continue;
+      const int cc = U::cc(idx), rg = U::rg(idx);
       const int64_t c = col0 + cc * 8;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = red0 + rg * 4 + i;
+      for (int i = 0; i < 8; ++i) {
+        const int64_t t = red0 + rg * 8 + i;
         reg[u][i] = (t < nred && c < ncols) ? *reinterpret_cast<const uint4 *>(src + t * ld + c)
                                             : make_uint4(0, 0, 0, 0);
       }
@@ -220,47 +286,49 @@ struct TransBf16 {
   }
   __device__ __forceinline__ void store(__bf16 *lds) const {
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {
+    for (int u = 0; u < U::CH; ++u) {
       const int idx = threadIdx.x + u * T;
-      if (UNITS % T != 0 && idx >= UNITS) continue;
-      const int cc = idx % UPR, rg = idx / UPR;
-      const uint32_t w[4][4] = {{reg[u][0].x, reg[u][0].y, reg[u][0].z, reg[u][0].w},
-                                {reg[u][1].x, reg[u][1].y, reg[u][1].z, reg[u][1].w},
-                                {reg[u][2].x, reg[u][2].y, reg[u][2].z, reg[u][2].w},
-                                {reg[u][3].x, reg[u][3].y, reg[u][3].z, reg[u][3].w}};
+      if (!U::active(idx)) continue;
+      const int cc = U::cc(idx), rg = U::rg(idx);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        // columns 2q (low halves) and 2q+1 (high halves) of the four rows
-        uint2 even = make_uint2(lo16x2(w[0][q], w[1][q]), lo16x2(w[2][q], w[3][q]));
-        uint2 odd = make_uint2(hi16x2(w[0][q], w[1][q]), hi16x2(w[2][q], w[3][q]));
-        *reinterpret_cast<uint2 *>(lds + (cc * 8 + 2 * q) * kLDK + rg * 4) = even;
-        *reinterpret_cast<uint2 *>(lds + (cc * 8 + 2 * q + 1) * kLDK + rg * 4) = odd;
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint4 &v = reg[u][i];
+          w[i] = q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+        }
+        // output rows 2q (low halves) and 2q+1 (high halves), 8 reduction values each
+        uint4 even = make_uint4(lo16x2(w[0], w[1]), lo16x2(w[2], w[3]), lo16x2(w[4], w[5]),
+                                lo16x2(w[6], w[7]));
+        uint4 odd = make_uint4(hi16x2(w[0], w[1]), hi16x2(w[2], w[3]), hi16x2(w[4], w[5]),
+                               hi16x2(w[6], w[7]));
+        *reinterpret_cast<uint4 *>(lds + lds_off(cc * 8 + 2 * q, rg)) = even;
+        *reinterpret_cast<uint4 *>(lds + lds_off(cc * 8 + 2 * q + 1, rg)) = odd;
       }
     }
   }
 };
 
 // Transposed fp32 source S[t][col] with any row stride: scalar loads, rounded
-// to bf16. Units of 4 reduction rows x 8 columns; out-of-range reads as 0.
+// to bf16. Out-of-range elements read as 0.
 template <int ROWS, int T>
 struct TransF32 {
-  static constexpr int UPR = ROWS / 8;
-  static constexpr int UNITS = 16 * UPR;
-  static constexpr int CH = (UNITS + T - 1) / T;
+  using U = TransUnits<ROWS, T>;
   const float *src;
   int64_t ld, nred, ncols, col0;
-  float reg[CH][4][8];
+  float reg[U::CH][8][8];
   __device__ TransF32(const void *s, int64_t ld_, int64_t nred_, int64_t ncols_, int64_t col0_)
       : src(static_cast<const float *>(s)), ld(ld_), nred(nred_), ncols(ncols_), col0(col0_) {}
   __device__ __forceinline__ void load(int64_t red0) {
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {
+    for (int u = 0; u < U::CH; ++u) {
       const int idx = threadIdx.x + u * T;
-      if (UNITS % T != 0 && idx >= UNITS) continue;
-      const int cc = idx % UPR, rg = idx / UPR;
+      if (!U::active(idx)) continue;
+      const int cc = U::cc(idx), rg = U::rg(idx);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = red0 + rg * 4 + i;
+      for (int i = 0; i < 8; ++i) {
+        const int64_t t = red0 + rg * 8 + i;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int64_t c = col0 + cc * 8 + j;
@@ -271,15 +339,15 @@ struct TransF32 {
   }
   __device__ __forceinline__ void store(__bf16 *lds) const {
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {
+    for (int u = 0; u < U::CH; ++u) {
       const int idx = threadIdx.x + u * T;
-      if (UNITS % T != 0 && idx >= UNITS) continue;
-      const int cc = idx % UPR, rg = idx / UPR;
+      if (!U::active(idx)) continue;
+      const int cc = U::cc(idx), rg = U::rg(idx);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        uint2 v = make_uint2(pack_bf16x2(reg[u][0][j], reg[u][1][j]),
-                             pack_bf16x2(reg[u][2][j], reg[u][3][j]));
-        *reinterpret_cast<uint2 *>(lds + (cc * 8 + j) * kLDK + rg * 4) = v;
+        uint4 v = make_uint4(pack_bf16x2(reg[u][0][j], reg[u][1][j]), pack_bf16x2(reg[u][2][j], reg[u][3][j]),
+                             pack_bf16x2(reg[u][4][j], reg[u][5][j]), pack_bf16x2(reg[u][6][j], reg[u][7][j]));
+        *reinterpret_cast<uint4 *>(lds + lds_off(cc * 8 + j, rg)) = v;
       }
     }
   }
@@ -287,33 +355,40 @@ struct TransF32 {
 
 // NF4 + DQ weight W [N][K] decoded along its rows: output row = n, reduction
 // over k. K is a multiple of 64, so a 64-step of one row is exactly one
-// quantization block with scale cs[(n*K + k0)/64]. lv: the 16 levels in LDS.
-template <int ROWS, int T>
+// quantization block with scale cs[(n*K + k0)/64]. lv2: LDS table of the level
+// pairs (level[b >> 4], level[b & 15]) for every code byte b.
+template <int ROWS, int T, bool GUARD = true>
 struct Nf4Row {
   static constexpr int CH = ROWS * 2 / T;       // 16-byte code chunks per thread
   static_assert(ROWS * 2 % T == 0, "tile/threads mismatch");
-  const uint8_t *codes;
-  const float *cs;
-  const float *lv;
-  int64_t N, K, row0;
+  const uint8_t *cbase;
+  const float *sbase;
+  const float2 *lv2;
+  uint32_t coff[CH], soff[CH];
+  bool ok[CH];
   uint4 reg[CH];
   float sc[CH];
-  __device__ Nf4Row(const uint8_t *c, const float *s, const float *lv_, int64_t N_, int64_t K_,
-                    int64_t row0_)
-      : codes(c), cs(s), lv(lv_), N(N_), K(K_), row0(row0_) {}
-  __device__ __forceinline__ void load(int64_t red0) {
+  __device__ Nf4Row(const uint8_t *c, const float *s, const float2 *lv2_, int64_t N, int64_t K,
+                    int64_t row0)
+      : cbase(c + row0 * K / 2), sbase(s + row0 * K / kBlock), lv2(lv2_) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int idx = threadIdx.x + i * T;
       const int64_t n = row0 + (idx >> 1);
-      if (n < N) {
-        const int64_t e = n * K + red0;
-        reg[i] = *reinterpret_cast<const uint4 *>(codes + e / 2 + (idx & 1) * 16);
-        sc[i] = cs[e / kBlock];
-      } else {
-        reg[i] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
-        sc[i] = 0.0f;
-      }
+      ok[i] = !GUARD || n < N;
+      const int64_t nc = (!GUARD || n < N) ? n : N - 1;
+      coff[i] = static_cast<uint32_t>((nc - row0) * K / 2 + (idx & 1) * 16);
+      soff[i] = static_cast<uint32_t>((nc - row0) * K / kBlock);
+    }
+  }
+  __device__ __forceinline__ void load(int64_t red0) {
+    const uint8_t *cp = cbase + red0 / 2;
+    const float *sp = sbase + red0 / kBlock;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      reg[i] = *reinterpret_cast<const uint4 *>(cp + coff[i]);
+      const float c = sp[soff[i]];
+      sc[i] = (!GUARD || ok[i]) ? c : 0.0f;     // rows past the end decode to 0
     }
   }
   __device__ __forceinline__ void store(__bf16 *lds) const {
@@ -321,76 +396,100 @@ struct Nf4Row {
     for (int i = 0; i < CH; ++i) {
       const int idx = threadIdx.x + i * T;
       const uint32_t w[4] = {reg[i].x, reg[i].y, reg[i].z, reg[i].w};
-      __bf16 *dst = lds + (idx >> 1) * kLDK + (idx & 1) * 32;
+      const int row = idx >> 1;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        uint4 o;
         uint32_t ow[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const uint32_t byte = (w[q] >> (8 * b)) & 0xFFu;
-          ow[b] = pack_bf16x2(__fmul_rn(lv[byte >> 4], sc[i]), __fmul_rn(lv[byte & 15u], sc[i]));
+          const float2 pr = lv2[(w[q] >> (8 * b)) & 0xFFu];
+          ow[b] = pack_bf16x2(__fmul_rn(pr.x, sc[i]), __fmul_rn(pr.y, sc[i]));
         }
-        o = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-        *reinterpret_cast<uint4 *>(dst + q * 8) = o;
+        *reinterpret_cast<uint4 *>(lds + lds_off(row, (idx & 1) * 4 + q)) =
+            make_uint4(ow[0], ow[1], ow[2], ow[3]);
       }
     }
   }
 };
 
 // NF4 + DQ weight W [N][K] decoded transposed: output row = k, reduction over
-// n. Units of 4 rows n x 8 columns k (one 32-bit word of codes per row, inside
-// one quantization block). Rows n >= N read as 0.
-template <int ROWS, int T>
+// n (N is a multiple of 64, so every reduction row of a step exists). A unit
+// is 8 rows n x 8 columns k: one 32-bit word of codes per row, inside one
+// quantization block. With twice as many threads as units, the two threads of
+// a unit read the same words and each decodes four of its eight output rows.
+// Columns k >= K decode to 0 (GUARD = false: the tile lies inside K).
+template <int ROWS, int T, bool GUARD = true>
 struct Nf4Trans {
-  static constexpr int UPR = ROWS / 8;
-  static constexpr int UNITS = 16 * UPR;
-  static constexpr int CH = (UNITS + T - 1) / T;
-  const uint8_t *codes;
-  const float *cs;
-  const float *lv;
-  int64_t N, K, col0;
-  uint32_t reg[CH][4];
-  float sc[CH][4];
-  __device__ Nf4Trans(const uint8_t *c, const float *s, const float *lv_, int64_t N_, int64_t K_,
-                      int64_t col0_)
-      : codes(c), cs(s), lv(lv_), N(N_), K(K_), col0(col0_) {}
-  __device__ __forceinline__ void load(int64_t red0) {
+  using U = TransUnits<ROWS, T>;
+  static constexpr bool kSplit = (T == 2 * U::UNITS);
+  static constexpr int CH = kSplit ? 1 : U::CH;
+  static constexpr int JN = kSplit ? 4 : 8;     // output rows decoded per thread and unit
+  const uint8_t *cbase;
+  const float *sbase;
+  const float2 *lv2;
+  int64_t K;
+  uint32_t coff[CH], soff[CH];
+  bool ok[CH];
+  uint32_t reg[CH][8];
+  float sc[CH][8];
+  __device__ __forceinline__ int unit(int u) const {
+    return kSplit ? (threadIdx.x % U::UNITS) : static_cast<int>(threadIdx.x) + u * T;
+  }
+  __device__ Nf4Trans(const uint8_t *c, const float *s, const float2 *lv2_, int64_t N, int64_t K_,
+                      int64_t col0)
+      : cbase(c + col0 / 2), sbase(s + col0 / kBlock), lv2(lv2_), K(K_) {
+    (void)N;
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const int idx = threadIdx.x + u * T;
-      if (UNITS % T != 0 && idx >= UNITS) continue;
-      const int cc = idx % UPR, rg = idx / UPR;
+      const int idx = unit(u);
+      const int cc = U::cc(idx), rg = U::rg(idx);
       const int64_t k = col0 + cc * 8;
+      ok[u] = !GUARD || k < K;
+      const int64_t kc = (!GUARD || k < K) ? k : K - 8;
+      coff[u] = static_cast<uint32_t>((rg * 8) * K / 2 + (kc - col0) / 2);
+      soff[u] = static_cast<uint32_t>((rg * 8) * K / kBlock + (kc - col0) / kBlock);
+    }
+  }
+  __device__ __forceinline__ void load(int64_t red0) {
+    const uint8_t *cp = cbase + red0 * K / 2;
+    const float *sp = sbase + red0 * K / kBlock;
+    const uint32_t rowc = static_cast<uint32_t>(K / 2), rows = static_cast<uint32_t>(K / kBlock);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t n = red0 + rg * 4 + i;
-        if (n < N && k < K) {
-          const int64_t e = n * K + k;
-          reg[u][i] = *reinterpret_cast<const uint32_t *>(codes + e / 2);
-          sc[u][i] = cs[e / kBlock];
-        } else {
-          reg[u][i] = 0x77777777u;
-          sc[u][i] = 0.0f;
-        }
+    for (int u = 0; u < CH; ++u) {
+      const int idx = unit(u);
+      if (!kSplit && !U::active(idx)) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        reg[u][i] = *reinterpret_cast<const uint32_t *>(cp + coff[u] + i * rowc);
+        const float c = sp[soff[u] + i * rows];
+        sc[u][i] = (!GUARD || ok[u]) ? c : 0.0f;
       }
     }
   }
   __device__ __forceinline__ void store(__bf16 *lds) const {
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const int idx = threadIdx.x + u * T;
-      if (UNITS % T != 0 && idx >= UNITS) continue;
-      const int cc = idx % UPR, rg = idx / UPR;
+      const int idx = unit(u);
+      if (!kSplit && !U::active(idx)) continue;
+      const int cc = U::cc(idx), rg = U::rg(idx);
+      const int j0 = kSplit ? 4 * (static_cast<int>(threadIdx.x) / U::UNITS) : 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        // element j of a word: byte j/2, high nibble for even j
-        const int sh = 8 * (j >> 1) + ((j & 1) ? 0 : 4);
-        float v[4];
+      for (int jb = 0; jb < JN / 2; ++jb) {
+        // one code byte per row gives output rows j and j + 1
+        const int j = j0 + 2 * jb;
+        float v0[8], v1[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = __fmul_rn(lv[(reg[u][i] >> sh) & 15u], sc[u][i]);
-        uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        *reinterpret_cast<uint2 *>(lds + (cc * 8 + j) * kLDK + rg * 4) = o;
+        for (int i = 0; i < 8; ++i) {
+          const float2 pr = lv2[(reg[u][i] >> (4 * j)) & 0xFFu];
+          v0[i] = __fmul_rn(pr.x, sc[u][i]);
+          v1[i] = __fmul_rn(pr.y, sc[u][i]);
+        }
+        *reinterpret_cast<uint4 *>(lds + lds_off(cc * 8 + j, rg)) =
+            make_uint4(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v0[4], v0[5]),
+                       pack_bf16x2(v0[6], v0[7]));
+        *reinterpret_cast<uint4 *>(lds + lds_off(cc * 8 + j + 1, rg)) =
+            make_uint4(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]), pack_bf16x2(v1[4], v1[5]),
+                       pack_bf16x2(v1[6], v1[7]));
       }
     }
   }
@@ -398,8 +497,9 @@ struct Nf4Trans {
 
 // ----------------------------------------------------------------- epilogues
 
-// bf16 C[row][col] = bf16(alpha * acc), rows < nrows, cols < ncols.
-template <class Cfg>
+// bf16 C[row][col] = bf16(alpha * acc), rows < nrows, cols < ncols (checked
+// only when GUARD).
+template <class Cfg, bool GUARD = true>
 __device__ __forceinline__ void store_bf16(const Acc<Cfg> &acc, __bf16 *C, int64_t ldc, int64_t nrows,
                                            int64_t ncols, int64_t m0, int64_t n0, float alpha) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -409,11 +509,11 @@ __device__ __forceinline__ void store_bf16(const Acc<Cfg> &acc, __bf16 *C, int64
 #pragma unroll
     for (int j = 0; j < Cfg::TN; ++j) {
       const int64_t col = n0 + wn * Cfg::WTN + j * 32 + (lane & 31);
-      if (col >= ncols) continue;
+      if (GUARD && col >= ncols) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t row = m0 + wm * Cfg::WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < nrows) C[row * ldc + col] = static_cast<__bf16>(alpha * acc.v[i][j][v]);
+        if (!GUARD || row < nrows) C[row * ldc + col] = static_cast<__bf16>(alpha * acc.v[i][j][v]);
       }
     }
 }
@@ -436,6 +536,26 @@ __device__ __forceinline__ void store_f32(const Acc<Cfg> &acc, float *C, int64_t
         if (row < nrows) C[row * ldc + col] = acc.v[i][j][v];
       }
     }
+}
+
+// Workgroup -> output tile. Consecutive workgroup ids are dispatched round
+// robin over the 8 XCDs (each with its own L2), so id b runs on XCD b % 8.
+// Tiles are numbered in groups of 4 tile-rows (grouped raster order) and each
+// XCD takes a contiguous range of tile numbers: the workgroups sharing an L2
+// then cover a compact block of tiles that reuse the same rows of both
+// operands.
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int T = tiles_m * tiles_n;
+  const int base = T / 8, extra = T % 8;
+  const int x = bid % 8, slot = bid / 8;
+  const int t = x * base + min(x, extra) + slot;
+  constexpr int G = 4;
+  const int group = t / (G * tiles_n);
+  const int first_m = group * G;
+  const int gm = min(tiles_m - first_m, G);
+  const int in = t - group * G * tiles_n;
+  tm = first_m + in % gm;
+  tn = in / gm;
 }
 
 }  // namespace qnf4

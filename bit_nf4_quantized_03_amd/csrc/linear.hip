@@ -21,13 +21,14 @@
 // Small M (decode) runs k_fwd with a 32-row tile and a K split instead.
 #include <algorithm>
 
-#include "gemm_core.h"
+#include "gemm_big.h"
 
 namespace qnf4 {
 namespace {
 
-__device__ __forceinline__ void load_levels(float *lv, const Nf4Tables &tab) {
-  if (threadIdx.x < 16) lv[threadIdx.x] = tab.lv[threadIdx.x];
+// LDS table of level pairs for every code byte: (level[b >> 4], level[b & 15]).
+__device__ __forceinline__ void load_level_pairs(float2 *lv2, const Nf4Tables &tab) {
+  for (int b = threadIdx.x; b < 256; b += blockDim.x) lv2[b] = make_float2(tab.lv[b >> 4], tab.lv[b & 15]);
 }
 
 // ------------------------------------------------------------------ forward
@@ -44,39 +45,76 @@ struct FwdParams {
   int steps_per_split;  // 64-deep reduction steps per split of K
 };
 
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::kThreads) void k_fwd(FwdParams p, Nf4Tables tab) {
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (Cfg::kLdsA + Cfg::kLdsB)];
-  __shared__ float lv[16];
-  load_levels(lv, tab);
-  __syncthreads();
-  __bf16 *sA0 = smem, *sA1 = smem + Cfg::kLdsA;
-  __bf16 *sB0 = smem + 2 * Cfg::kLdsA, *sB1 = sB0 + Cfg::kLdsB;
-
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * Cfg::BN;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * Cfg::BM;
-  const int z = blockIdx.z;
+template <class Cfg, bool GUARD>
+__device__ __forceinline__ void fwd_tile(const FwdParams &p, const float2 *lv, __bf16 *smem,
+                                         int64_t m0, int64_t n0, int z) {
   const int total_steps = static_cast<int>(p.K / kBK);
   const int s0 = z * p.steps_per_split;
   const int steps = min(p.steps_per_split, total_steps - s0);
-
   Acc<Cfg> acc;
   acc.zero();
   {
-    RowBf16<Cfg::BM, Cfg::kThreads> la(p.X, p.K, p.M, m0);
-    Nf4Row<Cfg::BN, Cfg::kThreads> lb(p.codes, p.cs, lv, p.N, p.K, n0);
-    mainloop<Cfg>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, sA0, sA1, sB0, sB1);
+    RowBf16<Cfg::BM, Cfg::kThreads, GUARD> la(p.X, p.K, p.M, m0);
+    Nf4Row<Cfg::BN, Cfg::kThreads, GUARD> lb(p.codes, p.cs, lv, p.N, p.K, n0);
+    mainloop<Cfg>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
   }
   if (z == 0 && p.rp > 0) {
-    RowBf16<Cfg::BM, Cfg::kThreads> la(p.Hs, p.rp, p.M, m0);
-    RowBf16<Cfg::BN, Cfg::kThreads> lb(p.Bb, p.rp, p.N, n0);
-    mainloop<Cfg>(acc, la, lb, 0, p.rp / kBK, sA0, sA1, sB0, sB1);
+    RowBf16<Cfg::BM, Cfg::kThreads, GUARD> la(p.Hs, p.rp, p.M, m0);
+    RowBf16<Cfg::BN, Cfg::kThreads, GUARD> lb(p.Bb, p.rp, p.N, n0);
+    mainloop<Cfg>(acc, la, lb, 0, p.rp / kBK, smem);
   }
   if (gridDim.z == 1)
-    store_bf16<Cfg>(acc, static_cast<__bf16 *>(p.Y), p.N, p.M, p.N, m0, n0, 1.0f);
+    store_bf16<Cfg, GUARD>(acc, static_cast<__bf16 *>(p.Y), p.N, p.M, p.N, m0, n0, 1.0f);
   else
     store_f32<Cfg>(acc, static_cast<float *>(p.Y) + static_cast<int64_t>(z) * p.M * p.N, p.N, p.M,
                    p.N, m0, n0);
+}
+
+// Large-M forward: one 256 x 256 tile of Y per workgroup (XCD-aware order).
+__global__ __launch_bounds__(kBigThreads, 1) void k_fwd_big(FwdParams p, Nf4Tables tab) {
+  __shared__ __attribute__((aligned(16))) __bf16 sa0[CfgBig::kLdsA], sa1[CfgBig::kLdsA];
+  __shared__ __attribute__((aligned(16))) __bf16 sb0[CfgBig::kLdsB], sb1[CfgBig::kLdsB];
+  const BigSmem smem{sa0, sa1, sb0, sb1};
+  __shared__ float2 lv[256];
+  load_level_pairs(lv, tab);
+  int tm, tn;
+  tile_of(blockIdx.x, static_cast<int>((p.M + 255) / 256), static_cast<int>((p.N + 255) / 256), tm, tn);
+  const int64_t n0 = static_cast<int64_t>(tn) * 256;
+  const int64_t m0 = static_cast<int64_t>(tm) * 256;
+  __syncthreads();
+  Acc<CfgBig> acc;
+  acc.zero();
+  {
+    DirectRows da(p.X, p.K, p.M, m0);
+    Nf4RowBig l0(p.codes, p.cs, p.N, p.K, n0), l1 = l0;
+    auto load = [](Nf4RowBig &l, int s) { l.load(static_cast<int64_t>(s) * kBK); };
+    big_mainloop_nf4(acc, da, l0, l1, load, static_cast<int>(p.K / kBK), smem, lv);
+  }
+  if (p.rp > 0) {
+    DirectRows da(p.Hs, p.rp, p.M, m0), db(p.Bb, p.rp, p.N, n0);
+    big_mainloop_dense(acc, da, db, p.rp / kBK, smem);
+  }
+  if (m0 + 256 <= p.M && n0 + 256 <= p.N)
+    store_bf16<CfgBig, false>(acc, static_cast<__bf16 *>(p.Y), p.N, p.M, p.N, m0, n0, 1.0f);
+  else
+    store_bf16<CfgBig, true>(acc, static_cast<__bf16 *>(p.Y), p.N, p.M, p.N, m0, n0, 1.0f);
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::kThreads, Cfg::kThreads / 256) void k_fwd(FwdParams p, Nf4Tables tab) {
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (Cfg::kLdsA + Cfg::kLdsB)];
+  __shared__ float2 lv[256];
+  load_level_pairs(lv, tab);
+  __syncthreads();
+  int tm, tn;
+  tile_of(blockIdx.x, static_cast<int>((p.M + Cfg::BM - 1) / Cfg::BM),
+          static_cast<int>((p.N + Cfg::BN - 1) / Cfg::BN), tm, tn);
+  const int64_t n0 = static_cast<int64_t>(tn) * Cfg::BN;
+  const int64_t m0 = static_cast<int64_t>(tm) * Cfg::BM;
+  if (m0 + Cfg::BM <= p.M && n0 + Cfg::BN <= p.N)
+    fwd_tile<Cfg, false>(p, lv, smem, m0, n0, blockIdx.z);
+  else
+    fwd_tile<Cfg, true>(p, lv, smem, m0, n0, blockIdx.z);
 }
 
 // ------------------------------------------------------------- backward dX
@@ -92,30 +130,70 @@ struct DxParams {
   int rp;
 };
 
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::kThreads) void k_bwd_dx(DxParams p, Nf4Tables tab) {
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (Cfg::kLdsA + Cfg::kLdsB)];
-  __shared__ float lv[16];
-  load_levels(lv, tab);
-  __syncthreads();
-  __bf16 *sA0 = smem, *sA1 = smem + Cfg::kLdsA;
-  __bf16 *sB0 = smem + 2 * Cfg::kLdsA, *sB1 = sB0 + Cfg::kLdsB;
-
-  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * Cfg::BN;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * Cfg::BM;
+template <class Cfg, bool GUARD>
+__device__ __forceinline__ void dx_tile(const DxParams &p, const float2 *lv, __bf16 *smem,
+                                        int64_t m0, int64_t k0) {
   Acc<Cfg> acc;
   acc.zero();
   {
-    RowBf16<Cfg::BM, Cfg::kThreads> la(p.dY, p.N, p.M, m0);
-    Nf4Trans<Cfg::BN, Cfg::kThreads> lb(p.codes, p.cs, lv, p.N, p.K, k0);
-    mainloop<Cfg>(acc, la, lb, 0, static_cast<int>(p.N / kBK), sA0, sA1, sB0, sB1);
+    RowBf16<Cfg::BM, Cfg::kThreads, GUARD> la(p.dY, p.N, p.M, m0);
+    Nf4Trans<Cfg::BN, Cfg::kThreads, GUARD> lb(p.codes, p.cs, lv, p.N, p.K, k0);
+    mainloop<Cfg>(acc, la, lb, 0, static_cast<int>(p.N / kBK), smem);
   }
   if (p.rp > 0) {
-    RowBf16<Cfg::BM, Cfg::kThreads> la(p.dHb, p.rp, p.M, m0);
-    RowBf16<Cfg::BN, Cfg::kThreads> lb(p.Atb, p.rp, p.K, k0);
-    mainloop<Cfg>(acc, la, lb, 0, p.rp / kBK, sA0, sA1, sB0, sB1);
+    RowBf16<Cfg::BM, Cfg::kThreads, GUARD> la(p.dHb, p.rp, p.M, m0);
+    RowBf16<Cfg::BN, Cfg::kThreads, GUARD> lb(p.Atb, p.rp, p.K, k0);
+    mainloop<Cfg>(acc, la, lb, 0, p.rp / kBK, smem);
   }
-  store_bf16<Cfg>(acc, static_cast<__bf16 *>(p.dX), p.K, p.M, p.K, m0, k0, 1.0f);
+  store_bf16<Cfg, GUARD>(acc, static_cast<__bf16 *>(p.dX), p.K, p.M, p.K, m0, k0, 1.0f);
+}
+
+// Input gradient: one 256 x 256 tile of dX per workgroup (XCD-aware order).
+__global__ __launch_bounds__(kBigThreads, 1) void k_dx_big(DxParams p, Nf4Tables tab) {
+  __shared__ __attribute__((aligned(16))) __bf16 sa0[CfgBig::kLdsA], sa1[CfgBig::kLdsA];
+  __shared__ __attribute__((aligned(16))) __bf16 sb0[CfgBig::kLdsB], sb1[CfgBig::kLdsB];
+  const BigSmem smem{sa0, sa1, sb0, sb1};
+  __shared__ float2 lv[256];
+  load_level_pairs(lv, tab);
+  int tm, tn;
+  tile_of(blockIdx.x, static_cast<int>((p.M + 255) / 256), static_cast<int>((p.K + 255) / 256), tm, tn);
+  const int64_t k0 = static_cast<int64_t>(tn) * 256;
+  const int64_t m0 = static_cast<int64_t>(tm) * 256;
+  __syncthreads();
+  Acc<CfgBig> acc;
+  acc.zero();
+  {
+    DirectRows da(p.dY, p.N, p.M, m0);
+    Nf4TransBig l0(p.codes, p.cs, p.K, k0), l1 = l0;
+    const int64_t K = p.K;
+    auto load = [K](Nf4TransBig &l, int s) { l.load(static_cast<int64_t>(s) * kBK, K); };
+    big_mainloop_nf4(acc, da, l0, l1, load, static_cast<int>(p.N / kBK), smem, lv);
+  }
+  if (p.rp > 0) {
+    DirectRows da(p.dHb, p.rp, p.M, m0), db(p.Atb, p.rp, p.K, k0);
+    big_mainloop_dense(acc, da, db, p.rp / kBK, smem);
+  }
+  if (m0 + 256 <= p.M && k0 + 256 <= p.K)
+    store_bf16<CfgBig, false>(acc, static_cast<__bf16 *>(p.dX), p.K, p.M, p.K, m0, k0, 1.0f);
+  else
+    store_bf16<CfgBig, true>(acc, static_cast<__bf16 *>(p.dX), p.K, p.M, p.K, m0, k0, 1.0f);
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::kThreads, Cfg::kThreads / 256) void k_bwd_dx(DxParams p, Nf4Tables tab) {
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (Cfg::kLdsA + Cfg::kLdsB)];
+  __shared__ float2 lv[256];
+  load_level_pairs(lv, tab);
+  __syncthreads();
+  int tm, tn;
+  tile_of(blockIdx.x, static_cast<int>((p.M + Cfg::BM - 1) / Cfg::BM),
+          static_cast<int>((p.K + Cfg::BN - 1) / Cfg::BN), tm, tn);
+  const int64_t k0 = static_cast<int64_t>(tn) * Cfg::BN;
+  const int64_t m0 = static_cast<int64_t>(tm) * Cfg::BM;
+  if (m0 + Cfg::BM <= p.M && k0 + Cfg::BN <= p.K)
+    dx_tile<Cfg, false>(p, lv, smem, m0, k0);
+  else
+    dx_tile<Cfg, true>(p, lv, smem, m0, k0);
 }
 
 // ------------------------------------------------- skinny adapter products
@@ -134,8 +212,6 @@ struct SkinnyParams {
 template <class Cfg, int KIND>
 __global__ __launch_bounds__(Cfg::kThreads) void k_skinny(SkinnyParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (Cfg::kLdsA + Cfg::kLdsB)];
-  __bf16 *sA0 = smem, *sA1 = smem + Cfg::kLdsA;
-  __bf16 *sB0 = smem + 2 * Cfg::kLdsA, *sB1 = sB0 + Cfg::kLdsB;
   const int64_t j0 = static_cast<int64_t>(blockIdx.x) * Cfg::BN;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * Cfg::BM;
   const int z = blockIdx.z;
@@ -147,10 +223,10 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_skinny(SkinnyParams p) {
   RowBf16<Cfg::BM, Cfg::kThreads> la(p.P, p.L, p.M, m0);
   if (KIND == kDown) {
     RowF32<Cfg::BN, Cfg::kThreads> lb(p.Q, p.L, p.r, j0);
-    mainloop<Cfg>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, sA0, sA1, sB0, sB1);
+    mainloop<Cfg>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
   } else {
     TransF32<Cfg::BN, Cfg::kThreads> lb(p.Q, p.r, p.L, p.r, j0);
-    mainloop<Cfg>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, sA0, sA1, sB0, sB1);
+    mainloop<Cfg>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
   }
   store_f32<Cfg>(acc, p.part + static_cast<int64_t>(z) * p.M * p.rp, p.rp, p.M, p.rp, m0, j0);
 }
@@ -168,8 +244,6 @@ struct GradParams {
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::kThreads) void k_grad(GradParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (Cfg::kLdsA + Cfg::kLdsB)];
-  __bf16 *sA0 = smem, *sA1 = smem + Cfg::kLdsA;
-  __bf16 *sB0 = smem + 2 * Cfg::kLdsA, *sB1 = sB0 + Cfg::kLdsB;
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * Cfg::BN;
   const int64_t r0 = static_cast<int64_t>(blockIdx.y) * Cfg::BM;
   const int z = blockIdx.z;
@@ -180,7 +254,7 @@ __global__ __launch_bounds__(Cfg::kThreads) void k_grad(GradParams p) {
   acc.zero();
   TransBf16<Cfg::BM, Cfg::kThreads> la(p.P1, p.R1, p.M, p.R1, r0);
   TransBf16<Cfg::BN, Cfg::kThreads> lb(p.P2, p.R2, p.M, p.R2, c0);
-  mainloop<Cfg>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, sA0, sA1, sB0, sB1);
+  mainloop<Cfg>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
   store_f32<Cfg>(acc, p.part + static_cast<int64_t>(z) * p.R1 * p.R2, p.R2, p.R1, p.R2, r0, c0);
 }
 
@@ -242,7 +316,6 @@ __global__ void k_transpose_pad_bf16(const float *__restrict__ A, int64_t K, int
 }
 
 // ------------------------------------------------------------- tile configs
-using CfgBig = TileCfg<128, 128, 2, 2>;    // fused forward / dX
 using CfgDecode = TileCfg<32, 64, 1, 2>;   // M <= 32 forward, split over K
 using CfgSkinny = TileCfg<64, 64, 2, 2>;   // adapter down / dH products
 using CfgGrad = TileCfg<64, 64, 2, 2>;     // adapter gradients
@@ -369,7 +442,7 @@ hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const 
   if (pl.small) {
     fp.steps_per_split = pl.dec.steps_per_split;
     if (pl.dec.splits > 1) fp.Y = b.y_part;
-    dim3 g(grid_blocks(a.N, CfgDecode::BN), grid_blocks(a.M, CfgDecode::BM), pl.dec.splits);
+    dim3 g(grid_blocks(a.N, CfgDecode::BN) * grid_blocks(a.M, CfgDecode::BM), 1, pl.dec.splits);
     prof_begin(kProfFwdGemm, s);
     hipLaunchKernelGGL(k_fwd<CfgDecode>, g, dim3(CfgDecode::kThreads), 0, s, fp, tab);
     prof_end(kProfFwdGemm, s);
@@ -378,9 +451,9 @@ hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const 
                          pl.dec.splits, a.M * a.N, static_cast<__bf16 *>(Y));
   } else {
     fp.steps_per_split = static_cast<int>(a.K / kBK);
-    dim3 g(grid_blocks(a.N, CfgBig::BN), grid_blocks(a.M, CfgBig::BM), 1);
+    dim3 g(grid_blocks(a.N, 256) * grid_blocks(a.M, 256), 1, 1);
     prof_begin(kProfFwdGemm, s);
-    hipLaunchKernelGGL(k_fwd<CfgBig>, g, dim3(CfgBig::kThreads), 0, s, fp, tab);
+    hipLaunchKernelGGL(k_fwd_big, g, dim3(kBigThreads), 0, s, fp, tab);
     prof_end(kProfFwdGemm, s);
   }
   return hipGetLastError();
@@ -409,9 +482,9 @@ hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const 
   }
   {
     DxParams dp{dY, a.codes, b.cs, b.dHb, b.Atb, dX, a.M, a.N, a.K, pl.rp};
-    dim3 g(grid_blocks(a.K, CfgBig::BN), grid_blocks(a.M, CfgBig::BM), 1);
+    dim3 g(grid_blocks(a.K, 256) * grid_blocks(a.M, 256), 1, 1);
     prof_begin(kProfBwdDx, s);
-    hipLaunchKernelGGL(k_bwd_dx<CfgBig>, g, dim3(CfgBig::kThreads), 0, s, dp, tab);
+    hipLaunchKernelGGL(k_dx_big, g, dim3(kBigThreads), 0, s, dp, tab);
     prof_end(kProfBwdDx, s);
   }
   if (pl.rp > 0) {
