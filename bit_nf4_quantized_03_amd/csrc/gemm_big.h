@@ -32,30 +32,46 @@ typedef __attribute__((address_space(3))) void lds_void;
 struct DirectRows {
   static constexpr int kPerWave = kBigRows / 8 / (kBigThreads / 64);  // 8
   const char *base;
-  uint32_t off[kPerWave];
+  uint32_t off;     // block 0 of this wave; block i adds i * bstride
+  uint32_t bstride; // bytes between the wave's blocks (32 rows)
+  uint32_t clamp;   // largest valid row offset (bytes), for a tile crossing the end
   __device__ DirectRows(const void *src, int64_t ld, int64_t nrows, int64_t row0) {
     base = static_cast<const char *>(src) + row0 * ld * 2;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int rb = lane >> 3, p = lane & 7;
-#pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-      const int b = w + 4 * i;
-      const int row = 8 * b + rb;
-      const int c = p ^ swz(row);
-      int64_t r = row0 + row;
-      if (r >= nrows) r = nrows - 1;
-      off[i] = static_cast<uint32_t>(((r - row0) * ld + 8 * c) * 2);
-    }
+    const int row = 8 * w + rb;              // the swizzle of row 8 (w + 4 i) + rb does not depend on i
+    const int c = p ^ swz(row);
+    off = static_cast<uint32_t>((row * ld + 8 * c) * 2);
+    bstride = static_cast<uint32_t>(32 * ld * 2);
+    const int64_t last = (nrows - 1 - row0) < 255 ? (nrows - 1 - row0) : 255;
+    clamp = static_cast<uint32_t>((last * ld + 8 * c) * 2);
   }
-  // Issue the copies of reduction step red0 into the LDS tile `lds`.
+  // Issue the copies of reduction step red0 into the LDS tile `lds`. They are
+  // written as inline assembly so that the compiler does not treat every
+  // later LDS access and barrier as depending on them: the kernels wait for
+  // the copies explicitly (wait_copies) before the barrier that publishes
+  // the tile. The instruction returns nothing into registers.
   __device__ __forceinline__ void issue(int64_t red0, __bf16 *lds) const {
     const char *p = base + red0 * 2;
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int b = w + 4 * i;
-      __builtin_amdgcn_global_load_lds(p + off[i], (lds_void *)(lds + b * 512), 16, 0, 0);
+      const uint32_t o = min(off + static_cast<uint32_t>(i) * bstride, clamp);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) __bf16 *)(lds + b * 512))));
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(dst), "v"(o), "s"(p)
+                   : "memory", "m0");
     }
+  }
+  // Wait until the copies issued before the last N vector-memory
+  // instructions of this wave have landed in LDS.
+  template <int N>
+  __device__ __forceinline__ static void wait_copies() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
   }
 };
 
@@ -89,21 +105,35 @@ struct Nf4RowBig {
     }
   }
   static constexpr int kLoads = 2 * CH;   // VMEM instructions issued by load()
-  // Decode quarter q (code word q of each chunk: 8 elements per chunk).
-  __device__ __forceinline__ void store_part(__bf16 *lds, const float2 *lv2, int q) const {
+  // Quarter q = code word q of each chunk (8 elements per chunk): the level
+  // pairs are fetched by lookup(), scaled, rounded and stored by finish().
+  struct Pairs {
+    float2 pr[CH][4];
+  };
+  __device__ __forceinline__ void lookup(Pairs &p, const float2 *lv2, int q) const {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const uint32_t w = q == 0 ? reg[i].x : q == 1 ? reg[i].y : q == 2 ? reg[i].z : reg[i].w;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) p.pr[i][b] = lv2[(w >> (8 * b)) & 0xFFu];
+    }
+  }
+  __device__ __forceinline__ void finish(__bf16 *lds, const Pairs &p, int q) const {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int idx = threadIdx.x + i * kBigThreads;
-      const uint32_t w = q == 0 ? reg[i].x : q == 1 ? reg[i].y : q == 2 ? reg[i].z : reg[i].w;
       uint32_t ow[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float2 pr = lv2[(w >> (8 * b)) & 0xFFu];
-        ow[b] = pack_bf16x2(__fmul_rn(pr.x, sc[i]), __fmul_rn(pr.y, sc[i]));
-      }
+      for (int b = 0; b < 4; ++b)
+        ow[b] = pack_bf16x2(__fmul_rn(p.pr[i][b].x, sc[i]), __fmul_rn(p.pr[i][b].y, sc[i]));
       *reinterpret_cast<uint4 *>(lds + lds_off(idx >> 1, (idx & 1) * 4 + q)) =
           make_uint4(ow[0], ow[1], ow[2], ow[3]);
     }
+  }
+  __device__ __forceinline__ void store_part(__bf16 *lds, const float2 *lv2, int q) const {
+    Pairs p;
+    lookup(p, lv2, q);
+    finish(lds, p, q);
   }
 };
 
@@ -138,15 +168,26 @@ struct Nf4TransBig {
     }
   }
   static constexpr int kLoads = 16;
+  struct Pairs {
+    float2 pr[8];
+  };
+  __device__ __forceinline__ void lookup(Pairs &p, const float2 *lv2, int q) const {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p.pr[i] = lv2[(reg[i] >> (8 * q)) & 0xFFu];
+  }
   __device__ __forceinline__ void store_part(__bf16 *lds, const float2 *lv2, int q) const {
+    Pairs p;
+    lookup(p, lv2, q);
+    finish(lds, p, q);
+  }
+  __device__ __forceinline__ void finish(__bf16 *lds, const Pairs &p, int q) const {
     const int idx = threadIdx.x;
     const int cc = U::cc(idx), rg = U::rg(idx);
     float v0[8], v1[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float2 pr = lv2[(reg[i] >> (8 * q)) & 0xFFu];
-      v0[i] = __fmul_rn(pr.x, sc[i]);
-      v1[i] = __fmul_rn(pr.y, sc[i]);
+      v0[i] = __fmul_rn(p.pr[i].x, sc[i]);
+      v1[i] = __fmul_rn(p.pr[i].y, sc[i]);
     }
     *reinterpret_cast<uint4 *>(lds + lds_off(cc * 8 + 2 * q, rg)) =
         make_uint4(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v0[4], v0[5]),
@@ -165,47 +206,89 @@ __device__ __forceinline__ void wait_vmem_below() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// MFMAs of one 16-deep slice kk of the current tiles.
-__device__ __forceinline__ void mma_slice(Acc<CfgBig> &acc, const __bf16 *sA, const __bf16 *sB,
-                                          const FragAddr<128> &fa, const FragAddr<128> &fb, int kk) {
-  bf16x8 a[4], b[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(sA + fa.off[kk] + i * 32 * kLDK);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(sB + fb.off[kk] + j * 32 * kLDK);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.v[i][j], 0, 0, 0);
-}
-
 // The four LDS tiles of the large-tile kernels, as distinct objects so that
 // alias analysis can tell the DMA target of a step from the tiles it reads.
 struct BigSmem {
   __bf16 *a0, *a1, *b0, *b1;
 };
 
+// Fragments of one 16-deep slice for a wave's 128 x 128 block.
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+__device__ __forceinline__ void load_frags(Frags &f, const __bf16 *sA, const __bf16 *sB,
+                                           const FragAddr<128> &fa, const FragAddr<128> &fb, int kk) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8 *>(sA + fa.off[kk] + i * 32 * kLDK);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(sB + fb.off[kk] + j * 32 * kLDK);
+}
+
+__device__ __forceinline__ void mma_frags(Acc<CfgBig> &acc, const Frags &f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.v[i][j], 0, 0, 0);
+}
+
+// MFMAs of one 16-deep slice kk of the current tiles.
+__device__ __forceinline__ void mma_slice(Acc<CfgBig> &acc, const __bf16 *sA, const __bf16 *sB,
+                                          const FragAddr<128> &fa, const FragAddr<128> &fb, int kk) {
+  Frags f;
+  load_frags(f, sA, sB, fa, fb, kk);
+  mma_frags(acc, f);
+}
+
+// Interleave one group of 16 MFMAs with the scale / round / store work of a
+// decode quarter (2 VALU per MFMA, then the LDS stores).
+__device__ __forceinline__ void interleave_group() {
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // 2 VALU
+  }
+  __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);     // LDS stores
+}
+
 // One step of the NF4 main loop: MFMAs on (aCur, bCur); the dense operand of
 // step sn1 is copied into aNxt; the codes in ldec (step sn1) are decoded into
 // bNxt; lload receives the codes of step sn2. The caller clamps sn1 and sn2
 // to the last step, so the body has no branches; extra copies and decodes
-// at the end land in the buffer nobody reads any more.
+// at the end land in the buffer nobody reads any more. Fragments of slice
+// kk + 1 and the codebook reads of quarter kk are issued before the MFMAs of
+// slice kk; the scale / round / store work runs between those MFMAs.
 template <class LB, class LoadFn>
 __device__ __forceinline__ void big_step(Acc<CfgBig> &acc, const DirectRows &da, LB &ldec, LB &lload,
                                          LoadFn &load, int sn1, int sn2, __bf16 *aCur, __bf16 *bCur,
                                          __bf16 *aNxt, __bf16 *bNxt, const FragAddr<128> &fa,
                                          const FragAddr<128> &fb, const float2 *lv2) {
+  // The only vector-memory operations in flight here are the code loads of
+  // ldec, issued one step ago: complete them before issuing anything new, so
+  // that no later wait on ldec has to drain this step's copies.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   da.issue(static_cast<int64_t>(sn1) * kBK, aNxt);
-  __builtin_amdgcn_sched_barrier(0);
   load(lload, sn2);
+  __builtin_amdgcn_sched_barrier(0);
+  Frags f0, f1;
+  load_frags(f0, aCur, bCur, fa, fb, 0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    mma_slice(acc, aCur, bCur, fa, fb, kk);
-    ldec.store_part(bNxt, lv2, kk);
+    Frags &cur = (kk & 1) ? f1 : f0;
+    Frags &nxt = (kk & 1) ? f0 : f1;
+    if (kk < 3) load_frags(nxt, aCur, bCur, fa, fb, kk + 1);
+    typename LB::Pairs pr;
+    ldec.lookup(pr, lv2, kk);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_frags(acc, cur);
+    ldec.finish(bNxt, pr, kk);
+    interleave_group();
+    __builtin_amdgcn_sched_barrier(0);
   }
-  wait_vmem_below<LB::kLoads>();
+  // the copies into aNxt were issued before the code loads of this step
+  DirectRows::wait_copies<LB::kLoads>();
   __syncthreads();
 }
 
