@@ -321,18 +321,27 @@ struct TransF32 {
   __device__ TransF32(const void *s, int64_t ld_, int64_t nred_, int64_t ncols_, int64_t col0_)
       : src(static_cast<const float *>(s)), ld(ld_), nred(nred_), ncols(ncols_), col0(col0_) {}
   __device__ __forceinline__ void load(int64_t red0) {
+    const bool vec = (ld & 3) == 0;   // rows 16-byte aligned: vector loads
 #pragma unroll
     for (int u = 0; u < U::CH; ++u) {
       const int idx = threadIdx.x + u * T;
       if (!U::active(idx)) continue;
       const int cc = U::cc(idx), rg = U::rg(idx);
+      const int64_t c0 = col0 + cc * 8;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int64_t t = red0 + rg * 8 + i;
+        if (vec && t < nred && c0 + 8 <= ncols) {
+          const float4 lo = *reinterpret_cast<const float4 *>(src + t * ld + c0);
+          const float4 hi = *reinterpret_cast<const float4 *>(src + t * ld + c0 + 4);
+          reg[u][i][0] = lo.x; reg[u][i][1] = lo.y; reg[u][i][2] = lo.z; reg[u][i][3] = lo.w;
+          reg[u][i][4] = hi.x; reg[u][i][5] = hi.y; reg[u][i][6] = hi.z; reg[u][i][7] = hi.w;
+        } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int64_t c = col0 + cc * 8 + j;
-          reg[u][i][j] = (t < nred && c < ncols) ? src[t * ld + c] : 0.0f;
+          for (int j = 0; j < 8; ++j) {
+            const int64_t c = c0 + j;
+            reg[u][i][j] = (t < nred && c < ncols) ? src[t * ld + c] : 0.0f;
+          }
         }
       }
     }
@@ -349,6 +358,55 @@ struct TransF32 {
                              pack_bf16x2(reg[u][4][j], reg[u][5][j]), pack_bf16x2(reg[u][6][j], reg[u][7][j]));
         *reinterpret_cast<uint4 *>(lds + lds_off(cc * 8 + j, rg)) = v;
       }
+    }
+  }
+};
+
+// Transposed fp32 source S[t][col] for small tiles: units of 8 reduction rows
+// x 2 output rows (one 8-byte load per reduction row), so that every thread
+// of the group has a unit. Out-of-range elements read as 0.
+template <int ROWS, int T>
+struct TransF32Narrow {
+  static constexpr int UPR = ROWS / 2;          // column pairs
+  static constexpr int UNITS = UPR * 8;         // x 8 reduction-row groups
+  static constexpr int CH = (UNITS + T - 1) / T;
+  const float *src;
+  int64_t ld, nred, ncols, col0;
+  float2 reg[CH][8];
+  __device__ TransF32Narrow(const void *s, int64_t ld_, int64_t nred_, int64_t ncols_, int64_t col0_)
+      : src(static_cast<const float *>(s)), ld(ld_), nred(nred_), ncols(ncols_), col0(col0_) {}
+  __device__ __forceinline__ void load(int64_t red0) {
+    const bool vec = (ld & 1) == 0;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int idx = threadIdx.x + u * T;
+      if (UNITS % T != 0 && idx >= UNITS) continue;
+      const int cp = idx % UPR, rg = idx / UPR;
+      const int64_t c = col0 + 2 * cp;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t t = red0 + rg * 8 + i;
+        if (vec && t < nred && c + 2 <= ncols) {
+          reg[u][i] = *reinterpret_cast<const float2 *>(src + t * ld + c);
+        } else {
+          reg[u][i].x = (t < nred && c < ncols) ? src[t * ld + c] : 0.0f;
+          reg[u][i].y = (t < nred && c + 1 < ncols) ? src[t * ld + c + 1] : 0.0f;
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void store(__bf16 *lds) const {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int idx = threadIdx.x + u * T;
+      if (UNITS % T != 0 && idx >= UNITS) continue;
+      const int cp = idx % UPR, rg = idx / UPR;
+      const uint4 lo = make_uint4(pack_bf16x2(reg[u][0].x, reg[u][1].x), pack_bf16x2(reg[u][2].x, reg[u][3].x),
+                                  pack_bf16x2(reg[u][4].x, reg[u][5].x), pack_bf16x2(reg[u][6].x, reg[u][7].x));
+      const uint4 hi = make_uint4(pack_bf16x2(reg[u][0].y, reg[u][1].y), pack_bf16x2(reg[u][2].y, reg[u][3].y),
+                                  pack_bf16x2(reg[u][4].y, reg[u][5].y), pack_bf16x2(reg[u][6].y, reg[u][7].y));
+      *reinterpret_cast<uint4 *>(lds + lds_off(2 * cp, rg)) = lo;
+      *reinterpret_cast<uint4 *>(lds + lds_off(2 * cp + 1, rg)) = hi;
     }
   }
 };

@@ -8,16 +8,17 @@
 //   backward   dH = s dY B,  dX = dY W + dH A,  dA = dH^T X,  dB = s dY^T (X A^T)
 //
 // Kernel plan (all on the caller's stream, no host synchronization):
-//   k_block_scales   c_b for every quantization block (fp32, workspace)
-//   k_skinny<Down>   partials of H = X A^T over a K split       -> Hs = bf16(s H)
-//   k_skinny<DH>     partials of dY B over an N split            -> dHb = bf16(s dY B)
-//   k_fwd            Y tile = [X | Hs] [W-hat | Bb]^T: the NF4 weight is decoded
-//                    into LDS step by step, the adapter term is 64-deep extra
-//                    reduction steps on the same accumulators (fused epilogue)
-//   k_bwd_dx         dX tile = [dY | dHb] [W-hat ; At]: the weight decoded
-//                    transposed (reduction over out_features)
-//   k_grad           split-M partials of dA = dHb^T X and dB = dY^T Hs
-//   k_reduce_*       fixed-order sums of the split partials
+//   k_adapter_prep    block scales c_b; bf16 copies of A, B in the layouts
+//                     the products below read (A, B^T, B, A^T)
+//   k_adapter_down    split partials of H = X A^T and (backward) of dY B
+//   k_adapter_finish  Hs = bf16(s H) and (backward) dHb = bf16(s dY B)
+//   k_fwd_big         Y tile = [X | Hs] [W-hat | Bb]^T: the NF4 weight is decoded
+//                     into LDS step by step, the adapter term is 64-deep extra
+//                     reduction steps on the same accumulators
+//   k_dx_big          dX tile = [dY | dHb] [W-hat ; At]: the weight decoded
+//                     transposed (reduction over out_features)
+//   k_grad            split-M partials of dA = dHb^T X and dB = dY^T Hs
+//   k_grad_finish     fixed-order sums of those partials
 // Small M (decode) runs k_fwd with a 32-row tile and a K split instead.
 #include <algorithm>
 
@@ -130,24 +131,6 @@ struct DxParams {
   int rp;
 };
 
-template <class Cfg, bool GUARD>
-__device__ __forceinline__ void dx_tile(const DxParams &p, const float2 *lv, __bf16 *smem,
-                                        int64_t m0, int64_t k0) {
-  Acc<Cfg> acc;
-  acc.zero();
-  {
-    RowBf16<Cfg::BM, Cfg::kThreads, GUARD> la(p.dY, p.N, p.M, m0);
-    Nf4Trans<Cfg::BN, Cfg::kThreads, GUARD> lb(p.codes, p.cs, lv, p.N, p.K, k0);
-    mainloop<Cfg>(acc, la, lb, 0, static_cast<int>(p.N / kBK), smem);
-  }
-  if (p.rp > 0) {
-    RowBf16<Cfg::BM, Cfg::kThreads, GUARD> la(p.dHb, p.rp, p.M, m0);
-    RowBf16<Cfg::BN, Cfg::kThreads, GUARD> lb(p.Atb, p.rp, p.K, k0);
-    mainloop<Cfg>(acc, la, lb, 0, p.rp / kBK, smem);
-  }
-  store_bf16<Cfg, GUARD>(acc, static_cast<__bf16 *>(p.dX), p.K, p.M, p.K, m0, k0, 1.0f);
-}
-
 // Input gradient: one 256 x 256 tile of dX per workgroup (XCD-aware order).
 __global__ __launch_bounds__(kBigThreads, 1) void k_dx_big(DxParams p, Nf4Tables tab) {
   __shared__ __attribute__((aligned(16))) __bf16 sa0[CfgBig::kLdsA], sa1[CfgBig::kLdsA];
@@ -179,113 +162,210 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_dx_big(DxParams p, Nf4Tables
     store_bf16<CfgBig, true>(acc, static_cast<__bf16 *>(p.dX), p.K, p.M, p.K, m0, k0, 1.0f);
 }
 
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::kThreads, Cfg::kThreads / 256) void k_bwd_dx(DxParams p, Nf4Tables tab) {
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (Cfg::kLdsA + Cfg::kLdsB)];
-  __shared__ float2 lv[256];
-  load_level_pairs(lv, tab);
-  __syncthreads();
-  int tm, tn;
-  tile_of(blockIdx.x, static_cast<int>((p.M + Cfg::BM - 1) / Cfg::BM),
-          static_cast<int>((p.K + Cfg::BN - 1) / Cfg::BN), tm, tn);
-  const int64_t k0 = static_cast<int64_t>(tn) * Cfg::BN;
-  const int64_t m0 = static_cast<int64_t>(tm) * Cfg::BM;
-  if (m0 + Cfg::BM <= p.M && k0 + Cfg::BN <= p.K)
-    dx_tile<Cfg, false>(p, lv, smem, m0, k0);
-  else
-    dx_tile<Cfg, true>(p, lv, smem, m0, k0);
-}
+// ------------------------------------------------ adapter pre-work
+//
+// k_adapter_prep (elementwise, one launch) writes, each in one segment:
+//   cs  [nb]      block scales c_b of the NF4 weight (for the GEMMs)
+//   Ab  [rp][K]   bf16(A), rows >= r zero          (operand of H = X A^T)
+//   Bt  [rp][N]   bf16(B^T), rows >= r zero        (operand of dY B; backward)
+//   Bb  [N][rp]   bf16(B), columns >= r zero       (forward adapter step)
+//   Atb [K][rp]   bf16(A^T), columns >= r zero     (backward adapter step)
+// k_adapter_down then computes 128 x 64 tiles of the split partials of
+// H = X Ab^T and (backward) dY Bt^T with 16-byte bf16 loads on both sides.
 
-// ------------------------------------------------- skinny adapter products
+using CfgSkinny = TileCfg<128, 64, 2, 2>;
+constexpr int kScaleBlocksPerThread = 4;
 
-enum SkinnyKind { kDown = 0, kDH = 1 };
-
-struct SkinnyParams {
-  const void *P;    // bf16 [M, L]: X (L = K) or dY (L = N)
-  const float *Q;   // fp32: A [r, K] (kDown) or B [N, r] (kDH)
-  float *part;      // fp32 partials [splits][M][rp]
-  int64_t M, L;
+struct PrepParams {
+  const int8_t *absmax_q;
+  const float *dq_scale;
+  const float *dq_mean;
+  const float *A, *B;
+  float *cs;
+  __bf16 *Ab, *Bt, *Bb, *Atb;
+  int64_t nb, N, K;
   int r, rp;
-  int steps_per_split;
+  int64_t n_cs, n_ab, n_bt, n_bb, n_atb;   // segment lengths (0 when absent)
 };
 
-template <class Cfg, int KIND>
-__global__ __launch_bounds__(Cfg::kThreads) void k_skinny(SkinnyParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (Cfg::kLdsA + Cfg::kLdsB)];
-  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * Cfg::BN;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * Cfg::BM;
-  const int z = blockIdx.z;
-  const int total_steps = static_cast<int>(p.L / kBK);
-  const int s0 = z * p.steps_per_split;
-  const int steps = min(p.steps_per_split, total_steps - s0);
-  Acc<Cfg> acc;
-  acc.zero();
-  RowBf16<Cfg::BM, Cfg::kThreads> la(p.P, p.L, p.M, m0);
-  if (KIND == kDown) {
-    RowF32<Cfg::BN, Cfg::kThreads> lb(p.Q, p.L, p.r, j0);
-    mainloop<Cfg>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
-  } else {
-    TransF32<Cfg::BN, Cfg::kThreads> lb(p.Q, p.r, p.L, p.r, j0);
-    mainloop<Cfg>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
+__global__ __launch_bounds__(256) void k_adapter_prep(PrepParams p) {
+  const int64_t n_cs_items = (p.n_cs + kScaleBlocksPerThread - 1) / kScaleBlocksPerThread;
+  const int64_t total = n_cs_items + p.n_ab + p.n_bt + p.n_bb + p.n_atb;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    int64_t e = i;
+    if (e < n_cs_items) {
+      const float mu = p.dq_mean[0];
+#pragma unroll
+      for (int u = 0; u < kScaleBlocksPerThread; ++u) {
+        const int64_t b = e * kScaleBlocksPerThread + u;
+        if (b < p.nb) {
+          const float kd = __fdiv_rn(p.dq_scale[b / kDqBlock], 127.0f);
+          p.cs[b] = __fadd_rn(__fmul_rn(static_cast<float>(p.absmax_q[b]), kd), mu);
+        }
+      }
+      continue;
+    }
+    e -= n_cs_items;
+    if (e < p.n_ab) {   // Ab[j][k]
+      const int64_t j = e / p.K, k = e % p.K;
+      p.Ab[e] = static_cast<__bf16>(j < p.r ? p.A[j * p.K + k] : 0.0f);
+      continue;
+    }
+    e -= p.n_ab;
+    if (e < p.n_bt) {   // Bt[j][n]
+      const int64_t j = e / p.N, n = e % p.N;
+      p.Bt[e] = static_cast<__bf16>(j < p.r ? p.B[n * p.r + j] : 0.0f);
+      continue;
+    }
+    e -= p.n_bt;
+    if (e < p.n_bb) {   // Bb[n][j]
+      const int64_t n = e / p.rp, j = e % p.rp;
+      p.Bb[e] = static_cast<__bf16>(j < p.r ? p.B[n * p.r + j] : 0.0f);
+      continue;
+    }
+    e -= p.n_bb;        // Atb[k][j]
+    const int64_t k = e / p.rp, j = e % p.rp;
+    p.Atb[e] = static_cast<__bf16>(j < p.r ? p.A[j * p.K + k] : 0.0f);
   }
-  store_f32<Cfg>(acc, p.part + static_cast<int64_t>(z) * p.M * p.rp, p.rp, p.M, p.rp, m0, j0);
+}
+
+struct DownParams {
+  const void *X, *dY;
+  const __bf16 *Ab, *Bt;
+  float *h_part, *dh_part;   // [splits][M][rp]
+  int64_t M, N, K;
+  int rp;
+  int jt;                    // rp / 64 column tiles
+  int mt;                    // M / 128 row tiles (rounded up)
+  int h_splits, h_steps, dh_splits, dh_steps;
+};
+
+__global__ __launch_bounds__(256) void k_adapter_down(DownParams p) {
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (CfgSkinny::kLdsA + CfgSkinny::kLdsB)];
+  int g = blockIdx.x;
+  const int per = p.jt * p.mt;
+  const bool is_h = g < per * p.h_splits;
+  if (!is_h) g -= per * p.h_splits;
+  const int z = g / per, t = g % per;
+  const int64_t j0 = static_cast<int64_t>(t % p.jt) * 64;
+  const int64_t m0 = static_cast<int64_t>(t / p.jt) * 128;
+  const void *P = is_h ? p.X : p.dY;
+  const __bf16 *Q = is_h ? p.Ab : p.Bt;
+  const int64_t L = is_h ? p.K : p.N;
+  const int steps_per = is_h ? p.h_steps : p.dh_steps;
+  float *part = is_h ? p.h_part : p.dh_part;
+  const int total = static_cast<int>(L / kBK);
+  const int s0 = z * steps_per, steps = min(steps_per, total - s0);
+  Acc<CfgSkinny> acc;
+  acc.zero();
+  RowBf16<128, 256> la(P, L, p.M, m0);
+  RowBf16<64, 256> lb(Q, L, p.rp, j0);
+  mainloop<CfgSkinny>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
+  store_f32<CfgSkinny>(acc, part + static_cast<int64_t>(z) * p.M * p.rp, p.rp, p.M, p.rp, m0, j0);
+}
+
+// k_adapter_finish sums the split partials into the bf16 operands of the
+// adapter steps: Hs [M][rp] = bf16(s * sum_z h_part) and (backward)
+// dHb [M][rp] = bf16(s * sum_z dh_part), in a fixed order.
+struct FinishParams {
+  const float *h_part, *dh_part;
+  __bf16 *Hs, *dHb;
+  int64_t n;        // M * rp
+  int r, rp, h_splits, dh_splits;
+  float scale;
+  bool backward;
+};
+
+__global__ __launch_bounds__(256) void k_adapter_finish(FinishParams p) {
+  const int64_t total = p.backward ? 2 * p.n : p.n;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const bool second = i >= p.n;
+    const int64_t e = second ? i - p.n : i;
+    const float *part = second ? p.dh_part : p.h_part;
+    const int splits = second ? p.dh_splits : p.h_splits;
+    float v = 0.0f;
+    if (static_cast<int>(e % p.rp) < p.r)
+      for (int z = 0; z < splits; ++z) v += part[static_cast<int64_t>(z) * p.n + e];
+    (second ? p.dHb : p.Hs)[e] = static_cast<__bf16>(p.scale * v);
+  }
 }
 
 // ------------------------------------------------ adapter gradient products
-
+//
+// k_grad: M-split partials of dA = dHb^T X  ([rp][K] tiles first) and
+// dB = dY^T Hs ([N][rp] tiles after them); k_grad_finish sums the partials in
+// a fixed order into dA [r][K] and dB [N][r].
 struct GradParams {
-  const void *P1;   // bf16 [M, R1]: operand whose columns are the output rows
-  const void *P2;   // bf16 [M, R2]: operand whose columns are the output cols
-  float *part;      // fp32 partials [splits][R1][R2]
-  int64_t M, R1, R2;
-  int steps_per_split;
+  const void *X, *dY, *Hs, *dHb;
+  float *a_part, *b_part;     // [splits][rp][K], [splits][N][rp]
+  int64_t M, N, K;
+  int rp;
+  int a_tiles_c, a_tiles, a_splits, a_steps;   // dA: 64 x 256 tiles over (rp, K)
+  int b_tiles_c, b_tiles, b_splits, b_steps;   // dB: 256 x 64 tiles over (N, rp)
 };
 
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::kThreads) void k_grad(GradParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (Cfg::kLdsA + Cfg::kLdsB)];
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * Cfg::BN;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * Cfg::BM;
-  const int z = blockIdx.z;
-  const int total_steps = static_cast<int>((p.M + kBK - 1) / kBK);
-  const int s0 = z * p.steps_per_split;
-  const int steps = min(p.steps_per_split, total_steps - s0);
-  Acc<Cfg> acc;
-  acc.zero();
-  TransBf16<Cfg::BM, Cfg::kThreads> la(p.P1, p.R1, p.M, p.R1, r0);
-  TransBf16<Cfg::BN, Cfg::kThreads> lb(p.P2, p.R2, p.M, p.R2, c0);
-  mainloop<Cfg>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
-  store_f32<Cfg>(acc, p.part + static_cast<int64_t>(z) * p.R1 * p.R2, p.R2, p.R1, p.R2, r0, c0);
+using CfgGradA = TileCfg<64, 256, 1, 4>;   // dA tile: 64 adapter rows x 256 columns of K
+using CfgGradB = TileCfg<256, 64, 4, 1>;   // dB tile: 256 rows of N x 64 adapter columns
+
+__global__ __launch_bounds__(256) void k_grad(GradParams p) {
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (CfgGradA::kLdsA + CfgGradA::kLdsB)];
+  int g = blockIdx.x;
+  const bool is_a = g < p.a_tiles * p.a_splits;
+  if (!is_a) g -= p.a_tiles * p.a_splits;
+  const int tiles = is_a ? p.a_tiles : p.b_tiles;
+  const int tiles_c = is_a ? p.a_tiles_c : p.b_tiles_c;
+  const int per = is_a ? p.a_steps : p.b_steps;
+  const int z = g / tiles, t = g % tiles;
+  const int total = static_cast<int>((p.M + kBK - 1) / kBK);
+  const int s0 = z * per, steps = min(per, total - s0);
+  if (is_a) {
+    const int64_t c0 = static_cast<int64_t>(t % tiles_c) * 256;
+    const int64_t r0 = static_cast<int64_t>(t / tiles_c) * 64;
+    Acc<CfgGradA> acc;
+    acc.zero();
+    TransBf16<64, 256> la(p.dHb, p.rp, p.M, p.rp, r0);
+    TransBf16<256, 256> lb(p.X, p.K, p.M, p.K, c0);
+    mainloop<CfgGradA>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
+    store_f32<CfgGradA>(acc, p.a_part + static_cast<int64_t>(z) * p.rp * p.K, p.K, p.rp, p.K, r0, c0);
+  } else {
+    const int64_t c0 = static_cast<int64_t>(t % tiles_c) * 64;
+    const int64_t r0 = static_cast<int64_t>(t / tiles_c) * 256;
+    Acc<CfgGradB> acc;
+    acc.zero();
+    TransBf16<256, 256> la(p.dY, p.N, p.M, p.N, r0);
+    TransBf16<64, 256> lb(p.Hs, p.rp, p.M, p.rp, c0);
+    mainloop<CfgGradB>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
+    store_f32<CfgGradB>(acc, p.b_part + static_cast<int64_t>(z) * p.N * p.rp, p.rp, p.N, p.rp, r0, c0);
+  }
 }
 
-// ------------------------------------------------------------ small kernels
+struct GradFinishParams {
+  const float *a_part, *b_part;
+  float *dA, *dB;
+  int64_t N, K;
+  int r, rp, a_splits, b_splits;
+};
 
-// out bf16 [rows][rp] = bf16(alpha * sum_z part[z][rows][rp]) for col < r, 0 beyond.
-__global__ void k_reduce_bf16(const float *__restrict__ part, int splits, int64_t rows, int rp,
-                              int r, float alpha, __bf16 *__restrict__ out) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = rows * rp;
-  if (i >= total) return;
-  const int col = static_cast<int>(i % rp);
-  float s = 0.0f;
-  if (col < r)
-    for (int z = 0; z < splits; ++z) s += part[static_cast<int64_t>(z) * total + i];
-  out[i] = static_cast<__bf16>(alpha * s);
+__global__ __launch_bounds__(256) void k_grad_finish(GradFinishParams p) {
+  const int64_t na = static_cast<int64_t>(p.r) * p.K, nbb = p.N * p.r;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < na + nbb;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float v = 0.0f;
+    if (i < na) {   // dA [r][K] from [splits][rp][K]
+      for (int z = 0; z < p.a_splits; ++z) v += p.a_part[static_cast<int64_t>(z) * p.rp * p.K + i];
+      p.dA[i] = v;
+    } else {        // dB [N][r] from [splits][N][rp]
+      const int64_t e = i - na, row = e / p.r, col = e % p.r;
+      for (int z = 0; z < p.b_splits; ++z)
+        v += p.b_part[static_cast<int64_t>(z) * p.N * p.rp + row * p.rp + col];
+      p.dB[e] = v;
+    }
+  }
 }
 
-// out fp32 [rows][ldo] = alpha * sum_z part[z * stride + row * ldp + col], col < cols.
-__global__ void k_reduce_f32(const float *__restrict__ part, int splits, int64_t stride,
-                             int64_t rows, int64_t cols, int64_t ldp, float alpha,
-                             float *__restrict__ out, int64_t ldo) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= rows * cols) return;
-  const int64_t row = i / cols, col = i % cols;
-  float s = 0.0f;
-  for (int z = 0; z < splits; ++z) s += part[z * stride + row * ldp + col];
-  out[row * ldo + col] = alpha * s;
-}
-
-// Y bf16 [M][N] = bf16(sum_z part[z][M][N]).
+// Y bf16 [M][N] = bf16(sum_z part[z][M][N]) (skinny-M forward with a K split).
 __global__ void k_reduce_out(const float *__restrict__ part, int splits, int64_t total,
                              __bf16 *__restrict__ Y) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -295,30 +375,8 @@ __global__ void k_reduce_out(const float *__restrict__ part, int splits, int64_t
   Y[i] = static_cast<__bf16>(s);
 }
 
-// dst bf16 [rows][rp] = bf16(src fp32 [rows][r]), zero padded.
-__global__ void k_pad_bf16(const float *__restrict__ src, int64_t rows, int r, int rp,
-                           __bf16 *__restrict__ dst) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= rows * rp) return;
-  const int64_t row = i / rp;
-  const int col = static_cast<int>(i % rp);
-  dst[i] = static_cast<__bf16>(col < r ? src[row * r + col] : 0.0f);
-}
-
-// dst bf16 [K][rp] = bf16(A[j][k]) for j < r, 0 beyond (transpose of A [r][K]).
-__global__ void k_transpose_pad_bf16(const float *__restrict__ A, int64_t K, int r, int rp,
-                                     __bf16 *__restrict__ dst) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= K * rp) return;
-  const int64_t k = i / rp;
-  const int j = static_cast<int>(i % rp);
-  dst[i] = static_cast<__bf16>(j < r ? A[static_cast<int64_t>(j) * K + k] : 0.0f);
-}
-
 // ------------------------------------------------------------- tile configs
 using CfgDecode = TileCfg<32, 64, 1, 2>;   // M <= 32 forward, split over K
-using CfgSkinny = TileCfg<64, 64, 2, 2>;   // adapter down / dH products
-using CfgGrad = TileCfg<64, 64, 2, 2>;     // adapter gradients
 
 constexpr int kSmallM = 32;
 constexpr int kTargetGroups = 512;
@@ -361,18 +419,20 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int r) {
   pl.rp = static_cast<int>(ceil_div(r, kBK) * kBK);
   pl.small = M <= kSmallM;
   const int ksteps = static_cast<int>(K / kBK), nsteps = static_cast<int>(N / kBK);
-  const int64_t skinny_tiles = grid_blocks(M, CfgSkinny::BM) * grid_blocks(pl.rp, CfgSkinny::BN);
+  const int64_t skinny_tiles = grid_blocks(M, 128) * grid_blocks(pl.rp, 64);
   pl.down = choose_split(skinny_tiles, ksteps, 64);
   pl.dh = choose_split(skinny_tiles, nsteps, 64);
   const int msteps = static_cast<int>(ceil_div(M, kBK));
-  pl.ga = choose_split(grid_blocks(pl.rp, CfgGrad::BM) * grid_blocks(K, CfgGrad::BN), msteps, 16);
-  pl.gb = choose_split(grid_blocks(N, CfgGrad::BM) * grid_blocks(pl.rp, CfgGrad::BN), msteps, 16);
+  pl.ga = choose_split(grid_blocks(pl.rp, 64) * grid_blocks(K, 256), msteps, 8);
+  pl.gb = choose_split(grid_blocks(N, 256) * grid_blocks(pl.rp, 64), msteps, 8);
   pl.dec = choose_split(grid_blocks(N, CfgDecode::BN), ksteps, 32);
   return pl;
 }
 
 struct Buffers {
   float *cs;
+  __bf16 *Ab;
+  __bf16 *Bt;
   float *down_part;
   __bf16 *Hs;
   __bf16 *Bb;
@@ -391,6 +451,8 @@ Buffers carve(void *ws, const Plan &pl, int64_t M, int64_t N, int64_t K, size_t 
   const int rp = pl.rp;
   b.cs = c.take<float>(nb);
   if (rp > 0) {
+    b.Ab = c.take<__bf16>(static_cast<size_t>(rp) * K);
+    b.Bt = c.take<__bf16>(static_cast<size_t>(rp) * N);
     b.down_part = c.take<float>(static_cast<size_t>(pl.down.splits) * M * rp);
     b.Hs = c.take<__bf16>(static_cast<size_t>(M) * rp);
     b.Bb = c.take<__bf16>(static_cast<size_t>(N) * rp);
@@ -405,14 +467,74 @@ Buffers carve(void *ws, const Plan &pl, int64_t M, int64_t N, int64_t K, size_t 
   return b;
 }
 
-hipError_t run_down(const LinearArgs &a, const Plan &pl, const Buffers &b, const void *X,
-                    const float *A, hipStream_t s) {
-  SkinnyParams sp{X, A, b.down_part, a.M, a.K, a.r, pl.rp, pl.down.steps_per_split};
-  dim3 g(grid_blocks(pl.rp, CfgSkinny::BN), grid_blocks(a.M, CfgSkinny::BM), pl.down.splits);
-  hipLaunchKernelGGL((k_skinny<CfgSkinny, kDown>), g, dim3(CfgSkinny::kThreads), 0, s, sp);
-  const int64_t total = a.M * pl.rp;
-  hipLaunchKernelGGL(k_reduce_bf16, dim3(grid_blocks(total, 256)), dim3(256), 0, s, b.down_part,
-                     pl.down.splits, a.M, pl.rp, a.r, a.scale, b.Hs);
+// Block scales and the bf16 adapter layouts (one elementwise launch).
+hipError_t run_adapter_prep(const LinearArgs &a, const Plan &pl, const Buffers &b, const float *A,
+                            const float *B, bool backward, hipStream_t s) {
+  PrepParams pp{};
+  pp.absmax_q = a.absmax_q;
+  pp.dq_scale = a.dq_scale;
+  pp.dq_mean = a.dq_mean;
+  pp.A = A;
+  pp.B = B;
+  pp.cs = b.cs;
+  pp.Ab = b.Ab;
+  pp.Bt = b.Bt;
+  pp.Bb = b.Bb;
+  pp.Atb = b.Atb;
+  pp.nb = ceil_div(a.N * a.K, kBlock);
+  pp.N = a.N;
+  pp.K = a.K;
+  pp.r = a.r;
+  pp.rp = pl.rp;
+  pp.n_cs = pp.nb;
+  const bool lora = pl.rp > 0;
+  pp.n_ab = lora ? static_cast<int64_t>(pl.rp) * a.K : 0;
+  pp.n_bt = (lora && backward) ? static_cast<int64_t>(pl.rp) * a.N : 0;
+  pp.n_bb = (lora && !backward) ? a.N * pl.rp : 0;
+  pp.n_atb = (lora && backward) ? a.K * pl.rp : 0;
+  const int64_t total = ceil_div(pp.n_cs, kScaleBlocksPerThread) + pp.n_ab + pp.n_bt + pp.n_bb + pp.n_atb;
+  const int64_t grid = std::min<int64_t>(grid_blocks(total, 256), 8192);
+  hipLaunchKernelGGL(k_adapter_prep, dim3(grid), dim3(256), 0, s, pp);
+  return hipGetLastError();
+}
+
+// H partials and (backward) dY B partials (one launch), then their sums.
+hipError_t run_adapter_down_finish(const LinearArgs &a, const Plan &pl, const Buffers &b, const void *X,
+                                   const void *dY, bool backward, hipStream_t s) {
+  DownParams dp{};
+  dp.X = X;
+  dp.dY = dY;
+  dp.Ab = b.Ab;
+  dp.Bt = b.Bt;
+  dp.h_part = b.down_part;
+  dp.dh_part = b.dh_part;
+  dp.M = a.M;
+  dp.N = a.N;
+  dp.K = a.K;
+  dp.rp = pl.rp;
+  dp.jt = pl.rp / 64;
+  dp.mt = static_cast<int>(ceil_div(a.M, 128));
+  dp.h_splits = pl.down.splits;
+  dp.h_steps = pl.down.steps_per_split;
+  dp.dh_splits = backward ? pl.dh.splits : 0;
+  dp.dh_steps = pl.dh.steps_per_split;
+  const int64_t groups = static_cast<int64_t>(dp.jt) * dp.mt * (dp.h_splits + dp.dh_splits);
+  hipLaunchKernelGGL(k_adapter_down, dim3(groups), dim3(256), 0, s, dp);
+  FinishParams fp{};
+  fp.h_part = b.down_part;
+  fp.dh_part = b.dh_part;
+  fp.Hs = b.Hs;
+  fp.dHb = b.dHb;
+  fp.n = a.M * pl.rp;
+  fp.r = a.r;
+  fp.rp = pl.rp;
+  fp.h_splits = pl.down.splits;
+  fp.dh_splits = pl.dh.splits;
+  fp.scale = a.scale;
+  fp.backward = backward;
+  const int64_t total = backward ? 2 * fp.n : fp.n;
+  hipLaunchKernelGGL(k_adapter_finish, dim3(std::min<int64_t>(grid_blocks(total, 256), 4096)), dim3(256), 0,
+                     s, fp);
   return hipGetLastError();
 }
 
@@ -429,14 +551,11 @@ hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const 
   const Plan pl = make_plan(a.M, a.N, a.K, a.r);
   const Buffers b = carve(ws, pl, a.M, a.N, a.K, nullptr);
   const Nf4Tables &tab = nf4_tables();
-  hipError_t err = launch_block_scales(a.absmax_q, a.dq_scale, a.dq_mean, ceil_div(a.N * a.K, kBlock),
-                                       b.cs, s);
+  hipError_t err = run_adapter_prep(a, pl, b, A, B, false, s);
   if (err != hipSuccess) return err;
   if (pl.rp > 0) {
-    err = run_down(a, pl, b, X, A, s);
+    err = run_adapter_down_finish(a, pl, b, X, nullptr, false, s);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_pad_bf16, dim3(grid_blocks(a.N * pl.rp, 256)), dim3(256), 0, s, B, a.N, a.r,
-                       pl.rp, b.Bb);
   }
   FwdParams fp{X, a.codes, b.cs, b.Hs, b.Bb, Y, a.M, a.N, a.K, pl.rp, 0};
   if (pl.small) {
@@ -464,21 +583,11 @@ hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const 
   const Plan pl = make_plan(a.M, a.N, a.K, a.r);
   const Buffers b = carve(ws, pl, a.M, a.N, a.K, nullptr);
   const Nf4Tables &tab = nf4_tables();
-  hipError_t err = launch_block_scales(a.absmax_q, a.dq_scale, a.dq_mean, ceil_div(a.N * a.K, kBlock),
-                                       b.cs, s);
+  hipError_t err = run_adapter_prep(a, pl, b, A, B, true, s);
   if (err != hipSuccess) return err;
   if (pl.rp > 0) {
-    // Hs = bf16(s X A^T)
-    err = run_down(a, pl, b, X, A, s);
+    err = run_adapter_down_finish(a, pl, b, X, dY, true, s);
     if (err != hipSuccess) return err;
-    // dHb = bf16(s dY B)
-    SkinnyParams sp{dY, B, b.dh_part, a.M, a.N, a.r, pl.rp, pl.dh.steps_per_split};
-    dim3 g(grid_blocks(pl.rp, CfgSkinny::BN), grid_blocks(a.M, CfgSkinny::BM), pl.dh.splits);
-    hipLaunchKernelGGL((k_skinny<CfgSkinny, kDH>), g, dim3(CfgSkinny::kThreads), 0, s, sp);
-    hipLaunchKernelGGL(k_reduce_bf16, dim3(grid_blocks(a.M * pl.rp, 256)), dim3(256), 0, s,
-                       b.dh_part, pl.dh.splits, a.M, pl.rp, a.r, a.scale, b.dHb);
-    hipLaunchKernelGGL(k_transpose_pad_bf16, dim3(grid_blocks(a.K * pl.rp, 256)), dim3(256), 0, s, A,
-                       a.K, a.r, pl.rp, b.Atb);
   }
   {
     DxParams dp{dY, a.codes, b.cs, b.dHb, b.Atb, dX, a.M, a.N, a.K, pl.rp};
@@ -488,20 +597,32 @@ hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const 
     prof_end(kProfBwdDx, s);
   }
   if (pl.rp > 0) {
-    // dA [r, K] = dHb^T X
-    GradParams gp{b.dHb, X, b.ga_part, a.M, pl.rp, a.K, pl.ga.steps_per_split};
-    dim3 g(grid_blocks(a.K, CfgGrad::BN), grid_blocks(pl.rp, CfgGrad::BM), pl.ga.splits);
-    hipLaunchKernelGGL(k_grad<CfgGrad>, g, dim3(CfgGrad::kThreads), 0, s, gp);
-    hipLaunchKernelGGL(k_reduce_f32, dim3(grid_blocks(static_cast<int64_t>(a.r) * a.K, 256)), dim3(256),
-                       0, s, b.ga_part, pl.ga.splits, static_cast<int64_t>(pl.rp) * a.K,
-                       static_cast<int64_t>(a.r), a.K, a.K, 1.0f, dA, a.K);
-    // dB [N, r] = dY^T Hs   (Hs already carries the factor s)
-    GradParams gq{dY, b.Hs, b.gb_part, a.M, a.N, pl.rp, pl.gb.steps_per_split};
-    dim3 g2(grid_blocks(pl.rp, CfgGrad::BN), grid_blocks(a.N, CfgGrad::BM), pl.gb.splits);
-    hipLaunchKernelGGL(k_grad<CfgGrad>, g2, dim3(CfgGrad::kThreads), 0, s, gq);
-    hipLaunchKernelGGL(k_reduce_f32, dim3(grid_blocks(a.N * a.r, 256)), dim3(256), 0, s, b.gb_part,
-                       pl.gb.splits, a.N * pl.rp, a.N, static_cast<int64_t>(a.r),
-                       static_cast<int64_t>(pl.rp), 1.0f, dB, static_cast<int64_t>(a.r));
+    GradParams gp{};
+    gp.X = X;
+    gp.dY = dY;
+    gp.Hs = b.Hs;
+    gp.dHb = b.dHb;
+    gp.a_part = b.ga_part;
+    gp.b_part = b.gb_part;
+    gp.M = a.M;
+    gp.N = a.N;
+    gp.K = a.K;
+    gp.rp = pl.rp;
+    gp.a_tiles_c = static_cast<int>(grid_blocks(a.K, 256));
+    gp.a_tiles = gp.a_tiles_c * (pl.rp / 64);
+    gp.a_splits = pl.ga.splits;
+    gp.a_steps = pl.ga.steps_per_split;
+    gp.b_tiles_c = pl.rp / 64;
+    gp.b_tiles = gp.b_tiles_c * static_cast<int>(grid_blocks(a.N, 256));
+    gp.b_splits = pl.gb.splits;
+    gp.b_steps = pl.gb.steps_per_split;
+    const int64_t groups = static_cast<int64_t>(gp.a_tiles) * gp.a_splits +
+                           static_cast<int64_t>(gp.b_tiles) * gp.b_splits;
+    hipLaunchKernelGGL(k_grad, dim3(groups), dim3(256), 0, s, gp);
+    GradFinishParams fp{b.ga_part, b.gb_part, dA, dB, a.N, a.K, a.r, pl.rp, pl.ga.splits, pl.gb.splits};
+    const int64_t total = static_cast<int64_t>(a.r) * a.K + a.N * a.r;
+    hipLaunchKernelGGL(k_grad_finish, dim3(std::min<int64_t>(grid_blocks(total, 256), 4096)), dim3(256), 0,
+                       s, fp);
   }
   return hipGetLastError();
 }
