@@ -228,6 +228,10 @@ def main():
     outs = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(R)]
 
     def timed(fn, reps=3):
+        """Per-call time of fn(0..R-1) (distinct buffers, so every call streams
+        from HBM): eager launches, and the same R calls captured as one HIP
+        graph and replayed (no host launch overhead). Returns (graph, eager)
+        in ms; graph is None if capture fails."""
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for i in range(R):
             fn(i)
@@ -238,14 +242,37 @@ def main():
                 fn(i)
         ev1.record()
         torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / (reps * R)
+        eager = ev0.elapsed_time(ev1) / (reps * R)
+        if args.no_graph:
+            return None, eager
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(R):
+                    fn(i)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(reps):
+                g.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            del g
+            return ev0.elapsed_time(ev1) / (reps * R), eager
+        except Exception as e:  # noqa: BLE001 - capture unsupported: eager only
+            log(f"graph capture failed ({e}); eager timing only")
+            return None, eager
 
-    qms = timed(lambda i: qb.qlora_nf4_quantize(Ws[i], out=qs[i], ws=ws_q))
-    dms = timed(lambda i: qb.qlora_nf4_dequantize(qs[i], torch.bfloat16, out=outs[i]))
+    qg, qe = timed(lambda i: qb.qlora_nf4_quantize(Ws[i], out=qs[i], ws=ws_q))
+    dg, de = timed(lambda i: qb.qlora_nf4_dequantize(qs[i], torch.bfloat16, out=outs[i]))
+    qms, dms = (qg if qg is not None else qe), (dg if dg is not None else de)
     q_bytes = 2 * n + stored
     d_bytes = stored + 2 * n
-    rows["quantize"] = {"us": qms * 1e3, "bytes": q_bytes, "gbs": q_bytes / (qms * 1e-3) / 1e9}
-    rows["dequantize_bf16"] = {"us": dms * 1e3, "bytes": d_bytes, "gbs": d_bytes / (dms * 1e-3) / 1e9}
+    rows["quantize"] = {"us": qms * 1e3, "us_eager": qe * 1e3, "bytes": q_bytes,
+                        "gbs": q_bytes / (qms * 1e-3) / 1e9}
+    rows["dequantize_bf16"] = {"us": dms * 1e3, "us_eager": de * 1e3, "bytes": d_bytes,
+                               "gbs": d_bytes / (dms * 1e-3) / 1e9}
     for k in ("quantize", "dequantize_bf16"):
         rows[k]["frac_of_hbm_peak"] = rows[k]["gbs"] / HBM_PEAK_GBS
     rows["quantize"]["rotation"] = R
@@ -268,24 +295,28 @@ def main():
             Xd = d_bf16(w2.X)
             Yd = torch.empty((Mx, Nx), dtype=torch.bfloat16, device=dev)
             wsd = torch.empty(qb.qlora_linear_workspace_bytes(Mx, Nx, Kx, r), dtype=torch.uint8, device=dev)
-            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            R_saved, R = R, Rd
+            qb.qlora_profile_reset()
+            qb.qlora_profile_enable(True)
             for i in range(Rd):
                 qb.qlora_linear_fwd(Xd, qd[i], Ad[i], Bd[i], w2.s, ws=wsd, out=Yd)
             torch.cuda.synchronize()
-            reps = 5
-            ev0.record()
-            for _ in range(reps):
-                for i in range(Rd):
-                    qb.qlora_linear_fwd(Xd, qd[i], Ad[i], Bd[i], w2.s, ws=wsd, out=Yd)
-            ev1.record()
-            torch.cuda.synchronize()
-            ms = ev0.elapsed_time(ev1) / (reps * Rd)
+            qb.qlora_profile_enable(False)
+            ktot, kcnt = qb.qlora_profile_read(qb.QLORA_PROF_FWD_GEMM)
+            qb.qlora_profile_reset()
+            g_ms, e_ms = timed(lambda i: qb.qlora_linear_fwd(Xd, qd[i], Ad[i], Bd[i], w2.s, ws=wsd, out=Yd),
+                               reps=5)
+            R = R_saved
+            ms = g_ms if g_ms is not None else e_ms
             byts = st + 4 * r * (Kx + Nx) + 2 * Mx * Kx + 2 * Mx * Nx
-            decode[name] = {"M": Mx, "N": Nx, "K": Kx, "us": ms * 1e3, "bytes": byts,
-                            "gbs": byts / (ms * 1e-3) / 1e9,
+            kus = ktot / kcnt * 1e3 if kcnt else None
+            # the streaming kernel alone moves the NF4+DQ stream, X, A and its partials
+            decode[name] = {"M": Mx, "N": Nx, "K": Kx, "us": ms * 1e3, "us_eager": e_ms * 1e3,
+                            "bytes": byts, "gbs": byts / (ms * 1e-3) / 1e9,
                             "frac_of_hbm_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                            "rotation": Rd}
-            log(f"decode {name}: {ms * 1e3:.2f} us, {decode[name]['gbs']:.0f} GB/s")
+                            "stream_kernel_us": kus, "rotation": Rd}
+            log(f"decode {name}: {ms * 1e3:.2f} us/call ({decode[name]['gbs']:.0f} GB/s), "
+                f"eager {e_ms * 1e3:.2f} us, streaming kernel {kus:.2f} us")
             del qd, Ad, Bd, Wd
             torch.cuda.empty_cache()
 

@@ -70,4 +70,10 @@ hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const 
                       const float *B, void *dX, float *dA, float *dB, void *ws,
                       hipStream_t s);
 
+// Skinny-M forward (M <= 32): fp32 split partials of Y and of X A^T at the
+// start of the workspace, then the bf16 output.
+size_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K, int r);
+hipError_t launch_gemv(const LinearArgs &a, const void *X, const float *A, const float *B, void *Y,
+                       void *ws, hipStream_t s);
+
 }  // namespace qnf4

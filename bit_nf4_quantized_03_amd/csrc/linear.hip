@@ -19,7 +19,7 @@
 //                     transposed (reduction over out_features)
 //   k_grad            split-M partials of dA = dHb^T X and dB = dY^T Hs
 //   k_grad_finish     fixed-order sums of those partials
-// Small M (decode) runs k_fwd with a 32-row tile and a K split instead.
+// Small M (decode, M <= 32) runs the weight-streaming kernels of gemv.hip instead.
 #include <algorithm>
 
 #include "gemm_big.h"
@@ -40,36 +40,10 @@ struct FwdParams {
   const float *cs;      // per-block scales
   const void *Hs;       // bf16 [M, rp] = bf16(s * X A^T), zero padded
   const void *Bb;       // bf16 [N, rp], zero padded
-  void *Y;              // bf16 [M, N] (splits == 1) or fp32 partials [splits][M][N]
+  void *Y;              // bf16 [M, N]
   int64_t M, N, K;
   int rp;
-  int steps_per_split;  // 64-deep reduction steps per split of K
 };
-
-template <class Cfg, bool GUARD>
-__device__ __forceinline__ void fwd_tile(const FwdParams &p, const float2 *lv, __bf16 *smem,
-                                         int64_t m0, int64_t n0, int z) {
-  const int total_steps = static_cast<int>(p.K / kBK);
-  const int s0 = z * p.steps_per_split;
-  const int steps = min(p.steps_per_split, total_steps - s0);
-  Acc<Cfg> acc;
-  acc.zero();
-  {
-    RowBf16<Cfg::BM, Cfg::kThreads, GUARD> la(p.X, p.K, p.M, m0);
-    Nf4Row<Cfg::BN, Cfg::kThreads, GUARD> lb(p.codes, p.cs, lv, p.N, p.K, n0);
-    mainloop<Cfg>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
-  }
-  if (z == 0 && p.rp > 0) {
-    RowBf16<Cfg::BM, Cfg::kThreads, GUARD> la(p.Hs, p.rp, p.M, m0);
-    RowBf16<Cfg::BN, Cfg::kThreads, GUARD> lb(p.Bb, p.rp, p.N, n0);
-    mainloop<Cfg>(acc, la, lb, 0, p.rp / kBK, smem);
-  }
-  if (gridDim.z == 1)
-    store_bf16<Cfg, GUARD>(acc, static_cast<__bf16 *>(p.Y), p.N, p.M, p.N, m0, n0, 1.0f);
-  else
-    store_f32<Cfg>(acc, static_cast<float *>(p.Y) + static_cast<int64_t>(z) * p.M * p.N, p.N, p.M,
-                   p.N, m0, n0);
-}
 
 // Large-M forward: one 256 x 256 tile of Y per workgroup (XCD-aware order).
 __global__ __launch_bounds__(kBigThreads, 1) void k_fwd_big(FwdParams p, Nf4Tables tab) {
@@ -99,23 +73,6 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_fwd_big(FwdParams p, Nf4Tabl
     store_bf16<CfgBig, false>(acc, static_cast<__bf16 *>(p.Y), p.N, p.M, p.N, m0, n0, 1.0f);
   else
     store_bf16<CfgBig, true>(acc, static_cast<__bf16 *>(p.Y), p.N, p.M, p.N, m0, n0, 1.0f);
-}
-
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::kThreads, Cfg::kThreads / 256) void k_fwd(FwdParams p, Nf4Tables tab) {
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (Cfg::kLdsA + Cfg::kLdsB)];
-  __shared__ float2 lv[256];
-  load_level_pairs(lv, tab);
-  __syncthreads();
-  int tm, tn;
-  tile_of(blockIdx.x, static_cast<int>((p.M + Cfg::BM - 1) / Cfg::BM),
-          static_cast<int>((p.N + Cfg::BN - 1) / Cfg::BN), tm, tn);
-  const int64_t n0 = static_cast<int64_t>(tn) * Cfg::BN;
-  const int64_t m0 = static_cast<int64_t>(tm) * Cfg::BM;
-  if (m0 + Cfg::BM <= p.M && n0 + Cfg::BN <= p.N)
-    fwd_tile<Cfg, false>(p, lv, smem, m0, n0, blockIdx.z);
-  else
-    fwd_tile<Cfg, true>(p, lv, smem, m0, n0, blockIdx.z);
 }
 
 // ------------------------------------------------------------- backward dX
@@ -365,19 +322,7 @@ __global__ __launch_bounds__(256) void k_grad_finish(GradFinishParams p) {
   }
 }
 
-// Y bf16 [M][N] = bf16(sum_z part[z][M][N]) (skinny-M forward with a K split).
-__global__ void k_reduce_out(const float *__restrict__ part, int splits, int64_t total,
-                             __bf16 *__restrict__ Y) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  float s = 0.0f;
-  for (int z = 0; z < splits; ++z) s += part[z * total + i];
-  Y[i] = static_cast<__bf16>(s);
-}
-
 // ------------------------------------------------------------- tile configs
-using CfgDecode = TileCfg<32, 64, 1, 2>;   // M <= 32 forward, split over K
-
 constexpr int kSmallM = 32;
 constexpr int kTargetGroups = 512;
 
@@ -410,7 +355,7 @@ struct Carve {
 
 struct Plan {
   int rp;
-  Split down, dh, ga, gb, dec;
+  Split down, dh, ga, gb;
   bool small;
 };
 
@@ -425,7 +370,6 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int r) {
   const int msteps = static_cast<int>(ceil_div(M, kBK));
   pl.ga = choose_split(grid_blocks(pl.rp, 64) * grid_blocks(K, 256), msteps, 8);
   pl.gb = choose_split(grid_blocks(N, 256) * grid_blocks(pl.rp, 64), msteps, 8);
-  pl.dec = choose_split(grid_blocks(N, CfgDecode::BN), ksteps, 32);
   return pl;
 }
 
@@ -441,7 +385,6 @@ struct Buffers {
   __bf16 *Atb;
   float *ga_part;
   float *gb_part;
-  float *y_part;
 };
 
 Buffers carve(void *ws, const Plan &pl, int64_t M, int64_t N, int64_t K, size_t *bytes) {
@@ -462,7 +405,6 @@ Buffers carve(void *ws, const Plan &pl, int64_t M, int64_t N, int64_t K, size_t 
     b.ga_part = c.take<float>(static_cast<size_t>(pl.ga.splits) * rp * K);
     b.gb_part = c.take<float>(static_cast<size_t>(pl.gb.splits) * N * rp);
   }
-  if (pl.small && pl.dec.splits > 1) b.y_part = c.take<float>(static_cast<size_t>(pl.dec.splits) * M * N);
   if (bytes) *bytes = c.off;
   return b;
 }
@@ -542,39 +484,28 @@ hipError_t run_adapter_down_finish(const LinearArgs &a, const Plan &pl, const Bu
 
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
   size_t bytes = 0;
-  carve(nullptr, make_plan(M, N, K, r), M, N, K, &bytes);
-  return bytes;
+  const Plan pl = make_plan(M, N, K, r);
+  carve(nullptr, pl, M, N, K, &bytes);
+  // the skinny-M forward reuses the same workspace from its start
+  return pl.small ? std::max(bytes, gemv_ws_bytes(M, N, K, r)) : bytes;
 }
 
 hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const float *B, void *Y,
                       void *ws, hipStream_t s) {
   const Plan pl = make_plan(a.M, a.N, a.K, a.r);
+  if (pl.small) return launch_gemv(a, X, A, B, Y, ws, s);
   const Buffers b = carve(ws, pl, a.M, a.N, a.K, nullptr);
-  const Nf4Tables &tab = nf4_tables();
   hipError_t err = run_adapter_prep(a, pl, b, A, B, false, s);
   if (err != hipSuccess) return err;
   if (pl.rp > 0) {
     err = run_adapter_down_finish(a, pl, b, X, nullptr, false, s);
     if (err != hipSuccess) return err;
   }
-  FwdParams fp{X, a.codes, b.cs, b.Hs, b.Bb, Y, a.M, a.N, a.K, pl.rp, 0};
-  if (pl.small) {
-    fp.steps_per_split = pl.dec.steps_per_split;
-    if (pl.dec.splits > 1) fp.Y = b.y_part;
-    dim3 g(grid_blocks(a.N, CfgDecode::BN) * grid_blocks(a.M, CfgDecode::BM), 1, pl.dec.splits);
-    prof_begin(kProfFwdGemm, s);
-    hipLaunchKernelGGL(k_fwd<CfgDecode>, g, dim3(CfgDecode::kThreads), 0, s, fp, tab);
-    prof_end(kProfFwdGemm, s);
-    if (pl.dec.splits > 1)
-      hipLaunchKernelGGL(k_reduce_out, dim3(grid_blocks(a.M * a.N, 256)), dim3(256), 0, s, b.y_part,
-                         pl.dec.splits, a.M * a.N, static_cast<__bf16 *>(Y));
-  } else {
-    fp.steps_per_split = static_cast<int>(a.K / kBK);
-    dim3 g(grid_blocks(a.N, 256) * grid_blocks(a.M, 256), 1, 1);
-    prof_begin(kProfFwdGemm, s);
-    hipLaunchKernelGGL(k_fwd_big, g, dim3(kBigThreads), 0, s, fp, tab);
-    prof_end(kProfFwdGemm, s);
-  }
+  FwdParams fp{X, a.codes, b.cs, b.Hs, b.Bb, Y, a.M, a.N, a.K, pl.rp};
+  dim3 g(grid_blocks(a.N, 256) * grid_blocks(a.M, 256), 1, 1);
+  prof_begin(kProfFwdGemm, s);
+  hipLaunchKernelGGL(k_fwd_big, g, dim3(kBigThreads), 0, s, fp, nf4_tables());
+  prof_end(kProfFwdGemm, s);
   return hipGetLastError();
 }
 

@@ -96,6 +96,17 @@ def test_ragged_m_and_rank(qb, cb, M, r):
     _bwd(qb, c, f"ragged M={M} r={r}")
 
 
+@pytest.mark.parametrize("M", [1, 7, 16, 23, 32])
+@pytest.mark.parametrize("r", [0, 8, 72])
+def test_decode_split_k_ragged(qb, cb, M, r):
+    """Skinny-M forward with several K splits, a short last split, K not a
+    multiple of 256 (absmax bytes not dword aligned) and a partial column strip."""
+    wl = synth.make_linear_workload("decode-ragged", M=M, N=320, K=2240, r=r, alpha=16.0,
+                                    seed=7000 + M * 10 + r, w_dtype="bf16")
+    c = Case(qb, wl, cb)
+    _fwd(qb, c, f"decode-ragged M={M} r={r}")
+
+
 def test_identity_input_gives_exact_weight(qb, cb):
     """X = I (M = K), no adapter: Y[m, n] = bf16(w-hat[n, m]) exactly.
     dY = I (M = N): dX = bf16(w-hat) exactly."""
