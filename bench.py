@@ -19,10 +19,16 @@ The JSON line also carries
                 GB/s with buffer rotation past the 256 MB last-level cache);
   decode        the skinny-M forward (GEMV) at the 7B MLP shapes in GB/s,
                 with rotation over > 512 MB of distinct weights;
+  mlp65b        forward and backward at the 65B MLP shapes (M = 2048);
+  dequant_solo  dequantize alone at 65B shapes, bf16 and fp32 out;
+  whole_model_roundtrip
+                quantize + dequantize of every tensor of a 65B-shaped
+                80-layer stack (tensors generated on the GPU per layer);
   cpu_baseline  the CPU oracle timed on this host for whole steps of the
                 same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-decode] [--no-large] [--wm-layers L] [--no-graph]
 """
 from __future__ import annotations
 
@@ -47,16 +53,22 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources; traffic counters are only reported while
-    the sources they were taken on are unchanged."""
+# Sources that define each timed kernel: stored traffic counters are reported
+# only while these files are unchanged.
+KERNEL_SOURCES = {
+    "fwd_gemm": ("linear.hip", "gemm_big.h", "gemm_core.h", "internal.h"),
+    "bwd_dx_gemm": ("linear.hip", "gemm_big.h", "gemm_core.h", "internal.h"),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the sources a kernel is built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_nf4_quantized_03_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode())
-                h.update(f.read())
+    for name in sorted(KERNEL_SOURCES[kernel]):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -69,7 +81,7 @@ def load_traffic(kernel: str):
     except (OSError, ValueError):
         return None
     ent = data.get(kernel)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or ent.get("source_hash") != kernel_source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 
@@ -81,6 +93,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the 65B MLP, 65B dequantize and whole-model rows")
+    ap.add_argument("--wm-layers", type=int, default=80,
+                    help="layers of the 65B-shaped stack in the whole-model round trip")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -320,6 +336,131 @@ def main():
             del qd, Ad, Bd, Wd
             torch.cuda.empty_cache()
 
+    # ------------------------------------- large shapes, generated on device
+    # Timing-only inputs with the same distributions as the parity workloads
+    # (N(0, 0.02) weights, 1 % outliers x10 for the 65B MLP, N(0, 1)
+    # activations), drawn on the GPU from seeded generators.
+    def dev_normal(shape, std, seed, outlier_frac=0.0):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+        x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std
+        if outlier_frac > 0:
+            mask = torch.rand(shape, generator=gen, device=dev) < outlier_frac
+            x = torch.where(mask, x * 10.0, x)
+        return x.to(torch.bfloat16)
+
+    def ev_time(fn, reps):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    mlp = {}
+    if not args.no_large:
+        for name, (Nm, Km) in (("up65b", (22016, 8192)), ("down65b", (8192, 22016))):
+            Mm = 2048
+            seed = 65 if name == "up65b" else 66
+            Wm = dev_normal((Nm, Km), 0.02, seed, 0.01)
+            qm = qb.qlora_nf4_quantize(Wm)
+            del Wm
+            Xm = dev_normal((Mm, Km), 1.0, seed + 1000)
+            dYm = dev_normal((Mm, Nm), 1.0, seed + 2000)
+            Am = dev_normal((r, Km), 0.01, seed + 3000).float()
+            Bm = dev_normal((Nm, r), 0.01, seed + 4000).float()
+            wsm = torch.empty(qb.qlora_linear_workspace_bytes(Mm, Nm, Km, r), dtype=torch.uint8, device=dev)
+            Ym = torch.empty((Mm, Nm), dtype=torch.bfloat16, device=dev)
+            dXm = torch.empty((Mm, Km), dtype=torch.bfloat16, device=dev)
+            dAm = torch.empty((r, Km), dtype=torch.float32, device=dev)
+            dBm = torch.empty((Nm, r), dtype=torch.float32, device=dev)
+            fwd_ms = ev_time(lambda: qb.qlora_linear_fwd(Xm, qm, Am, Bm, s, ws=wsm, out=Ym), 5)
+            bwd_ms = ev_time(lambda: qb.qlora_linear_bwd(dYm, Xm, qm, Am, Bm, s, ws=wsm, outs=(dXm, dAm, dBm)), 5)
+            qb.qlora_profile_reset()
+            qb.qlora_profile_enable(True)
+            for _ in range(3):
+                qb.qlora_linear_fwd(Xm, qm, Am, Bm, s, ws=wsm, out=Ym)
+                qb.qlora_linear_bwd(dYm, Xm, qm, Am, Bm, s, ws=wsm, outs=(dXm, dAm, dBm))
+            torch.cuda.synchronize()
+            qb.qlora_profile_enable(False)
+            kf = qb.qlora_profile_read(qb.QLORA_PROF_FWD_GEMM)
+            kd = qb.qlora_profile_read(qb.QLORA_PROF_BWD_DX)
+            qb.qlora_profile_reset()
+            ff = 2.0 * Mm * Nm * Km + 2.0 * Mm * r * (Km + Nm)
+            bf = 2.0 * Mm * Nm * Km + 4.0 * Mm * r * (Nm + Km)
+            kf_us, kd_us = kf[0] / kf[1] * 1e3, kd[0] / kd[1] * 1e3
+            mlp[name] = {"M": Mm, "N": Nm, "K": Km, "r": r,
+                         "fwd_us": fwd_ms * 1e3, "fwd_tflops": ff / (fwd_ms * 1e-3) / 1e12,
+                         "bwd_us": bwd_ms * 1e3, "bwd_tflops": bf / (bwd_ms * 1e-3) / 1e12,
+                         "fwd_gemm_kernel_us": kf_us,
+                         "fwd_gemm_kernel_tflops": 2.0 * Mm * Nm * (Km + r) / (kf_us * 1e-6) / 1e12,
+                         "bwd_dx_kernel_us": kd_us,
+                         "bwd_dx_kernel_tflops": 2.0 * Mm * Km * (Nm + r) / (kd_us * 1e-6) / 1e12}
+            for k in ("fwd_tflops", "bwd_tflops", "fwd_gemm_kernel_tflops", "bwd_dx_kernel_tflops"):
+                mlp[name][k.replace("tflops", "frac_of_bf16_peak")] = mlp[name][k] / BF16_PEAK_TFLOPS
+            log(f"{name}: fwd {fwd_ms * 1e3:.1f} us ({mlp[name]['fwd_tflops']:.0f} TFLOP/s), "
+                f"bwd {bwd_ms * 1e3:.1f} us ({mlp[name]['bwd_tflops']:.0f} TFLOP/s)")
+            del qm, Xm, dYm, Am, Bm, wsm, Ym, dXm, dAm, dBm
+            torch.cuda.empty_cache()
+
+    # dequantize alone at the 65B shapes (bf16 and fp32 out), two rotating sets
+    dq_solo = {}
+    if not args.no_large:
+        for name, (Nq, Kq) in (("up65b", (22016, 8192)), ("attn65b", (8192, 8192))):
+            st = qb.qlora_nf4_storage_bytes(Nq, Kq)
+            qs2 = [qb.qlora_nf4_quantize(dev_normal((Nq, Kq), 0.02, 500 + i)) for i in range(2)]
+            for dt, esz in ((torch.bfloat16, 2), (torch.float32, 4)):
+                outs2 = [torch.empty((Nq, Kq), dtype=dt, device=dev) for _ in range(2)]
+                ms = ev_time(lambda: [qb.qlora_nf4_dequantize(qs2[i], dt, out=outs2[i]) for i in range(2)], 5) / 2
+                byts = st + esz * Nq * Kq
+                key = f"{name}_{'bf16' if esz == 2 else 'f32'}"
+                dq_solo[key] = {"N": Nq, "K": Kq, "us": ms * 1e3, "bytes": byts,
+                                "gbs": byts / (ms * 1e-3) / 1e9,
+                                "frac_of_hbm_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                log(f"dequantize {key}: {ms * 1e3:.1f} us, {dq_solo[key]['gbs']:.0f} GB/s")
+                del outs2
+            del qs2
+            torch.cuda.empty_cache()
+
+    # whole 65B-shaped stack: per layer, 4 x 8192^2 + 3 x 8192x22016 bf16
+    # tensors generated on the device, then quantize + dequantize (bf16) of
+    # all seven timed back to back
+    wm = None
+    if not args.no_large:
+        shapes = [(8192, 8192)] * 4 + [(22016, 8192), (22016, 8192), (8192, 22016)]
+        layers = args.wm_layers
+        qs7 = [qb.NF4Weight.empty(a, b, dev) for a, b in shapes]
+        outs7 = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for sh in shapes]
+        wsq = torch.empty(max(qb.qlora_nf4_quantize_workspace_bytes(a, b) for a, b in shapes),
+                          dtype=torch.uint8, device=dev)
+        total_ms = 0.0
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for layer in range(layers):
+            ws7 = [dev_normal(sh, 0.02, 1000 * layer + t) for t, sh in enumerate(shapes)]
+            torch.cuda.synchronize()
+            ev0.record()
+            for t in range(7):
+                qb.qlora_nf4_quantize(ws7[t], out=qs7[t], ws=wsq)
+                qb.qlora_nf4_dequantize(qs7[t], torch.bfloat16, out=outs7[t])
+            ev1.record()
+            torch.cuda.synchronize()
+            total_ms += ev0.elapsed_time(ev1)
+            del ws7
+        n_layer = sum(a * b for a, b in shapes)
+        st_layer = sum(qb.qlora_nf4_storage_bytes(a, b) for a, b in shapes)
+        byts = layers * 2 * (2 * n_layer + st_layer)
+        wm = {"layers": layers, "params_per_layer": n_layer, "total_ms": total_ms,
+              "ms_per_layer": total_ms / layers, "ms_80_layers": total_ms / layers * 80,
+              "bytes": byts, "gbs": byts / (total_ms * 1e-3) / 1e9,
+              "frac_of_hbm_peak": byts / (total_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"whole-model round trip: {layers} layers in {total_ms:.1f} ms "
+            f"({total_ms / layers:.3f} ms/layer, {wm['gbs']:.0f} GB/s)")
+        del qs7, outs7, wsq
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -361,6 +502,9 @@ def main():
         "roofline": roofline,
         "rows": rows,
         "decode": decode,
+        "mlp65b": mlp,
+        "dequant_solo": dq_solo,
+        "whole_model_roundtrip": wm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

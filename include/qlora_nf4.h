@@ -136,13 +136,16 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
  *     Y = X W^T + scale * (X A^T) B^T
  * with W the NF4 + DQ weight [N, K] dequantized block by block on the fly.
  *   X      bf16 [M, K] (device)
- *   W      NF4 weight with rows = N, cols = K; K must be a multiple of 64
+ *   W      NF4 weight with rows = N, cols = K; N and K must be multiples
+ *          of 64
  *   A      fp32 [r, K], B fp32 [N, r] (device); r = 0 with A = B = NULL
  *          means no adapter; 0 <= r <= 256
  *   scale  the LoRA scale s (alpha / r in the usual convention)
  *   Y      bf16 [M, N] (device), overwritten
  * Products run on bf16 matrix cores with fp32 accumulation; A, B and the
- * adapter activations enter them rounded to bf16. M >= 1.
+ * adapter activations enter them rounded to bf16. For M > 32 the base enters
+ * as bf16(w_i); for M <= 32 (the decode path) it enters as bf16(level) and
+ * the fp32 block scale c_b multiplies each block's partial product. M >= 1.
  */
 int qlora_linear_fwd(const void *X, int64_t M, const qlora_nf4_weight *W,
                      const float *A, const float *B, int32_t r, float scale,
