@@ -48,9 +48,6 @@ hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, uint8_t *codes
 hipError_t launch_dequantize(const uint8_t *codes, const int8_t *absmax_q,
                              const float *dq_scale, const float *dq_mean, int64_t n,
                              void *out, bool out_bf16, hipStream_t s);
-// Per-block scales c_b (fp32 [nb]) of the reconstruction, for the GEMM kernels.
-hipError_t launch_block_scales(const int8_t *absmax_q, const float *dq_scale,
-                               const float *dq_mean, int64_t nb, float *cs, hipStream_t s);
 
 // ------------------------------------------------------------------ linear
 struct LinearArgs {

@@ -12,17 +12,16 @@
 // fp32 values of the definition in qlora_nf4.h.
 //
 // Kernels
-//   k_absmax_codes  one workgroup per DQ block (256 absmax blocks = 16384
-//                   elements): coalesced 16-byte loads, per-64 absmax by lane
-//                   shuffles, nearest-level codes, packed stores, fp32 absmax
+//   k_absmax_codes  workgroups loop over DQ blocks (256 absmax blocks = 16384
+//                   elements), the next block's loads in flight: coalesced
+//                   16-byte loads, per-64 absmax by DPP lane exchanges, nearest-level codes, packed stores, fp32 absmax
 //                   to the workspace and the fp64 tree sum of the DQ block's
 //                   256 constants.
-//   k_tree256       sums aligned 256-entry groups of fp64 partials in the same
-//                   tree shape (repeated until one value is left).
-//   k_dq_codes      one workgroup per DQ block: mean, per-block scale, int8 codes.
+//   k_tree_mean     one workgroup completes the fp64 tree over the per-DQ-block
+//                   partials, pairwise level by level in LDS, and writes the mean.
+//   k_dq_codes      one workgroup per DQ block: per-block scale and int8 codes.
 //   k_dequant       one workgroup per DQ block: per-block scales in LDS, then
 //                   4-byte code loads expanded to fp32 or bf16 stores.
-//   k_block_scales  the per-block reconstruction scale c_b for the GEMMs.
 #include "internal.h"
 
 namespace qnf4 {
@@ -30,7 +29,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kElemsPerDq = kBlock * kDqBlock;  // 16384
-constexpr int kCells = 258;                      // z-cells -129 .. 128
+constexpr int kCells = 257;                      // trunc(z) = -128 .. 128
 
 // Exact code from an fp32 y already equal to fp32(x / a): number of
 // thresholds strictly below y.
@@ -41,27 +40,32 @@ __device__ __forceinline__ int code_from_y(float y, const Nf4Tables &t) {
   return c;
 }
 
-// The fast code search works on z = fp32(x * fp32(128 / a)), which is within
-// 2^-15 of 128 * fp32(x / a) when 2^-100 <= a <= 2^100 (two roundings of
-// relative size 2^-24 each on a value of magnitude <= 128, plus the rounding
-// of the exact quotient). A lookup table over unit cells of z gives, for the
-// cell floor(z), the number of thresholds certainly below any y whose z lies
-// in the cell, and the one threshold (scaled by 128) that may lie within the
-// cell or 2^-13 of it. When z is within 2^-14 of that threshold the element
-// is recomputed with a correctly rounded division instead.
+// The fast code search works on z = fp32(x * 128 r), r = the hardware
+// reciprocal of a (within 1 ulp): |z - 128 x / a| <= 128 (2^-23 + 2^-24) and
+// |128 fp32(x / a) - 128 x / a| <= 2^-17 for |x| <= a, so z is within 2^-15.5
+// of 128 fp32(x / a) when 2^-100 <= a <= 2^100; and |z| < 129. A table over
+// the cells of trunc(z) (cell t covers [t, t + 1) for t > 0, (t - 1, t] for
+// t < 0 and (-1, 1) for t = 0) gives the number of thresholds certainly below
+// any z of the cell and the one threshold tz (scaled by 128) that may lie
+// within the cell or 2^-13 of it (thresholds are more than 9 apart in z).
+// Entry: (tz or +inf, base count as int bits). The code is base + (z > tz);
+// when z is within 2^-14 of tz the element is recomputed with a correctly
+// rounded division instead.
 __device__ void build_lut(float2 *lut, const Nf4Tables &t) {
   for (int c = threadIdx.x; c < kCells; c += blockDim.x) {
-    const float lo = static_cast<float>(c - 129);
-    const float hi = lo + 1.0f;
+    const int iz = c - 128;
+    const float lo = static_cast<float>(iz > 0 ? iz : iz - 1);
+    const float hi = static_cast<float>(iz < 0 ? iz : iz + 1);
     const float win = 0x1p-13f;
     int base = 0;
     float tc = __builtin_huge_valf();
+#pragma unroll
     for (int i = 0; i < 15; ++i) {
       const float tz = t.thr[i] * 128.0f;  // exact (power-of-two scaling)
-      if (tz < lo - win) ++base;
-      else if (tz < hi + win) tc = tz;
+      base += tz < lo - win ? 1 : 0;
+      tc = (tz >= lo - win && tz < hi + win) ? tz : tc;
     }
-    lut[c] = make_float2(tc, static_cast<float>(base));
+    lut[c] = make_float2(tc, __int_as_float(base));
   }
 }
 
@@ -90,12 +94,87 @@ struct InTraits<false> {  // fp32 weights: 4 elements per 16-byte load
   }
 };
 
+// Maximum of a non-negative float over aligned groups of G lanes (G = 8 or
+// 16), by DPP lane exchanges on the bit patterns (for non-negative floats the
+// unsigned order is the float order): quad swaps, then the half-row mirror
+// (lane i with 7 - i) and, for 16, the row mirror (lane i with 15 - i).
+template <int G>
+__device__ __forceinline__ float block_max(float v) {
+  static_assert(G == 8 || G == 16, "8 or 16 lanes per block");
+  uint32_t u = __float_as_uint(v);
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0xB1, 0xF, 0xF, false)));
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x4E, 0xF, 0xF, false)));
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x141, 0xF, 0xF, false)));
+  if (G == 16) u = max(u, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x140, 0xF, 0xF, false)));
+  return __uint_as_float(u);
+}
+
+// One lane's share of a pass: kEpl elements of one 64-block. Returns the
+// block absmax; writes the packed codes. kGuard handles a tensor tail.
+template <bool kBf16, bool kGuard>
+__device__ __forceinline__ float code_lane(const uint4 &raw, int64_t e, int64_t n, uint8_t *__restrict__ codes,
+                                           const float2 *lut, const Nf4Tables &tab) {
+  using IT = InTraits<kBf16>;
+  constexpr int kEpl = IT::kEpl;
+  constexpr int kLpb = kBlock / kEpl;   // lanes per 64-block
+  float x[kEpl];
+  IT::widen(raw, x);
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kEpl; ++i) m = fmaxf(m, fabsf(x[i]));
+  const float a = block_max<kLpb>(m);
+
+  const bool fast_scale = (a == 0.0f) || (a >= 0x1p-100f && a <= 0x1p100f);
+  // Outside the fast range the lookup runs on z = 0 (always a valid cell)
+  // and the exact path below recomputes every code of the lane.
+  const float r128 = (a == 0.0f || !fast_scale) ? 0.0f : __fmul_rn(__builtin_amdgcn_rcpf(a), 128.0f);
+  int c[kEpl];
+  bool near = !fast_scale;
+#pragma unroll
+  for (int i = 0; i < kEpl; ++i) {
+    const float z = __fmul_rn(x[i], r128);
+    const float2 en = lut[static_cast<int>(z) + 128];   // truncation: |z| < 129
+    c[i] = __float_as_int(en.y) + ((z > en.x) ? 1 : 0);
+    near |= fabsf(__fsub_rn(z, en.x)) <= 0x1p-14f;
+  }
+  if (near) {  // rare: exact division for this lane's elements
+#pragma unroll
+    for (int i = 0; i < kEpl; ++i) {
+      const float y = (a == 0.0f) ? 0.0f : __fdiv_rn(x[i], a);
+      c[i] = code_from_y(y, tab);
+    }
+  }
+  if (kGuard) {
+#pragma unroll
+    for (int i = 0; i < kEpl; ++i)
+      if (e + i >= n) c[i] = 0;  // padding nibble of an odd tail
+  }
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < kEpl / 2; ++j)
+    word |= static_cast<uint32_t>((c[2 * j] << 4) | c[2 * j + 1]) << (8 * j);
+  const int64_t byte0 = e / 2;
+  if (!kGuard || e + kEpl <= n) {
+    if (kBf16) *reinterpret_cast<uint32_t *>(codes + byte0) = word;
+    else *reinterpret_cast<uint16_t *>(codes + byte0) = static_cast<uint16_t>(word);
+  } else {
+    const int64_t nbytes = (n + 1) / 2;
+    for (int j = 0; j < kEpl / 2; ++j)
+      if (byte0 + j < nbytes) codes[byte0 + j] = static_cast<uint8_t>(word >> (8 * j));
+  }
+  return a;
+}
+
+// Workgroups loop over DQ blocks d = blockIdx.x + i * gridDim.x (256 absmax
+// blocks = 16384 elements each): absmax and codes of its 256 blocks, the fp32
+// absmax to the workspace and the fp64 tree sum of the 256 constants. The
+// next DQ block's loads are issued before the current one is coded.
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void k_absmax_codes(const uint8_t *__restrict__ W, int64_t n,
                                                            uint8_t *__restrict__ codes,
                                                            float *__restrict__ absmax_ws,
                                                            double *__restrict__ partial,
-                                                           int64_t nb, Nf4Tables tab) {
+                                                           int64_t nb, int64_t nd, Nf4Tables tab) {
   using IT = InTraits<kBf16>;
   constexpr int kEpl = IT::kEpl;                    // elements per lane
   constexpr int kLpb = kBlock / kEpl;               // lanes per 64-block
@@ -106,133 +185,144 @@ __global__ __launch_bounds__(kThreads) void k_absmax_codes(const uint8_t *__rest
   __shared__ float sa[kDqBlock];
   __shared__ double wsum[kThreads / 64];
 
-  build_lut(lut, tab);
-
-  const int64_t d = blockIdx.x;
   const int tid = threadIdx.x;
-  const int64_t e0 = d * kElemsPerDq;
-  const int64_t nbytes = (n + 1) / 2;
-
-  // Issue every load of the DQ block first (memory-level parallelism).
-  uint4 raw[kPasses];
+  auto elem = [&](int64_t d, int pass) {
+    return d * kElemsPerDq + static_cast<int64_t>(pass) * kThreads * kEpl + static_cast<int64_t>(tid) * kEpl;
+  };
+  auto full = [&](int64_t d) { return (d + 1) * kElemsPerDq <= n; };
+  // loads of a DQ block; a block with a tail is loaded element by element
+  auto load = [&](int64_t d, uint4 *raw) {
+    if (full(d)) {
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int64_t e = e0 + static_cast<int64_t>(p) * kThreads * kEpl + static_cast<int64_t>(tid) * kEpl;
-    if (e + kEpl <= n) {
-      raw[p] = *reinterpret_cast<const uint4 *>(W + e * kEsz);
+      for (int p = 0; p < kPasses; ++p) raw[p] = *reinterpret_cast<const uint4 *>(W + elem(d, p) * kEsz);
     } else {
-      uint32_t tmp[4] = {0u, 0u, 0u, 0u};
-      for (int i = 0; i < kEpl; ++i) {
-        if (e + i < n) {
-          if (kBf16) {
-            uint32_t h = reinterpret_cast<const uint16_t *>(W)[e + i];
-            tmp[i / 2] |= h << (16 * (i % 2));
-          } else {
-            tmp[i] = reinterpret_cast<const uint32_t *>(W)[e + i];
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p) {
+        const int64_t e = elem(d, p);
+        uint32_t tmp[4] = {0u, 0u, 0u, 0u};
+        for (int i = 0; i < kEpl; ++i) {
+          if (e + i < n) {
+            if (kBf16) tmp[i / 2] |= static_cast<uint32_t>(reinterpret_cast<const uint16_t *>(W)[e + i]) << (16 * (i % 2));
+            else tmp[i] = reinterpret_cast<const uint32_t *>(W)[e + i];
           }
         }
-      }
-      raw[p] = make_uint4(tmp[0], tmp[1], tmp[2], tmp[3]);
-    }
-  }
-  __syncthreads();  // LUT ready
-
-#pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int64_t e = e0 + static_cast<int64_t>(p) * kThreads * kEpl + static_cast<int64_t>(tid) * kEpl;
-    float x[kEpl];
-    IT::widen(raw[p], x);
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kEpl; ++i) m = fmaxf(m, fabsf(x[i]));
-#pragma unroll
-    for (int off = 1; off < kLpb; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-    const float a = m;
-
-    const bool fast_scale = (a == 0.0f) || (a >= 0x1p-100f && a <= 0x1p100f);
-    // Outside the fast range the lookup runs on z = 0 (always a valid cell)
-    // and the exact path below recomputes every code of the lane.
-    const float r128 = (a == 0.0f || !fast_scale) ? 0.0f : __fmul_rn(__fdiv_rn(1.0f, a), 128.0f);
-    int c[kEpl];
-    bool near = !fast_scale;
-#pragma unroll
-    for (int i = 0; i < kEpl; ++i) {
-      const float z = __fmul_rn(x[i], r128);
-      int cell = static_cast<int>(floorf(z)) + 129;
-      cell = min(max(cell, 0), kCells - 1);
-      const float2 en = lut[cell];
-      c[i] = static_cast<int>(en.y) + ((z > en.x) ? 1 : 0);
-      near |= fabsf(__fsub_rn(z, en.x)) <= 0x1p-14f;
-    }
-    if (near) {  // rare: exact division for this lane's elements
-#pragma unroll
-      for (int i = 0; i < kEpl; ++i) {
-        const float y = (a == 0.0f) ? 0.0f : __fdiv_rn(x[i], a);
-        c[i] = code_from_y(y, tab);
+        raw[p] = make_uint4(tmp[0], tmp[1], tmp[2], tmp[3]);
       }
     }
-#pragma unroll
-    for (int i = 0; i < kEpl; ++i)
-      if (e + i >= n) c[i] = 0;  // padding nibble of an odd tail
+  };
 
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < kEpl / 2; ++j)
-      word |= static_cast<uint32_t>((c[2 * j] << 4) | c[2 * j + 1]) << (8 * j);
-    const int64_t byte0 = e / 2;
-    if (e + kEpl <= n) {
-      if (kBf16) *reinterpret_cast<uint32_t *>(codes + byte0) = word;
-      else *reinterpret_cast<uint16_t *>(codes + byte0) = static_cast<uint16_t>(word);
-    } else {
-      for (int j = 0; j < kEpl / 2; ++j)
-        if (byte0 + j < nbytes) codes[byte0 + j] = static_cast<uint8_t>(word >> (8 * j));
-    }
+  int64_t d = blockIdx.x;
+  uint4 raw[kPasses];
+  if (d < nd) load(d, raw);
+  build_lut(lut, tab);
+  __syncthreads();  // table ready
 
-    const int64_t blk = e / kBlock;
-    if ((tid % kLpb) == 0) {
-      const int lb = static_cast<int>(blk - d * kDqBlock);
-      sa[lb] = a;
-      if (blk < nb) absmax_ws[blk] = a;
+  for (; d < nd; d += gridDim.x) {
+    uint4 nxt[kPasses];
+    const int64_t dn = d + gridDim.x;
+    if (dn < nd) load(dn, nxt);
+    const bool f = full(d);
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int64_t e = elem(d, p);
+      const float a = f ? code_lane<kBf16, false>(raw[p], e, n, codes, lut, tab)
+                        : code_lane<kBf16, true>(raw[p], e, n, codes, lut, tab);
+      if ((tid % kLpb) == 0) {
+        const int64_t blk = e / kBlock;
+        sa[blk - d * kDqBlock] = a;
+        if (blk < nb) absmax_ws[blk] = a;
+      }
     }
+    __syncthreads();
+    // fp64 tree sum of the 256 constants: xor butterflies give the
+    // adjacent-pair tree inside each wave's 64 leaves, then (w0 + w1) + (w2 + w3).
+    const int64_t myblk = d * kDqBlock + tid;
+    double v = (myblk < nb) ? static_cast<double>(sa[tid]) : 0.0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off);
+    if ((tid & 63) == 0) wsum[tid >> 6] = v;
+    __syncthreads();
+    if (tid == 0) partial[d] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) raw[p] = nxt[p];
   }
-  __syncthreads();
-
-  // fp64 tree sum of the 256 constants: xor butterflies give the adjacent-pair
-  // tree inside each wave's 64 leaves, then (w0 + w1) + (w2 + w3).
-  const int64_t myblk = d * kDqBlock + tid;
-  double v = (myblk < nb) ? static_cast<double>(sa[tid]) : 0.0;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off);
-  if ((tid & 63) == 0) wsum[tid >> 6] = v;
-  __syncthreads();
-  if (tid == 0) partial[d] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
 }
 
-__global__ __launch_bounds__(kThreads) void k_tree256(const double *__restrict__ in, int64_t L,
-                                                      double *__restrict__ out) {
-  __shared__ double wsum[kThreads / 64];
+// One workgroup: the sum of all per-DQ-block fp64 partials. The partials are
+// the 256-leaf subtrees of the perfect binary tree over all absmax constants
+// (zero padded), so the tree is completed in the same shape: aligned chunks
+// of up to kTreeChunk partials, where thread t first sums its aligned run of
+// S = top / 256 partials pairwise in registers and the 256 run sums are
+// combined by xor butterflies inside each wave, then (w0 + w1) + (w2 + w3);
+// the chunk sums are combined the same way. Writes mean = fp32(sum / nb).
+constexpr int kTreeChunk = 8192;
+constexpr int kTreeRun = kTreeChunk / kThreads;   // 32
+constexpr int kTreeMaxChunks = kThreads * kTreeRun;
+
+// Sum of the perfect binary tree over top leaves (top a power of two <= kTreeChunk)
+// src[base + i], zero past limit. Every thread gets the result.
+__device__ double tree_sum(const double *src, int64_t base, int64_t limit, int top, double *wsum) {
   const int tid = threadIdx.x;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + tid;
-  double v = (i < L) ? in[i] : 0.0;
+  const int run = top > kThreads ? top / kThreads : 1;
+  double v[kTreeRun];
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off);
-  if ((tid & 63) == 0) wsum[tid >> 6] = v;
+  for (int u = 0; u < kTreeRun; ++u) {
+    const int64_t i = base + static_cast<int64_t>(tid) * run + u;
+    v[u] = (u < run && tid * run + u < top && i < limit) ? src[i] : 0.0;
+  }
+#pragma unroll
+  for (int len = kTreeRun; len > 1; len >>= 1) {
+    if (len <= run) {
+#pragma unroll
+      for (int u = 0; u < len / 2; ++u) v[u] = v[2 * u] + v[2 * u + 1];
+    }
+  }
+  double t = v[0];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) t = t + __shfl_xor(t, off);
+  __syncthreads();   // wsum free
+  if ((tid & 63) == 0) wsum[tid >> 6] = t;
   __syncthreads();
-  if (tid == 0) out[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  return (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
 }
 
+__global__ __launch_bounds__(kThreads) void k_tree_mean(const double *__restrict__ partial, int64_t nd,
+                                                        int64_t nb, float *__restrict__ dq_mean) {
+  __shared__ double wsum[kThreads / 64];
+  __shared__ double csum[kTreeMaxChunks];
+  const int tid = threadIdx.x;
+  const int64_t nchunks = (nd + kTreeChunk - 1) / kTreeChunk;
+  int top = 1;
+  while (top < (nd < kTreeChunk ? nd : kTreeChunk)) top *= 2;
+  double total;
+  if (nchunks == 1) {
+    total = tree_sum(partial, 0, nd, top, wsum);
+  } else {
+    for (int64_t c = 0; c < nchunks; ++c) {
+      const double sc = tree_sum(partial, c * kTreeChunk, nd, kTreeChunk, wsum);
+      if (tid == 0) csum[c] = sc;
+    }
+    __syncthreads();
+    int ctop = 1;
+    while (ctop < nchunks) ctop *= 2;
+    total = tree_sum(csum, 0, nchunks, ctop, wsum);
+  }
+  if (tid == 0) dq_mean[0] = static_cast<float>(total / static_cast<double>(nb));
+}
+
+// One workgroup per DQ block: scale s2 = max |fp32(a - mean)| and int8 codes.
 __global__ __launch_bounds__(kThreads) void k_dq_codes(const float *__restrict__ absmax_ws, int64_t nb,
-                                                       const double *__restrict__ total,
+                                                       const float *__restrict__ dq_mean,
                                                        int8_t *__restrict__ absmax_q,
-                                                       float *__restrict__ dq_scale,
-                                                       float *__restrict__ dq_mean) {
+                                                       float *__restrict__ dq_scale) {
   __shared__ float wmax[kThreads / 64];
   const int tid = threadIdx.x;
   const int64_t d = blockIdx.x;
   const int64_t b = d * kDqBlock + tid;
-  const float mu = static_cast<float>(total[0] / static_cast<double>(nb));
   const bool valid = b < nb;
-  const float dv = valid ? __fsub_rn(absmax_ws[b], mu) : 0.0f;
+  const float a = valid ? absmax_ws[b] : 0.0f;
+  const float mu = dq_mean[0];
+  const float dv = valid ? __fsub_rn(a, mu) : 0.0f;
   float m = fabsf(dv);
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -247,7 +337,6 @@ __global__ __launch_bounds__(kThreads) void k_dq_codes(const float *__restrict__
   }
   if (valid) absmax_q[b] = static_cast<int8_t>(q);
   if (tid == 0) dq_scale[d] = s2;
-  if (d == 0 && tid == 0) dq_mean[0] = mu;
 }
 
 // ------------------------------------------------------------ dequantize
@@ -333,15 +422,6 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict_
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_block_scales(const int8_t *__restrict__ absmax_q,
-                                                           const float *__restrict__ dq_scale,
-                                                           const float *__restrict__ dq_mean,
-                                                           int64_t nb, float *__restrict__ cs) {
-  const int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (b >= nb) return;
-  const float kd = __fdiv_rn(dq_scale[b / kDqBlock], 127.0f);
-  cs[b] = block_scale(absmax_q[b], kd, dq_mean[0]);
-}
 
 }  // namespace
 
@@ -365,29 +445,19 @@ hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, uint8_t *codes
                                             align_up(static_cast<size_t>(nb) * 4, 256));
   const Nf4Tables &tab = nf4_tables();
   prof_begin(kProfQuantize, s);
+  const int64_t grid = nd;   // one DQ block per workgroup
   if (w_bf16)
-    hipLaunchKernelGGL(k_absmax_codes<true>, dim3(nd), dim3(kThreads), 0, s,
-                       static_cast<const uint8_t *>(W), n, codes, absmax_ws, part, nb, tab);
+    hipLaunchKernelGGL(k_absmax_codes<true>, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const uint8_t *>(W), n, codes, absmax_ws, part, nb, nd, tab);
   else
-    hipLaunchKernelGGL(k_absmax_codes<false>, dim3(nd), dim3(kThreads), 0, s,
-                       static_cast<const uint8_t *>(W), n, codes, absmax_ws, part, nb, tab);
+    hipLaunchKernelGGL(k_absmax_codes<false>, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const uint8_t *>(W), n, codes, absmax_ws, part, nb, nd, tab);
   prof_end(kProfQuantize, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // Reduce the per-DQ-block partials 256 at a time until one value is left.
-  double *cur = part;
-  int64_t L = nd;
-  while (L > 1) {
-    const int64_t L2 = ceil_div(L, kDqBlock);
-    double *next = cur + L;
-    hipLaunchKernelGGL(k_tree256, dim3(L2), dim3(kThreads), 0, s, cur, L, next);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    cur = next;
-    L = L2;
-  }
-  hipLaunchKernelGGL(k_dq_codes, dim3(nd), dim3(kThreads), 0, s, absmax_ws, nb, cur, absmax_q,
-                     dq_scale, dq_mean);
+  if (ceil_div(nd, kTreeChunk) > kTreeMaxChunks) return hipErrorInvalidValue;   // > 2^37 elements
+  hipLaunchKernelGGL(k_tree_mean, dim3(1), dim3(kThreads), 0, s, part, nd, nb, dq_mean);
+  hipLaunchKernelGGL(k_dq_codes, dim3(nd), dim3(kThreads), 0, s, absmax_ws, nb, dq_mean, absmax_q, dq_scale);
   return hipGetLastError();
 }
 
@@ -408,11 +478,5 @@ hipError_t launch_dequantize(const uint8_t *codes, const int8_t *absmax_q, const
   return hipGetLastError();
 }
 
-hipError_t launch_block_scales(const int8_t *absmax_q, const float *dq_scale,
-                               const float *dq_mean, int64_t nb, float *cs, hipStream_t s) {
-  hipLaunchKernelGGL(k_block_scales, dim3(ceil_div(nb, kThreads)), dim3(kThreads), 0, s,
-                     absmax_q, dq_scale, dq_mean, nb, cs);
-  return hipGetLastError();
-}
 
 }  // namespace qnf4
