@@ -21,6 +21,11 @@
 namespace qnf4 {
 
 constexpr int kBigThreads = 256;
+// Copies of the 256-entry level-pair table in LDS, interleaved entry by entry
+// (entry e of copy c at e * kLvCopies + c); lane l reads copy l % kLvCopies,
+// so two lanes of one 32-lane LDS pass meet in a bank only when they share a
+// copy and their entries have the same parity.
+constexpr int kLvCopies = 16;
 constexpr int kBigRows = 256;
 using CfgBig = TileCfg<256, 256, 2, 2>;
 
@@ -51,15 +56,19 @@ struct DirectRows {
   // later LDS access and barrier as depending on them: the kernels wait for
   // the copies explicitly (wait_copies) before the barrier that publishes
   // the tile. The instruction returns nothing into registers.
-  __device__ __forceinline__ void issue(int64_t red0, __bf16 *lds) const {
+  __device__ __forceinline__ void issue(int64_t red0, __bf16 *lds) const { issue_range(red0, lds, 0, kPerWave); }
+  // Copies i0 .. i0 + n - 1 of the wave's blocks only.
+  __device__ __forceinline__ void issue_range(int64_t red0, __bf16 *lds, int i0, int n) const {
     const char *p = base + red0 * 2;
     const int w = threadIdx.x >> 6;
+    // LDS byte address of this wave's block 0 (wave-uniform)
+    const uint32_t dst0 = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) __bf16 *)lds)) +
+        static_cast<uint32_t>(w) * 1024u);
 #pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-      const int b = w + 4 * i;
+    for (int i = i0; i < i0 + n; ++i) {
       const uint32_t o = min(off + static_cast<uint32_t>(i) * bstride, clamp);
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) __bf16 *)(lds + b * 512))));
+      const uint32_t dst = dst0 + static_cast<uint32_t>(i) * 4096u;   // block w + 4 i, 512 bf16 each
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                    :
                    : "s"(dst), "v"(o), "s"(p)
@@ -67,11 +76,14 @@ struct DirectRows {
     }
   }
   // Wait until the copies issued before the last N vector-memory
-  // instructions of this wave have landed in LDS.
+  // instructions of this wave have landed in LDS. The wait is the builtin,
+  // so the compiler knows the register loads before it are complete too;
+  // the empty statement keeps memory accesses from moving across it.
   template <int N>
   __device__ __forceinline__ static void wait_copies() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    asm volatile("" ::: "memory");
   }
 };
 
@@ -115,7 +127,7 @@ struct Nf4RowBig {
     for (int i = 0; i < CH; ++i) {
       const uint32_t w = q == 0 ? reg[i].x : q == 1 ? reg[i].y : q == 2 ? reg[i].z : reg[i].w;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) p.pr[i][b] = lv2[(w >> (8 * b)) & 0xFFu];
+      for (int b = 0; b < 4; ++b) p.pr[i][b] = lv2[((w >> (8 * b)) & 0xFFu) * kLvCopies];
     }
   }
   __device__ __forceinline__ void finish(__bf16 *lds, const Pairs &p, int q) const {
@@ -173,7 +185,7 @@ struct Nf4TransBig {
   };
   __device__ __forceinline__ void lookup(Pairs &p, const float2 *lv2, int q) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p.pr[i] = lv2[(reg[i] >> (8 * q)) & 0xFFu];
+    for (int i = 0; i < 8; ++i) p.pr[i] = lv2[((reg[i] >> (8 * q)) & 0xFFu) * kLvCopies];
   }
   __device__ __forceinline__ void store_part(__bf16 *lds, const float2 *lv2, int q) const {
     Pairs p;
@@ -241,54 +253,90 @@ __device__ __forceinline__ void mma_slice(Acc<CfgBig> &acc, const __bf16 *sA, co
   mma_frags(acc, f);
 }
 
-// Interleave one group of 16 MFMAs with the scale / round / store work of a
-// decode quarter (2 VALU per MFMA, then the LDS stores).
+// Interleave one slice's 16 MFMAs with the rest of its work: the LDS reads
+// for the next slice ride on the first 8 MFMAs (2 each, so they are in
+// flight early), the VALU work (read addresses, scale / round of a decode
+// quarter) fills the gaps, the decode stores come last. kLead puts most of
+// the VALU work ahead of the first MFMA (slice 0, whose fragments are read
+// just before use).
+template <bool kLead>
 __device__ __forceinline__ void interleave_group() {
+  __builtin_amdgcn_sched_group_barrier(0x002, kLead ? 28 : 4, 0);   // VALU
 #pragma unroll
-  for (int g = 0; g < 16; ++g) {
+  for (int g = 0; g < 8; ++g) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
     __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // 2 VALU
   }
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // 3 VALU
+  }
   __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);     // LDS stores
+}
+
+// Wait until at most N LDS operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_lds_below() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
 }
 
 // One step of the NF4 main loop: MFMAs on (aCur, bCur); the dense operand of
 // step sn1 is copied into aNxt; the codes in ldec (step sn1) are decoded into
 // bNxt; lload receives the codes of step sn2. The caller clamps sn1 and sn2
 // to the last step, so the body has no branches; extra copies and decodes
-// at the end land in the buffer nobody reads any more. Fragments of slice
-// kk + 1 and the codebook reads of quarter kk are issued before the MFMAs of
-// slice kk; the scale / round / store work runs between those MFMAs.
-template <class LB, class LoadFn>
+// at the end land in the buffer nobody reads any more.
+//
+// The wave issues its instructions in order, so a wait on memory stalls the
+// MFMAs queued behind it; everything a group of MFMAs consumes is therefore
+// read one group earlier. The MFMA groups are shifted by one 16-deep slice
+// against the barrier: a step starts with the MFMAs of the previous step's
+// last slice (fragments f1, read before the barrier), which cover the reads
+// of this step's first slice; then slices 0, 1, 2 follow. Decode quarter q
+// runs with group q (group 0 being the previous step's last slice), its
+// codebook pairs read one group earlier (pe even quarters, po odd ones; the
+// pairs of quarter 0 come from the codes loaded at the start of this step).
+// The copies for the next dense tile are spread over the first two groups.
+template <bool kFirst, class LB, class LoadFn>
 __device__ __forceinline__ void big_step(Acc<CfgBig> &acc, const DirectRows &da, LB &ldec, LB &lload,
-                                         LoadFn &load, int sn1, int sn2, __bf16 *aCur, __bf16 *bCur,
-                                         __bf16 *aNxt, __bf16 *bNxt, const FragAddr<128> &fa,
-                                         const FragAddr<128> &fb, const float2 *lv2) {
-  // The only vector-memory operations in flight here are the code loads of
-  // ldec, issued one step ago: complete them before issuing anything new, so
-  // that no later wait on ldec has to drain this step's copies.
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  da.issue(static_cast<int64_t>(sn1) * kBK, aNxt);
-  load(lload, sn2);
-  __builtin_amdgcn_sched_barrier(0);
-  Frags f0, f1;
+                                         LoadFn &load, int sn1, int sn2, const __bf16 *aCur,
+                                         const __bf16 *bCur, __bf16 *aNxt, __bf16 *bNxt,
+                                         const FragAddr<128> &fa, const FragAddr<128> &fb, const float2 *lv2,
+                                         Frags &f0, Frags &f1, typename LB::Pairs &pe,
+                                         typename LB::Pairs &po) {
+  const int64_t red1 = static_cast<int64_t>(sn1) * kBK;
+  // group 0: last slice of the previous step; reads for slice 0
   load_frags(f0, aCur, bCur, fa, fb, 0);
+  load(lload, sn2);
+  da.issue_range(red1, aNxt, 0, DirectRows::kPerWave / 2);
+  ldec.lookup(po, lv2, 1);
+  if (!kFirst) mma_frags(acc, f1);
+  ldec.finish(bNxt, pe, 0);
+  interleave_group<kFirst>();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
+  for (int kk = 0; kk < 3; ++kk) {
     Frags &cur = (kk & 1) ? f1 : f0;
     Frags &nxt = (kk & 1) ? f0 : f1;
-    if (kk < 3) load_frags(nxt, aCur, bCur, fa, fb, kk + 1);
-    typename LB::Pairs pr;
-    ldec.lookup(pr, lv2, kk);
-    __builtin_amdgcn_sched_barrier(0);
+    typename LB::Pairs &pc = (kk & 1) ? pe : po;   // quarter kk + 1
+    typename LB::Pairs &pn = (kk & 1) ? po : pe;   // quarter kk + 2 (mod 4)
+    // what this group consumes was read one group ago; only the stores of
+    // the last quarter may stay in flight
+    wait_lds_below<2>();
+    if (kk == 0) da.issue_range(red1, aNxt, DirectRows::kPerWave / 2, DirectRows::kPerWave / 2);
+    if (kk < 2)
+      ldec.lookup(pn, lv2, kk + 2);
+    else
+      lload.lookup(pn, lv2, 0);
+    load_frags(nxt, aCur, bCur, fa, fb, kk + 1);
     mma_frags(acc, cur);
-    ldec.finish(bNxt, pr, kk);
-    interleave_group();
+    ldec.finish(bNxt, pc, kk + 1);
+    interleave_group<false>();
     __builtin_amdgcn_sched_barrier(0);
   }
-  // the copies into aNxt were issued before the code loads of this step
-  DirectRows::wait_copies<LB::kLoads>();
+  DirectRows::wait_copies<0>();
   __syncthreads();
 }
 
@@ -301,26 +349,34 @@ __device__ __forceinline__ void big_mainloop_nf4(Acc<CfgBig> &acc, const DirectR
   const FragAddr<128> fa(wm * 128, lane);
   const FragAddr<128> fb(wn * 128, lane);
   const int last = steps - 1;
+  typename LB::Pairs pe, po;
+  Frags f0, f1;
 
-  // prologue: step 0 into buffers 0, codes of step 1 in l1
+  // prologue: step 0 into buffers 0, codes of step 1 in l1 and the pairs of
+  // its first decode quarter in pe
   da.issue(0, sm.a0);
   load(l0, 0);
   load(l1, min(1, last));
 #pragma unroll
   for (int q = 0; q < 4; ++q) l0.store_part(sm.b0, lv2, q);
+  l1.lookup(pe, lv2, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // steps come in pairs (buffers 0, then 1); the codes of step s + 1 are in l1
-  int s = 0;
+  // step 0 has no previous slice; then pairs of steps (buffers 1, then 0)
+  big_step<true>(acc, da, l1, l0, load, min(1, last), min(2, last), sm.a0, sm.b0, sm.a1, sm.b1, fa, fb, lv2,
+                 f0, f1, pe, po);
+  int s = 1;
   for (; s + 1 < steps; s += 2) {
-    big_step(acc, da, l1, l0, load, min(s + 1, last), min(s + 2, last), sm.a0, sm.b0, sm.a1, sm.b1,
-             fa, fb, lv2);
-    big_step(acc, da, l0, l1, load, min(s + 2, last), min(s + 3, last), sm.a1, sm.b1, sm.a0, sm.b0,
-             fa, fb, lv2);
+    big_step<false>(acc, da, l0, l1, load, min(s + 1, last), min(s + 2, last), sm.a1, sm.b1, sm.a0, sm.b0,
+                    fa, fb, lv2, f0, f1, pe, po);
+    big_step<false>(acc, da, l1, l0, load, min(s + 2, last), min(s + 3, last), sm.a0, sm.b0, sm.a1, sm.b1,
+                    fa, fb, lv2, f0, f1, pe, po);
   }
   if (s < steps)
-    big_step(acc, da, l1, l0, load, last, last, sm.a0, sm.b0, sm.a1, sm.b1, fa, fb, lv2);
+    big_step<false>(acc, da, l0, l1, load, last, last, sm.a1, sm.b1, sm.a0, sm.b0, fa, fb, lv2, f0, f1, pe,
+                    po);
+  mma_frags(acc, f1);   // last slice of the last step
   __builtin_amdgcn_s_waitcnt(0);   // no copy may still be landing in LDS
   __syncthreads();
 }

@@ -27,9 +27,14 @@
 namespace qnf4 {
 namespace {
 
-// LDS table of level pairs for every code byte: (level[b >> 4], level[b & 15]).
-__device__ __forceinline__ void load_level_pairs(float2 *lv2, const Nf4Tables &tab) {
-  for (int b = threadIdx.x; b < 256; b += blockDim.x) lv2[b] = make_float2(tab.lv[b >> 4], tab.lv[b & 15]);
+// LDS table of level pairs for every code byte: (level[b >> 4], level[b & 15]),
+// kLvCopies interleaved copies; returns this lane's copy.
+__device__ __forceinline__ const float2 *load_level_pairs(float2 *lv2, const Nf4Tables &tab) {
+  for (int i = threadIdx.x; i < 256 * kLvCopies; i += blockDim.x) {
+    const int b = i / kLvCopies;
+    lv2[i] = make_float2(tab.lv[b >> 4], tab.lv[b & 15]);
+  }
+  return lv2 + (threadIdx.x & (kLvCopies - 1));
 }
 
 // ------------------------------------------------------------------ forward
@@ -50,8 +55,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_fwd_big(FwdParams p, Nf4Tabl
   __shared__ __attribute__((aligned(16))) __bf16 sa0[CfgBig::kLdsA], sa1[CfgBig::kLdsA];
   __shared__ __attribute__((aligned(16))) __bf16 sb0[CfgBig::kLdsB], sb1[CfgBig::kLdsB];
   const BigSmem smem{sa0, sa1, sb0, sb1};
-  __shared__ float2 lv[256];
-  load_level_pairs(lv, tab);
+  __shared__ float2 lv_tab[256 * kLvCopies];
+  const float2 *lv = load_level_pairs(lv_tab, tab);
   int tm, tn;
   tile_of(blockIdx.x, static_cast<int>((p.M + 255) / 256), static_cast<int>((p.N + 255) / 256), tm, tn);
   const int64_t n0 = static_cast<int64_t>(tn) * 256;
@@ -93,8 +98,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_dx_big(DxParams p, Nf4Tables
   __shared__ __attribute__((aligned(16))) __bf16 sa0[CfgBig::kLdsA], sa1[CfgBig::kLdsA];
   __shared__ __attribute__((aligned(16))) __bf16 sb0[CfgBig::kLdsB], sb1[CfgBig::kLdsB];
   const BigSmem smem{sa0, sa1, sb0, sb1};
-  __shared__ float2 lv[256];
-  load_level_pairs(lv, tab);
+  __shared__ float2 lv_tab[256 * kLvCopies];
+  const float2 *lv = load_level_pairs(lv_tab, tab);
   int tm, tn;
   tile_of(blockIdx.x, static_cast<int>((p.M + 255) / 256), static_cast<int>((p.K + 255) / 256), tm, tn);
   const int64_t k0 = static_cast<int64_t>(tn) * 256;
