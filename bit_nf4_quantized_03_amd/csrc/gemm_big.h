@@ -6,11 +6,12 @@
 // Per 64-deep reduction step s:
 //   * the dense operand (X, dY or an adapter factor) of step s + 1 is copied
 //     straight from global memory into the other LDS buffer with
-//     global_load_lds_dwordx4 (no registers, no LDS store instructions);
+//     global_load_lds_dwordx4 (no registers, no LDS store instructions),
+//     spread over the first three of the step's four MFMA groups;
 //   * the NF4 codes of step s + 2 are loaded into registers;
 //   * the codes of step s + 1 (loaded one step earlier) are decoded into the
-//     other LDS buffer in four quarters, each issued after the MFMAs of one
-//     16-deep slice of step s, so decode and matrix work overlap;
+//     other LDS buffer in four quarters, one per MFMA group, so decode and
+//     matrix work overlap;
 //   * one barrier.
 // Rows past the end of M, N or K are read from a clamped (valid) row: they
 // only feed output rows or columns that are never stored.
@@ -298,7 +299,7 @@ __device__ __forceinline__ void wait_lds_below() {
 // runs with group q (group 0 being the previous step's last slice), its
 // codebook pairs read one group earlier (pe even quarters, po odd ones; the
 // pairs of quarter 0 come from the codes loaded at the start of this step).
-// The copies for the next dense tile are spread over the first two groups.
+// The copies for the next dense tile are spread over the first three groups.
 template <bool kFirst, class LB, class LoadFn>
 __device__ __forceinline__ void big_step(Acc<CfgBig> &acc, const DirectRows &da, LB &ldec, LB &lload,
                                          LoadFn &load, int sn1, int sn2, const __bf16 *aCur,
@@ -306,11 +307,14 @@ __device__ __forceinline__ void big_step(Acc<CfgBig> &acc, const DirectRows &da,
                                          const FragAddr<128> &fa, const FragAddr<128> &fb, const float2 *lv2,
                                          Frags &f0, Frags &f1, typename LB::Pairs &pe,
                                          typename LB::Pairs &po) {
+  // copies of the next dense tile per group (group 0, 1, 2), so that few
+  // vector-memory instructions queue up behind each other in any one group
+  constexpr int kDmaA = 2, kDma0 = 3, kDma1 = DirectRows::kPerWave - kDmaA - kDma0;
   const int64_t red1 = static_cast<int64_t>(sn1) * kBK;
   // group 0: last slice of the previous step; reads for slice 0
   load_frags(f0, aCur, bCur, fa, fb, 0);
   load(lload, sn2);
-  da.issue_range(red1, aNxt, 0, DirectRows::kPerWave / 2);
+  da.issue_range(red1, aNxt, 0, kDmaA);
   ldec.lookup(po, lv2, 1);
   if (!kFirst) mma_frags(acc, f1);
   ldec.finish(bNxt, pe, 0);
@@ -325,7 +329,8 @@ __device__ __forceinline__ void big_step(Acc<CfgBig> &acc, const DirectRows &da,
     // what this group consumes was read one group ago; only the stores of
     // the last quarter may stay in flight
     wait_lds_below<2>();
-    if (kk == 0) da.issue_range(red1, aNxt, DirectRows::kPerWave / 2, DirectRows::kPerWave / 2);
+    if (kk == 0) da.issue_range(red1, aNxt, kDmaA, kDma0);
+    if (kk == 1) da.issue_range(red1, aNxt, kDmaA + kDma0, kDma1);
     if (kk < 2)
       ldec.lookup(pn, lv2, kk + 2);
     else
