@@ -86,6 +86,78 @@ def load_traffic(kernel: str):
     return ent.get("bytes_per_launch")
 
 
+def _counter_per_dispatch(folder: str, counter: str, grid: int = 0):
+    """{kernel name: [counter value summed per dispatch]} from a rocprofv3 --pmc run
+    (only dispatches of `grid` work-items when grid > 0)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    per = {}
+    for path in files:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                if grid and int(row["Grid_Size"]) != grid:
+                    continue
+                key = (path, row["Dispatch_Id"])
+                name, val = row["Kernel_Name"], float(row["Counter_Value"])
+                if key in per:
+                    per[key] = (name, per[key][1] + val)
+                else:
+                    per[key] = (name, val)
+    out = {}
+    for name, val in per.values():
+        out.setdefault(name, []).append(val)
+    return out
+
+
+def write_traffic(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str):
+    """Calibrated HBM bytes per launch of the two dequant-GEMMs of the step
+    (the Llama-7B attention shape, M = N = K = 4096, r = 64).
+
+    FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch; each is scaled by
+    the factor that makes the 1 GiB copy of --calib-copy read (write) exactly
+    1 GiB (the largest dispatch of the calibration run is the copy)."""
+    gib = 1 << 30
+    cal_f = max(v for vals in _counter_per_dispatch(cal_fetch_dir, "FETCH_SIZE").values() for v in vals)
+    cal_w = max(v for vals in _counter_per_dispatch(cal_write_dir, "WRITE_SIZE").values() for v in vals)
+    ff, fw = gib / (cal_f * 1024), gib / (cal_w * 1024)
+    M = N = K = 4096
+    rp = 64
+    grid = (M // 256) * (N // 256) * 256   # the step's 256 x 256 tiles, 256 work-items each
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", grid)
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE", grid)
+    nb = N * K // 64
+    nf4 = N * K // 2 + nb + 4 * ((nb + 255) // 256) + 4
+    act, out = M * K * 2, M * N * 2
+    data = {"calibration": {"copy_bytes_each_way": gib, "fetch_kib_read": cal_f, "write_kib_read": cal_w,
+                            "fetch_factor": ff, "write_factor": fw}}
+    for key, kname in (("fwd_gemm", "k_fwd_big"), ("bwd_dx_gemm", "k_dx_big")):
+        fv = [v for n, vals in fetch.items() if kname in n for v in vals]
+        wv = [v for n, vals in write.items() if kname in n for v in vals]
+        if not fv or not wv:
+            raise SystemExit(f"{kname} missing from the counter runs")
+        f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
+        data[key] = {
+            "kernel": kname,
+            "fetch_kib_per_dispatch": f_kib,
+            "write_kib_per_dispatch": w_kib,
+            "dispatches": [len(fv), len(wv)],
+            "bytes_per_launch": f_kib * 1024 * ff + w_kib * 1024 * fw,
+            "algorithmic_read_bytes": act + nf4 + 2 * M * rp * 2,
+            "algorithmic_write_bytes": out,
+            "source_hash": kernel_source_hash(key),
+        }
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    print(json.dumps({k: (v["bytes_per_launch"] if "bytes_per_launch" in v else v) for k, v in data.items()}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,7 +174,14 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (the reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="no GPU: turn four rocprofv3 --pmc output folders (FETCH_SIZE and "
+                         "WRITE_SIZE of a short bench run, then of --calib-copy) into "
+                         "profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the path runs on a single MI355X; see the design notes on sharding).",
