@@ -53,6 +53,11 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python bit_nf4_quantized_03_amd/build.py`")
+    # torch ships its own HIP runtime under the soname the library links
+    # against (libamdhip64.so.7). Loading torch first makes the library bind
+    # to that same runtime; loading the library first would put a second HIP
+    # runtime in the process, which then finds no device.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     i64, sz, vp, i32, f32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
     wp = ctypes.POINTER(_Weight)
