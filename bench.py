@@ -391,6 +391,9 @@ def main():
             Yd = torch.empty((Mx, Nx), dtype=torch.bfloat16, device=dev)
             wsd = torch.empty(qb.qlora_linear_workspace_bytes(Mx, Nx, Kx, r), dtype=torch.uint8, device=dev)
             R_saved, R = R, Rd
+            # one untimed call first: a kernel's first launch also loads its code
+            qb.qlora_linear_fwd(Xd, qd[0], Ad[0], Bd[0], w2.s, ws=wsd, out=Yd)
+            torch.cuda.synchronize()
             qb.qlora_profile_reset()
             qb.qlora_profile_enable(True)
             for i in range(Rd):
