@@ -1,7 +1,10 @@
 // Large-tile main loop for the two dequant-GEMMs (forward Y and input
-// gradient dX): a 256 x 256 output tile per workgroup of four waves, each
-// wave a 128 x 128 block of 4 x 4 v_mfma_f32_32x32x16_bf16 tiles whose 256
-// fp32 accumulators live in the accumulation registers.
+// gradient dX): a 256 x 256 output tile per workgroup, built on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulators in registers. Two layouts:
+// four waves of 128 x 128 (CfgBig, one wave per SIMD, 256 accumulation
+// registers each) and eight waves of 128 x 64 (CfgBig8, two waves per SIMD,
+// 128 accumulators each, so one wave's waits are covered by the other's
+// MFMAs).
 //
 // Per 64-deep reduction step s:
 //   * the dense operand (X, dY or an adapter factor) of step s + 1 is copied
@@ -21,7 +24,8 @@
 
 namespace qnf4 {
 
-constexpr int kBigThreads = 256;
+constexpr int kBigThreads = 256;    // four waves: 128 x 128 per wave
+constexpr int kBig8Threads = 512;   // eight waves: 128 x 64 per wave, two waves per SIMD
 // Copies of the 256-entry level-pair table in LDS, interleaved entry by entry
 // (entry e of copy c at e * kLvCopies + c); lane l reads copy l % kLvCopies,
 // so two lanes of one 32-lane LDS pass meet in a bank only when they share a
@@ -29,26 +33,30 @@ constexpr int kBigThreads = 256;
 constexpr int kLvCopies = 16;
 constexpr int kBigRows = 256;
 using CfgBig = TileCfg<256, 256, 2, 2>;
+using CfgBig8 = TileCfg<256, 256, 2, 4>;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Dense bf16 operand rows [256][64] of src (row stride ld) via LDS DMA. Each
-// wave copies eight 1 KB blocks (8 rows each); lane L of a block fetches the
-// global chunk that the swizzle places at byte 16 L of the block.
-struct DirectRows {
-  static constexpr int kPerWave = kBigRows / 8 / (kBigThreads / 64);  // 8
+// Dense bf16 operand rows [256][64] of src (row stride ld) via LDS DMA. The
+// tile is 32 blocks of 1 KB (8 rows each); wave w copies blocks w + W i
+// (W waves), and lane L of a block fetches the global chunk that the swizzle
+// places at byte 16 L of the block.
+template <int T>
+struct DirectRowsT {
+  static constexpr int kWaves = T / 64;
+  static constexpr int kPerWave = kBigRows / 8 / kWaves;   // 8 or 4
   const char *base;
   uint32_t off;     // block 0 of this wave; block i adds i * bstride
-  uint32_t bstride; // bytes between the wave's blocks (32 rows)
+  uint32_t bstride; // bytes between the wave's blocks (8 W rows)
   uint32_t clamp;   // largest valid row offset (bytes), for a tile crossing the end
-  __device__ DirectRows(const void *src, int64_t ld, int64_t nrows, int64_t row0) {
+  __device__ DirectRowsT(const void *src, int64_t ld, int64_t nrows, int64_t row0) {
     base = static_cast<const char *>(src) + row0 * ld * 2;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int rb = lane >> 3, p = lane & 7;
-    const int row = 8 * w + rb;              // the swizzle of row 8 (w + 4 i) + rb does not depend on i
+    const int row = 8 * w + rb;              // the swizzle of row 8 (w + W i) + rb does not depend on i
     const int c = p ^ swz(row);
     off = static_cast<uint32_t>((row * ld + 8 * c) * 2);
-    bstride = static_cast<uint32_t>(32 * ld * 2);
+    bstride = static_cast<uint32_t>(8 * kWaves * ld * 2);
     const int64_t last = (nrows - 1 - row0) < 255 ? (nrows - 1 - row0) : 255;
     clamp = static_cast<uint32_t>((last * ld + 8 * c) * 2);
   }
@@ -69,7 +77,7 @@ struct DirectRows {
 #pragma unroll
     for (int i = i0; i < i0 + n; ++i) {
       const uint32_t o = min(off + static_cast<uint32_t>(i) * bstride, clamp);
-      const uint32_t dst = dst0 + static_cast<uint32_t>(i) * 4096u;   // block w + 4 i, 512 bf16 each
+      const uint32_t dst = dst0 + static_cast<uint32_t>(i) * (1024u * kWaves);   // block w + W i
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                    :
                    : "s"(dst), "v"(o), "s"(p)
@@ -87,21 +95,24 @@ struct DirectRows {
     asm volatile("" ::: "memory");
   }
 };
+using DirectRows = DirectRowsT<kBigThreads>;
 
 // Forward B operand: NF4 rows n (reduction along k). Thread t decodes the
-// 16-byte code chunks of rows t/2 and 128 + t/2, half t&1 of the 64-step.
-struct Nf4RowBig {
-  static constexpr int CH = 2;
+// 16-byte code chunks of rows t/2 + (T/2) i (i < 512/T), half t&1 of the
+// 64-step.
+template <int T>
+struct Nf4RowBigT {
+  static constexpr int CH = 512 / T;
   const uint8_t *cbase;
   const float *sbase;
   uint32_t coff[CH], soff[CH];
   uint4 reg[CH];
   float sc[CH];
-  __device__ Nf4RowBig(const uint8_t *c, const float *s, int64_t N, int64_t K, int64_t row0)
+  __device__ Nf4RowBigT(const uint8_t *c, const float *s, int64_t N, int64_t K, int64_t row0)
       : cbase(c + row0 * K / 2), sbase(s + row0 * K / kBlock) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int idx = threadIdx.x + i * kBigThreads;
+      const int idx = threadIdx.x + i * T;
       int64_t n = row0 + (idx >> 1);
       if (n >= N) n = N - 1;
       coff[i] = static_cast<uint32_t>((n - row0) * K / 2 + (idx & 1) * 16);
@@ -118,6 +129,7 @@ struct Nf4RowBig {
     }
   }
   static constexpr int kLoads = 2 * CH;   // VMEM instructions issued by load()
+  static constexpr int kWrites = CH;      // LDS stores per decode quarter
   // Quarter q = code word q of each chunk (8 elements per chunk): the level
   // pairs are fetched by lookup(), scaled, rounded and stored by finish().
   struct Pairs {
@@ -134,7 +146,7 @@ struct Nf4RowBig {
   __device__ __forceinline__ void finish(__bf16 *lds, const Pairs &p, int q) const {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int idx = threadIdx.x + i * kBigThreads;
+      const int idx = threadIdx.x + i * T;
       uint32_t ow[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b)
@@ -149,6 +161,7 @@ struct Nf4RowBig {
     finish(lds, p, q);
   }
 };
+using Nf4RowBig = Nf4RowBigT<kBigThreads>;
 
 // Input-gradient B operand: NF4 decoded transposed (output row k, reduction
 // along n). One unit of 8 rows n x 8 columns k per thread (see TransUnits);
@@ -181,6 +194,7 @@ struct Nf4TransBig {
     }
   }
   static constexpr int kLoads = 16;
+  static constexpr int kWrites = 2;
   struct Pairs {
     float2 pr[8];
   };
@@ -211,70 +225,61 @@ struct Nf4TransBig {
   }
 };
 
-// Wait until at most `n` vector-memory operations of this wave are still in
-// flight (the LDS DMA copies were issued before the last n code loads).
-template <int N>
-__device__ __forceinline__ void wait_vmem_below() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// The four LDS tiles of the large-tile kernels, as distinct objects so that
-// alias analysis can tell the DMA target of a step from the tiles it reads.
-struct BigSmem {
-  __bf16 *a0, *a1, *b0, *b1;
-};
-
-// Fragments of one 16-deep slice for a wave's 128 x 128 block.
+// Fragments of one 16-deep slice for a wave's WTM x WTN block.
+template <class Cfg>
 struct Frags {
-  bf16x8 a[4], b[4];
+  bf16x8 a[Cfg::TM], b[Cfg::TN];
 };
 
-__device__ __forceinline__ void load_frags(Frags &f, const __bf16 *sA, const __bf16 *sB,
-                                           const FragAddr<128> &fa, const FragAddr<128> &fb, int kk) {
+template <class Cfg>
+__device__ __forceinline__ void load_frags(Frags<Cfg> &f, const __bf16 *sA, const __bf16 *sB,
+                                           const FragAddr<Cfg::WTM> &fa, const FragAddr<Cfg::WTN> &fb, int kk) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8 *>(sA + fa.off[kk] + i * 32 * kLDK);
+  for (int i = 0; i < Cfg::TM; ++i) f.a[i] = *reinterpret_cast<const bf16x8 *>(sA + fa.off[kk] + i * 32 * kLDK);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(sB + fb.off[kk] + j * 32 * kLDK);
+  for (int j = 0; j < Cfg::TN; ++j) f.b[j] = *reinterpret_cast<const bf16x8 *>(sB + fb.off[kk] + j * 32 * kLDK);
 }
 
-__device__ __forceinline__ void mma_frags(Acc<CfgBig> &acc, const Frags &f) {
+template <class Cfg>
+__device__ __forceinline__ void mma_frags(Acc<Cfg> &acc, const Frags<Cfg> &f) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < Cfg::TN; ++j)
       acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.v[i][j], 0, 0, 0);
 }
 
 // MFMAs of one 16-deep slice kk of the current tiles.
-__device__ __forceinline__ void mma_slice(Acc<CfgBig> &acc, const __bf16 *sA, const __bf16 *sB,
-                                          const FragAddr<128> &fa, const FragAddr<128> &fb, int kk) {
-  Frags f;
+template <class Cfg>
+__device__ __forceinline__ void mma_slice(Acc<Cfg> &acc, const __bf16 *sA, const __bf16 *sB,
+                                          const FragAddr<Cfg::WTM> &fa, const FragAddr<Cfg::WTN> &fb, int kk) {
+  Frags<Cfg> f;
   load_frags(f, sA, sB, fa, fb, kk);
   mma_frags(acc, f);
 }
 
-// Interleave one slice's 16 MFMAs with the rest of its work: the LDS reads
-// for the next slice ride on the first 8 MFMAs (2 each, so they are in
+// Interleave one slice's MFMAs with the rest of its work: the LDS reads for
+// the next slice ride two to an MFMA on the first MFMAs (so they are in
 // flight early), the VALU work (read addresses, scale / round of a decode
 // quarter) fills the gaps, the decode stores come last. kLead puts most of
-// the VALU work ahead of the first MFMA (slice 0, whose fragments are read
-// just before use).
-template <bool kLead>
+// the VALU work ahead of the first MFMA.
+template <class Cfg, int kReads, int kWrites, bool kLead>
 __device__ __forceinline__ void interleave_group() {
+  constexpr int kMfma = Cfg::TM * Cfg::TN;
+  constexpr int kWithReads = (kReads + 1) / 2 < kMfma ? (kReads + 1) / 2 : kMfma;
   __builtin_amdgcn_sched_group_barrier(0x002, kLead ? 28 : 4, 0);   // VALU
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
+  for (int g = 0; g < kWithReads; ++g) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
     __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // 2 VALU
   }
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
+  for (int g = kWithReads; g < kMfma; ++g) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // 3 VALU
   }
-  __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);     // LDS stores
+  __builtin_amdgcn_sched_group_barrier(0x200, kWrites, 0);   // LDS stores
 }
 
 // Wait until at most N LDS operations of this wave are in flight.
@@ -283,6 +288,12 @@ __device__ __forceinline__ void wait_lds_below() {
   static_assert(N >= 0 && N < 16, "lgkmcnt range");
   __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
 }
+
+// The four LDS tiles of the large-tile kernels, as distinct objects so that
+// alias analysis can tell the DMA target of a step from the tiles it reads.
+struct BigSmem {
+  __bf16 *a0, *a1, *b0, *b1;
+};
 
 // One step of the NF4 main loop: MFMAs on (aCur, bCur); the dense operand of
 // step sn1 is copied into aNxt; the codes in ldec (step sn1) are decoded into
@@ -300,16 +311,17 @@ __device__ __forceinline__ void wait_lds_below() {
 // codebook pairs read one group earlier (pe even quarters, po odd ones; the
 // pairs of quarter 0 come from the codes loaded at the start of this step).
 // The copies for the next dense tile are spread over the first three groups.
-template <bool kFirst, class LB, class LoadFn>
-__device__ __forceinline__ void big_step(Acc<CfgBig> &acc, const DirectRows &da, LB &ldec, LB &lload,
-                                         LoadFn &load, int sn1, int sn2, const __bf16 *aCur,
-                                         const __bf16 *bCur, __bf16 *aNxt, __bf16 *bNxt,
-                                         const FragAddr<128> &fa, const FragAddr<128> &fb, const float2 *lv2,
-                                         Frags &f0, Frags &f1, typename LB::Pairs &pe,
-                                         typename LB::Pairs &po) {
+template <class Cfg, bool kFirst, class DA, class LB, class LoadFn>
+__device__ __forceinline__ void big_step(Acc<Cfg> &acc, const DA &da, LB &ldec, LB &lload, LoadFn &load, int sn1,
+                                         int sn2, const __bf16 *aCur, const __bf16 *bCur, __bf16 *aNxt,
+                                         __bf16 *bNxt, const FragAddr<Cfg::WTM> &fa,
+                                         const FragAddr<Cfg::WTN> &fb, const float2 *lv2, Frags<Cfg> &f0,
+                                         Frags<Cfg> &f1, typename LB::Pairs &pe, typename LB::Pairs &po) {
   // copies of the next dense tile per group (group 0, 1, 2), so that few
   // vector-memory instructions queue up behind each other in any one group
-  constexpr int kDmaA = 2, kDma0 = 3, kDma1 = DirectRows::kPerWave - kDmaA - kDma0;
+  constexpr int kDmaA = DA::kPerWave / 4, kDma0 = (DA::kPerWave - kDmaA + 1) / 2;
+  constexpr int kDma1 = DA::kPerWave - kDmaA - kDma0;
+  constexpr int kReads = Cfg::TM + Cfg::TN + 4 * sizeof(typename LB::Pairs) / sizeof(float2) / 4;
   const int64_t red1 = static_cast<int64_t>(sn1) * kBK;
   // group 0: last slice of the previous step; reads for slice 0
   load_frags(f0, aCur, bCur, fa, fb, 0);
@@ -318,19 +330,19 @@ __device__ __forceinline__ void big_step(Acc<CfgBig> &acc, const DirectRows &da,
   ldec.lookup(po, lv2, 1);
   if (!kFirst) mma_frags(acc, f1);
   ldec.finish(bNxt, pe, 0);
-  interleave_group<kFirst>();
+  interleave_group<Cfg, kReads, LB::kWrites, kFirst>();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
-    Frags &cur = (kk & 1) ? f1 : f0;
-    Frags &nxt = (kk & 1) ? f0 : f1;
+    Frags<Cfg> &cur = (kk & 1) ? f1 : f0;
+    Frags<Cfg> &nxt = (kk & 1) ? f0 : f1;
     typename LB::Pairs &pc = (kk & 1) ? pe : po;   // quarter kk + 1
     typename LB::Pairs &pn = (kk & 1) ? po : pe;   // quarter kk + 2 (mod 4)
     // what this group consumes was read one group ago; only the stores of
     // the last quarter may stay in flight
-    wait_lds_below<2>();
+    wait_lds_below<LB::kWrites>();
     if (kk == 0) da.issue_range(red1, aNxt, kDmaA, kDma0);
-    if (kk == 1) da.issue_range(red1, aNxt, kDmaA + kDma0, kDma1);
+    if (kk == 1 && kDma1 > 0) da.issue_range(red1, aNxt, kDmaA + kDma0, kDma1);
     if (kk < 2)
       ldec.lookup(pn, lv2, kk + 2);
     else
@@ -338,24 +350,23 @@ __device__ __forceinline__ void big_step(Acc<CfgBig> &acc, const DirectRows &da,
     load_frags(nxt, aCur, bCur, fa, fb, kk + 1);
     mma_frags(acc, cur);
     ldec.finish(bNxt, pc, kk + 1);
-    interleave_group<false>();
+    interleave_group<Cfg, kReads, LB::kWrites, false>();
     __builtin_amdgcn_sched_barrier(0);
   }
-  DirectRows::wait_copies<0>();
+  DA::template wait_copies<0>();
   __syncthreads();
 }
 
-template <class LB, class LoadFn>
-__device__ __forceinline__ void big_mainloop_nf4(Acc<CfgBig> &acc, const DirectRows &da, LB &l0, LB &l1,
-                                                 LoadFn load, int steps, const BigSmem &sm,
-                                                 const float2 *lv2) {
+template <class Cfg, class DA, class LB, class LoadFn>
+__device__ __forceinline__ void big_mainloop_nf4(Acc<Cfg> &acc, const DA &da, LB &l0, LB &l1, LoadFn load,
+                                                 int steps, const BigSmem &sm, const float2 *lv2) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w / CfgBig::WAVES_N, wn = w % CfgBig::WAVES_N;
-  const FragAddr<128> fa(wm * 128, lane);
-  const FragAddr<128> fb(wn * 128, lane);
+  const int wm = w / Cfg::WAVES_N, wn = w % Cfg::WAVES_N;
+  const FragAddr<Cfg::WTM> fa(wm * Cfg::WTM, lane);
+  const FragAddr<Cfg::WTN> fb(wn * Cfg::WTN, lane);
   const int last = steps - 1;
   typename LB::Pairs pe, po;
-  Frags f0, f1;
+  Frags<Cfg> f0, f1;
 
   // prologue: step 0 into buffers 0, codes of step 1 in l1 and the pairs of
   // its first decode quarter in pe
@@ -369,30 +380,31 @@ __device__ __forceinline__ void big_mainloop_nf4(Acc<CfgBig> &acc, const DirectR
   __syncthreads();
 
   // step 0 has no previous slice; then pairs of steps (buffers 1, then 0)
-  big_step<true>(acc, da, l1, l0, load, min(1, last), min(2, last), sm.a0, sm.b0, sm.a1, sm.b1, fa, fb, lv2,
-                 f0, f1, pe, po);
+  big_step<Cfg, true>(acc, da, l1, l0, load, min(1, last), min(2, last), sm.a0, sm.b0, sm.a1, sm.b1, fa, fb, lv2,
+                      f0, f1, pe, po);
   int s = 1;
   for (; s + 1 < steps; s += 2) {
-    big_step<false>(acc, da, l0, l1, load, min(s + 1, last), min(s + 2, last), sm.a1, sm.b1, sm.a0, sm.b0,
-                    fa, fb, lv2, f0, f1, pe, po);
-    big_step<false>(acc, da, l1, l0, load, min(s + 2, last), min(s + 3, last), sm.a0, sm.b0, sm.a1, sm.b1,
-                    fa, fb, lv2, f0, f1, pe, po);
+    big_step<Cfg, false>(acc, da, l0, l1, load, min(s + 1, last), min(s + 2, last), sm.a1, sm.b1, sm.a0,
+                         sm.b0, fa, fb, lv2, f0, f1, pe, po);
+    big_step<Cfg, false>(acc, da, l1, l0, load, min(s + 2, last), min(s + 3, last), sm.a0, sm.b0, sm.a1,
+                         sm.b1, fa, fb, lv2, f0, f1, pe, po);
   }
   if (s < steps)
-    big_step<false>(acc, da, l0, l1, load, last, last, sm.a1, sm.b1, sm.a0, sm.b0, fa, fb, lv2, f0, f1, pe,
-                    po);
+    big_step<Cfg, false>(acc, da, l0, l1, load, last, last, sm.a1, sm.b1, sm.a0, sm.b0, fa, fb, lv2, f0, f1, pe,
+                         po);
   mma_frags(acc, f1);   // last slice of the last step
   __builtin_amdgcn_s_waitcnt(0);   // no copy may still be landing in LDS
   __syncthreads();
 }
 
 // Both operands dense bf16 (the adapter steps): plain double-buffered loop.
-__device__ __forceinline__ void big_mainloop_dense(Acc<CfgBig> &acc, const DirectRows &da,
-                                                   const DirectRows &db, int steps, const BigSmem &sm) {
+template <class Cfg, class DA>
+__device__ __forceinline__ void big_mainloop_dense(Acc<Cfg> &acc, const DA &da, const DA &db, int steps,
+                                                   const BigSmem &sm) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w / CfgBig::WAVES_N, wn = w % CfgBig::WAVES_N;
-  const FragAddr<128> fa(wm * 128, lane);
-  const FragAddr<128> fb(wn * 128, lane);
+  const int wm = w / Cfg::WAVES_N, wn = w % Cfg::WAVES_N;
+  const FragAddr<Cfg::WTM> fa(wm * Cfg::WTM, lane);
+  const FragAddr<Cfg::WTN> fb(wn * Cfg::WTN, lane);
   for (int s = 0; s < steps; ++s) {
     da.issue(static_cast<int64_t>(s) * kBK, sm.a0);
     db.issue(static_cast<int64_t>(s) * kBK, sm.b0);

@@ -50,10 +50,14 @@ struct FwdParams {
   int rp;
 };
 
-// Large-M forward: one 256 x 256 tile of Y per workgroup (XCD-aware order).
-__global__ __launch_bounds__(kBigThreads, 1) void k_fwd_big(FwdParams p, Nf4Tables tab) {
-  __shared__ __attribute__((aligned(16))) __bf16 sa0[CfgBig::kLdsA], sa1[CfgBig::kLdsA];
-  __shared__ __attribute__((aligned(16))) __bf16 sb0[CfgBig::kLdsB], sb1[CfgBig::kLdsB];
+// Large-M forward: one 256 x 256 tile of Y per workgroup (XCD-aware order),
+// run with eight waves (CfgBig8): two waves per SIMD cover each other's
+// waits, at 128 x 64 accumulators per wave.
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::kThreads, 1) void k_fwd_big(FwdParams p, Nf4Tables tab) {
+  constexpr int T = Cfg::kThreads;
+  __shared__ __attribute__((aligned(16))) __bf16 sa0[Cfg::kLdsA], sa1[Cfg::kLdsA];
+  __shared__ __attribute__((aligned(16))) __bf16 sb0[Cfg::kLdsB], sb1[Cfg::kLdsB];
   const BigSmem smem{sa0, sa1, sb0, sb1};
   __shared__ float2 lv_tab[256 * kLvCopies];
   const float2 *lv = load_level_pairs(lv_tab, tab);
@@ -62,22 +66,22 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_fwd_big(FwdParams p, Nf4Tabl
   const int64_t n0 = static_cast<int64_t>(tn) * 256;
   const int64_t m0 = static_cast<int64_t>(tm) * 256;
   __syncthreads();
-  Acc<CfgBig> acc;
+  Acc<Cfg> acc;
   acc.zero();
   {
-    DirectRows da(p.X, p.K, p.M, m0);
-    Nf4RowBig l0(p.codes, p.cs, p.N, p.K, n0), l1 = l0;
-    auto load = [](Nf4RowBig &l, int s) { l.load(static_cast<int64_t>(s) * kBK); };
-    big_mainloop_nf4(acc, da, l0, l1, load, static_cast<int>(p.K / kBK), smem, lv);
+    DirectRowsT<T> da(p.X, p.K, p.M, m0);
+    Nf4RowBigT<T> l0(p.codes, p.cs, p.N, p.K, n0), l1 = l0;
+    auto load = [](Nf4RowBigT<T> &l, int s) { l.load(static_cast<int64_t>(s) * kBK); };
+    big_mainloop_nf4<Cfg>(acc, da, l0, l1, load, static_cast<int>(p.K / kBK), smem, lv);
   }
   if (p.rp > 0) {
-    DirectRows da(p.Hs, p.rp, p.M, m0), db(p.Bb, p.rp, p.N, n0);
-    big_mainloop_dense(acc, da, db, p.rp / kBK, smem);
+    DirectRowsT<T> da(p.Hs, p.rp, p.M, m0), db(p.Bb, p.rp, p.N, n0);
+    big_mainloop_dense<Cfg>(acc, da, db, p.rp / kBK, smem);
   }
   if (m0 + 256 <= p.M && n0 + 256 <= p.N)
-    store_bf16<CfgBig, false>(acc, static_cast<__bf16 *>(p.Y), p.N, p.M, p.N, m0, n0, 1.0f);
+    store_bf16<Cfg, false>(acc, static_cast<__bf16 *>(p.Y), p.N, p.M, p.N, m0, n0, 1.0f);
   else
-    store_bf16<CfgBig, true>(acc, static_cast<__bf16 *>(p.Y), p.N, p.M, p.N, m0, n0, 1.0f);
+    store_bf16<Cfg, true>(acc, static_cast<__bf16 *>(p.Y), p.N, p.M, p.N, m0, n0, 1.0f);
 }
 
 // ------------------------------------------------------------- backward dX
@@ -93,10 +97,13 @@ struct DxParams {
   int rp;
 };
 
-// Input gradient: one 256 x 256 tile of dX per workgroup (XCD-aware order).
+// Input gradient: one 256 x 256 tile of dX per workgroup of four waves
+// (XCD-aware order). Eight waves, as in the forward, ran slower here: the
+// transposed decode needs more registers than two waves per SIMD leave.
 __global__ __launch_bounds__(kBigThreads, 1) void k_dx_big(DxParams p, Nf4Tables tab) {
-  __shared__ __attribute__((aligned(16))) __bf16 sa0[CfgBig::kLdsA], sa1[CfgBig::kLdsA];
-  __shared__ __attribute__((aligned(16))) __bf16 sb0[CfgBig::kLdsB], sb1[CfgBig::kLdsB];
+  using Cfg = CfgBig;
+  __shared__ __attribute__((aligned(16))) __bf16 sa0[Cfg::kLdsA], sa1[Cfg::kLdsA];
+  __shared__ __attribute__((aligned(16))) __bf16 sb0[Cfg::kLdsB], sb1[Cfg::kLdsB];
   const BigSmem smem{sa0, sa1, sb0, sb1};
   __shared__ float2 lv_tab[256 * kLvCopies];
   const float2 *lv = load_level_pairs(lv_tab, tab);
@@ -105,23 +112,23 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_dx_big(DxParams p, Nf4Tables
   const int64_t k0 = static_cast<int64_t>(tn) * 256;
   const int64_t m0 = static_cast<int64_t>(tm) * 256;
   __syncthreads();
-  Acc<CfgBig> acc;
+  Acc<Cfg> acc;
   acc.zero();
   {
     DirectRows da(p.dY, p.N, p.M, m0);
     Nf4TransBig l0(p.codes, p.cs, p.K, k0), l1 = l0;
     const int64_t K = p.K;
     auto load = [K](Nf4TransBig &l, int s) { l.load(static_cast<int64_t>(s) * kBK, K); };
-    big_mainloop_nf4(acc, da, l0, l1, load, static_cast<int>(p.N / kBK), smem, lv);
+    big_mainloop_nf4<Cfg>(acc, da, l0, l1, load, static_cast<int>(p.N / kBK), smem, lv);
   }
   if (p.rp > 0) {
     DirectRows da(p.dHb, p.rp, p.M, m0), db(p.Atb, p.rp, p.K, k0);
-    big_mainloop_dense(acc, da, db, p.rp / kBK, smem);
+    big_mainloop_dense<Cfg>(acc, da, db, p.rp / kBK, smem);
   }
   if (m0 + 256 <= p.M && k0 + 256 <= p.K)
-    store_bf16<CfgBig, false>(acc, static_cast<__bf16 *>(p.dX), p.K, p.M, p.K, m0, k0, 1.0f);
+    store_bf16<Cfg, false>(acc, static_cast<__bf16 *>(p.dX), p.K, p.M, p.K, m0, k0, 1.0f);
   else
-    store_bf16<CfgBig, true>(acc, static_cast<__bf16 *>(p.dX), p.K, p.M, p.K, m0, k0, 1.0f);
+    store_bf16<Cfg, true>(acc, static_cast<__bf16 *>(p.dX), p.K, p.M, p.K, m0, k0, 1.0f);
 }
 
 // ------------------------------------------------ adapter pre-work
@@ -509,7 +516,7 @@ hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const 
   FwdParams fp{X, a.codes, b.cs, b.Hs, b.Bb, Y, a.M, a.N, a.K, pl.rp};
   dim3 g(grid_blocks(a.N, 256) * grid_blocks(a.M, 256), 1, 1);
   prof_begin(kProfFwdGemm, s);
-  hipLaunchKernelGGL(k_fwd_big, g, dim3(kBigThreads), 0, s, fp, nf4_tables());
+  hipLaunchKernelGGL(k_fwd_big<CfgBig8>, g, dim3(CfgBig8::kThreads), 0, s, fp, nf4_tables());
   prof_end(kProfFwdGemm, s);
   return hipGetLastError();
 }
