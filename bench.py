@@ -86,9 +86,8 @@ def load_traffic(kernel: str):
     return ent.get("bytes_per_launch")
 
 
-def _counter_per_dispatch(folder: str, counter: str, grid: int = 0):
-    """{kernel name: [counter value summed per dispatch]} from a rocprofv3 --pmc run
-    (only dispatches of `grid` work-items when grid > 0)."""
+def _counter_per_dispatch(folder: str, counter: str):
+    """{kernel name: [counter value summed per dispatch]} from a rocprofv3 --pmc run."""
     import csv
     import glob
     files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
@@ -99,8 +98,6 @@ def _counter_per_dispatch(folder: str, counter: str, grid: int = 0):
         with open(path) as f:
             for row in csv.DictReader(f):
                 if row["Counter_Name"] != counter:
-                    continue
-                if grid and int(row["Grid_Size"]) != grid:
                     continue
                 key = (path, row["Dispatch_Id"])
                 name, val = row["Kernel_Name"], float(row["Counter_Value"])
@@ -127,9 +124,10 @@ def write_traffic(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_
     ff, fw = gib / (cal_f * 1024), gib / (cal_w * 1024)
     M = N = K = 4096
     rp = 64
-    grid = (M // 256) * (N // 256) * 256   # the step's 256 x 256 tiles, 256 work-items each
-    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", grid)
-    write = _counter_per_dispatch(write_dir, "WRITE_SIZE", grid)
+    # the counter runs time the step only (--no-large), so every dispatch of
+    # the two kernels is one of the step's
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
     nb = N * K // 64
     nf4 = N * K // 2 + nb + 4 * ((nb + 255) // 256) + 4
     act, out = M * K * 2, M * N * 2
