@@ -548,8 +548,8 @@ def main():
 
     dom_row = rows[dom]
     roofline = {
-        "kernel": "k_fwd (fused NF4 dequant-GEMM + LoRA fold)" if dom == "fwd_gemm"
-        else "k_bwd_dx (transposed NF4 dequant-GEMM + dH A fold)",
+        "kernel": "k_fwd_big (fused NF4 dequant-GEMM + LoRA fold)" if dom == "fwd_gemm"
+        else "k_dx_big (transposed NF4 dequant-GEMM + dH A fold)",
         "bound": "mfma",
         "achieved": dom_row["tflops"],
         "peak": BF16_PEAK_TFLOPS,
