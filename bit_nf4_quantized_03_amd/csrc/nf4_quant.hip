@@ -360,30 +360,33 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict_
   const float mu = dq_mean[0];
 
   for (int64_t d = blockIdx.x; d * kElemsPerDq < n; d += gridDim.x) {
-    __syncthreads();  // previous iteration done with cs
-    {
-      const float kd = __fdiv_rn(dq_scale[d], 127.0f);
-      const int64_t b = d * kDqBlock + tid;
-      cs[tid] = (b < nb) ? block_scale(absmax_q[b], kd, mu) : 0.0f;
-    }
-    __syncthreads();
+    // The code loads go out first: they do not depend on the scales, so the
+    // codes and the scale inputs travel together.
     const int64_t byte_base = d * (kElemsPerDq / 2);
     // 8 pieces of 4 code bytes (8 elements) per thread; piece p of thread t
     // starts at byte 4t + 1024p of the DQ block, so each wave touches a
     // contiguous 256-byte run of codes per piece.
     uint32_t w[8];
+    if ((d + 1) * kElemsPerDq <= n) {   // whole DQ block: every load in flight at once
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int64_t byte0 = byte_base + 4 * tid + 1024 * p;
-      if (byte0 + 4 <= nbytes) {
-        w[p] = *reinterpret_cast<const uint32_t *>(codes + byte0);
-      } else {
+      for (int p = 0; p < 8; ++p)
+        w[p] = *reinterpret_cast<const uint32_t *>(codes + byte_base + 4 * tid + 1024 * p);
+    } else {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int64_t byte0 = byte_base + 4 * tid + 1024 * p;
         uint32_t t = 0;
         for (int j = 0; j < 4; ++j)
           if (byte0 + j < nbytes) t |= static_cast<uint32_t>(codes[byte0 + j]) << (8 * j);
         w[p] = t;
       }
     }
+    const int64_t b = d * kDqBlock + tid;
+    const float s2 = dq_scale[d];
+    const int8_t q = (b < nb) ? absmax_q[b] : static_cast<int8_t>(0);
+    __syncthreads();  // previous iteration done with cs
+    cs[tid] = (b < nb) ? block_scale(q, __fdiv_rn(s2, 127.0f), mu) : 0.0f;
+    __syncthreads();
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int64_t e = d * kElemsPerDq + 8 * tid + 2048 * p;  // first element of the piece
