@@ -234,6 +234,22 @@ __global__ __launch_bounds__(256) void k_adapter_down(DownParams p) {
   store_f32<CfgSkinny>(acc, part + static_cast<int64_t>(z) * p.M * p.rp, p.rp, p.M, p.rp, m0, j0);
 }
 
+// sum_z part[z * plane + e] for z = 0 .. splits - 1, added in that order; the
+// loads go out eight at a time (clamped indices, the extra terms dropped), so
+// the sum costs a few memory round trips instead of one per split.
+__device__ __forceinline__ float split_sum(const float *part, int64_t plane, int64_t e, int splits) {
+  float v = 0.0f;
+  for (int z0 = 0; z0 < splits; z0 += 8) {
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = part[static_cast<int64_t>(min(z0 + u, splits - 1)) * plane + e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (z0 + u < splits) v += t[u];
+  }
+  return v;
+}
+
 // k_adapter_finish sums the split partials into the bf16 operands of the
 // adapter steps: Hs [M][rp] = bf16(s * sum_z h_part) and (backward)
 // dHb [M][rp] = bf16(s * sum_z dh_part), in a fixed order.
@@ -254,9 +270,7 @@ __global__ __launch_bounds__(256) void k_adapter_finish(FinishParams p) {
     const int64_t e = second ? i - p.n : i;
     const float *part = second ? p.dh_part : p.h_part;
     const int splits = second ? p.dh_splits : p.h_splits;
-    float v = 0.0f;
-    if (static_cast<int>(e % p.rp) < p.r)
-      for (int z = 0; z < splits; ++z) v += part[static_cast<int64_t>(z) * p.n + e];
+    const float v = static_cast<int>(e % p.rp) < p.r ? split_sum(part, p.n, e, splits) : 0.0f;
     (second ? p.dHb : p.Hs)[e] = static_cast<__bf16>(p.scale * v);
   }
 }
@@ -321,15 +335,11 @@ __global__ __launch_bounds__(256) void k_grad_finish(GradFinishParams p) {
   const int64_t na = static_cast<int64_t>(p.r) * p.K, nbb = p.N * p.r;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < na + nbb;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    float v = 0.0f;
     if (i < na) {   // dA [r][K] from [splits][rp][K]
-      for (int z = 0; z < p.a_splits; ++z) v += p.a_part[static_cast<int64_t>(z) * p.rp * p.K + i];
-      p.dA[i] = v;
+      p.dA[i] = split_sum(p.a_part, static_cast<int64_t>(p.rp) * p.K, i, p.a_splits);
     } else {        // dB [N][r] from [splits][N][rp]
       const int64_t e = i - na, row = e / p.r, col = e % p.r;
-      for (int z = 0; z < p.b_splits; ++z)
-        v += p.b_part[static_cast<int64_t>(z) * p.N * p.rp + row * p.rp + col];
-      p.dB[e] = v;
+      p.dB[e] = split_sum(p.b_part, p.N * p.rp, row * p.rp + col, p.b_splits);
     }
   }
 }
