@@ -8,22 +8,24 @@
 // One pass handles up to 16 rows of X (more rows run as further passes).
 // Two launches per pass:
 //   k_gemv         grid = (column strips of 128) x (K splits of 1024). A wave
-//                  owns 16 output columns. Each lane issues every code and
-//                  absmax load of its split up front, so the whole weight is in
-//                  flight at once; while those loads travel the workgroup
-//                  stages its X chunk in LDS, forms its share of the split
-//                  partials of H = X A^T and builds a byte table. Then, per
-//                  64-element block, a lane maps its 8 code bytes to bf16 level
-//                  pairs (8 table lookups = two MFMA operands), runs two
+//                  owns 16 output columns. The workgroup first loads its X
+//                  chunk, absmax bytes and DQ constants and stages X and a
+//                  byte table in LDS; then each lane streams the code words of
+//                  its split, two to six super-blocks ahead of their use (the
+//                  stream starts after X is staged, so X is not queued behind
+//                  it). Per 64-element block, a lane maps its code bytes to
+//                  bf16 level pairs (table lookups = MFMA B operands), runs
 //                  v_mfma_f32_16x16x32_bf16 into a temporary and adds
 //                  c_b * temporary to its accumulator: the block scale is
 //                  applied once per block and output, not once per weight.
+//                  The workgroups then form the split partials of H = X A^T.
 //   k_gemv_finish  per output: the fixed-order sum of the split partials plus
 //                  the adapter term bf16(s H) bf16(B)^T (MFMA), rounded to bf16.
-// Within a block the reduction order is free: lane group g (lane / 16) takes
-// elements 16g .. 16g + 15 (8 contiguous code bytes) and reads X in the same
-// order. Levels enter the MFMA as bf16 and c_b is applied in fp32, so Y
-// differs from bf16(X bf16(W-hat)^T) at the bf16 operand level.
+// For M <= 4 (M <= 8) one MFMA spans 4 (2) blocks in block-diagonal row
+// groups (see k_gemv). Within a block the reduction order is free: each lane
+// group takes contiguous code bytes and reads X in the same order. Levels
+// enter the MFMA as bf16 and c_b is applied in fp32, so Y differs from
+// bf16(X bf16(W-hat)^T) at the bf16 operand level.
 #include <algorithm>
 
 #include "gemm_core.h"
