@@ -428,14 +428,10 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict_
 
 }  // namespace
 
+// fp32 absmax [nb], then one fp64 tree partial per DQ block [nd].
 size_t quantize_ws_bytes(int64_t n) {
   const int64_t nb = ceil_div(n, kBlock);
-  int64_t partials = 0;
-  for (int64_t L = ceil_div(nb, kDqBlock);; L = ceil_div(L, kDqBlock)) {
-    partials += L;
-    if (L == 1) break;
-  }
-  return align_up(static_cast<size_t>(nb) * 4, 256) + static_cast<size_t>(partials) * 8;
+  return align_up(static_cast<size_t>(nb) * 4, 256) + static_cast<size_t>(ceil_div(nb, kDqBlock)) * 8;
 }
 
 hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, uint8_t *codes,
