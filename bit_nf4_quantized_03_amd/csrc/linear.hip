@@ -210,28 +210,133 @@ struct DownParams {
   int h_splits, h_steps, dh_splits, dh_steps;
 };
 
-__global__ __launch_bounds__(256) void k_adapter_down(DownParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (CfgSkinny::kLdsA + CfgSkinny::kLdsB)];
+// Skinny product tile of k_adapter_down: 128 rows of P (32 per wave) by the
+// 64 adapter columns j0 .. j0 + 63 of Q, over a range of the reduction.
+//
+// P is streamed straight from memory into the MFMA A operand (no LDS): the
+// reduction is processed in chunks of CS 64-deep steps, and within a chunk
+// lane (row i = lane % 32, half h = lane / 32) holds the contiguous run
+// k = h * 32 CS + 8 s .. + 7 for slices s = 0 .. 4 CS - 1. The Q operand is
+// staged in LDS as [64][264] bf16 (rows padded by 16 bytes, so that the 32
+// rows a fragment read touches start in different banks) and read with the
+// same permutation of k, so each MFMA pairs equal k.
+constexpr int kDownWaves = 4;
+constexpr int kDownRows = 32 * kDownWaves;
+constexpr int kDownThreads = 64 * kDownWaves;
+constexpr int kDownLd = 256 + 8;      // LDS row of the Q chunk (bf16)
+constexpr int kDownLds = 64 * kDownLd;   // bf16 per Q buffer
+
+template <int CS>
+struct DownChunk {
+  static constexpr int kSlices = 4 * CS;                 // 16-deep MFMA slices
+  static constexpr int kQLoads = 64 * 8 * CS / kDownThreads;
+  uint4 x[kSlices];
+  uint4 q[kQLoads];
+  __device__ __forceinline__ const char *xptr(const char *xrow, int64_t kc, int h) const {
+    return xrow + (kc + h * 32 * CS) * 2;
+  }
+  __device__ __forceinline__ void load_x(const char *xrow, int64_t kc, int h) {
+    const char *px = xptr(xrow, kc, h);
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s) x[s] = *reinterpret_cast<const uint4 *>(px + 16 * s);
+  }
+  __device__ __forceinline__ void load_q(const __bf16 *Q, int64_t ldq, int64_t kc) {
+#pragma unroll
+    for (int u = 0; u < kQLoads; ++u) {
+      const int idx = threadIdx.x + u * kDownThreads, j = idx / (8 * CS), c = idx % (8 * CS);
+      q[u] = *reinterpret_cast<const uint4 *>(Q + j * ldq + kc + 8 * c);
+    }
+  }
+  __device__ __forceinline__ void stage(__bf16 *lds) const {
+#pragma unroll
+    for (int u = 0; u < kQLoads; ++u) {
+      const int idx = threadIdx.x + u * kDownThreads, j = idx / (8 * CS), c = idx % (8 * CS);
+      *reinterpret_cast<uint4 *>(lds + j * kDownLd + 8 * c) = q[u];
+    }
+  }
+  // MFMAs of the staged chunk; with NEXT, slice s of the next chunk (at px)
+  // is loaded into x[s] as soon as slice s has been consumed.
+  template <bool NEXT>
+  __device__ __forceinline__ void mma(f32x16 (&acc)[2], const __bf16 *lds, int lane, const char *px) {
+    const __bf16 *lb = lds + (lane & 31) * kDownLd + (lane >> 5) * 32 * CS;
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, x[s]);
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(lb + jb * 32 * kDownLd + 8 * s);
+        acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[jb], 0, 0, 0);
+      }
+      if (NEXT) x[s] = *reinterpret_cast<const uint4 *>(px + 16 * s);
+    }
+  }
+};
+
+// `n` chunks of CS steps from reduction offset k0. The Q chunk alternates
+// between the two LDS buffers, one barrier per chunk; the P operand streams
+// through the registers slice by slice. On entry and on exit the LDS is free.
+template <int CS>
+__device__ __forceinline__ void down_chunks(f32x16 (&acc)[2], const char *xrow, const __bf16 *Q, int64_t ldq,
+                                            int64_t k0, int n, __bf16 *lds) {
+  if (n <= 0) return;
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  constexpr int64_t kLen = 64 * CS;
+  DownChunk<CS> c;
+  c.load_x(xrow, k0, h);
+  c.load_q(Q, ldq, k0);
+  for (int i = 0; i < n; ++i) {
+    __bf16 *buf = lds + (i & 1) * kDownLds;
+    c.stage(buf);
+    __syncthreads();
+    const int64_t kn = k0 + (i + 1) * kLen;
+    if (i + 1 < n) {
+      c.load_q(Q, ldq, kn);
+      c.template mma<true>(acc, buf, lane, c.xptr(xrow, kn, h));
+    } else {
+      c.template mma<false>(acc, buf, lane, nullptr);
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kDownThreads, 2) void k_adapter_down(DownParams p) {
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * kDownLds];
   int g = blockIdx.x;
   const int per = p.jt * p.mt;
   const bool is_h = g < per * p.h_splits;
   if (!is_h) g -= per * p.h_splits;
   const int z = g / per, t = g % per;
   const int64_t j0 = static_cast<int64_t>(t % p.jt) * 64;
-  const int64_t m0 = static_cast<int64_t>(t / p.jt) * 128;
-  const void *P = is_h ? p.X : p.dY;
-  const __bf16 *Q = is_h ? p.Ab : p.Bt;
+  const int64_t m0 = static_cast<int64_t>(t / p.jt) * kDownRows;
+  const char *P = static_cast<const char *>(is_h ? p.X : p.dY);
+  const __bf16 *Q = (is_h ? p.Ab : p.Bt) + j0 * (is_h ? p.K : p.N);
   const int64_t L = is_h ? p.K : p.N;
   const int steps_per = is_h ? p.h_steps : p.dh_steps;
-  float *part = is_h ? p.h_part : p.dh_part;
+  float *part = (is_h ? p.h_part : p.dh_part) + static_cast<int64_t>(z) * p.M * p.rp;
   const int total = static_cast<int>(L / kBK);
   const int s0 = z * steps_per, steps = min(steps_per, total - s0);
-  Acc<CfgSkinny> acc;
-  acc.zero();
-  RowBf16<128, 256> la(P, L, p.M, m0);
-  RowBf16<64, 256> lb(Q, L, p.rp, j0);
-  mainloop<CfgSkinny>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
-  store_f32<CfgSkinny>(acc, part + static_cast<int64_t>(z) * p.M * p.rp, p.rp, p.M, p.rp, m0, j0);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // rows past M read row M - 1 (always valid) and are not stored
+  const int64_t row = min(m0 + 32 * w + (lane & 31), p.M - 1);
+  const char *xrow = P + row * L * 2;
+  f32x16 acc[2];
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[jb][v] = 0.0f;
+  const int64_t k0 = static_cast<int64_t>(s0) * kBK;
+  down_chunks<4>(acc, xrow, Q, L, k0, steps / 4, lds);
+  down_chunks<1>(acc, xrow, Q, L, k0 + (steps / 4) * 4 * kBK, steps % 4, lds);
+  const int h = lane >> 5;
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb) {
+    const int64_t col = j0 + jb * 32 + (lane & 31);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t r = m0 + 32 * w + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (r < p.M) part[r * p.rp + col] = acc[jb][v];
+    }
+  }
 }
 
 // sum_z part[z * plane + e] for z = 0 .. splits - 1, added in that order; the
@@ -347,6 +452,7 @@ __global__ __launch_bounds__(256) void k_grad_finish(GradFinishParams p) {
 // ------------------------------------------------------------- tile configs
 constexpr int kSmallM = 32;
 constexpr int kTargetGroups = 512;
+constexpr int kDownGroups = 256;
 
 int64_t grid_blocks(int64_t n, int64_t b) { return ceil_div(n, b); }
 
@@ -356,8 +462,8 @@ struct Split {
 };
 
 // Split `steps` reduction steps so that tiles * splits reaches the target.
-Split choose_split(int64_t tiles, int steps, int max_splits) {
-  int want = static_cast<int>(ceil_div(kTargetGroups, tiles > 0 ? tiles : 1));
+Split choose_split(int64_t tiles, int steps, int max_splits, int target = kTargetGroups) {
+  int want = static_cast<int>(ceil_div(target, tiles > 0 ? tiles : 1));
   want = std::max(1, std::min({want, steps, max_splits}));
   const int per = static_cast<int>(ceil_div(steps, want));
   return {static_cast<int>(ceil_div(steps, per)), per};
@@ -386,9 +492,9 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int r) {
   pl.rp = static_cast<int>(ceil_div(r, kBK) * kBK);
   pl.small = M <= kSmallM;
   const int ksteps = static_cast<int>(K / kBK), nsteps = static_cast<int>(N / kBK);
-  const int64_t skinny_tiles = grid_blocks(M, 128) * grid_blocks(pl.rp, 64);
-  pl.down = choose_split(skinny_tiles, ksteps, 64);
-  pl.dh = choose_split(skinny_tiles, nsteps, 64);
+  const int64_t skinny_tiles = grid_blocks(M, kDownRows) * grid_blocks(pl.rp, 64);
+  pl.down = choose_split(skinny_tiles, ksteps, 64, kDownGroups);
+  pl.dh = choose_split(skinny_tiles, nsteps, 64, kDownGroups);
   const int msteps = static_cast<int>(ceil_div(M, kBK));
   pl.ga = choose_split(grid_blocks(pl.rp, 64) * grid_blocks(K, 256), msteps, 8);
   pl.gb = choose_split(grid_blocks(N, 256) * grid_blocks(pl.rp, 64), msteps, 8);
@@ -477,13 +583,13 @@ hipError_t run_adapter_down_finish(const LinearArgs &a, const Plan &pl, const Bu
   dp.K = a.K;
   dp.rp = pl.rp;
   dp.jt = pl.rp / 64;
-  dp.mt = static_cast<int>(ceil_div(a.M, 128));
+  dp.mt = static_cast<int>(ceil_div(a.M, kDownRows));
   dp.h_splits = pl.down.splits;
   dp.h_steps = pl.down.steps_per_split;
   dp.dh_splits = backward ? pl.dh.splits : 0;
   dp.dh_steps = pl.dh.steps_per_split;
   const int64_t groups = static_cast<int64_t>(dp.jt) * dp.mt * (dp.h_splits + dp.dh_splits);
-  hipLaunchKernelGGL(k_adapter_down, dim3(groups), dim3(256), 0, s, dp);
+  hipLaunchKernelGGL(k_adapter_down, dim3(groups), dim3(kDownThreads), 0, s, dp);
   FinishParams fp{};
   fp.h_part = b.down_part;
   fp.dh_part = b.dh_part;
