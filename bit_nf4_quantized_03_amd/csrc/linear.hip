@@ -8,10 +8,11 @@
 //   backward   dH = s dY B,  dX = dY W + dH A,  dA = dH^T X,  dB = s dY^T (X A^T)
 //
 // Kernel plan (all on the caller's stream, no host synchronization):
-//   k_adapter_prep    block scales c_b; bf16 copies of A, B in the layouts
-//                     the products below read (A, B^T, B, A^T)
-//   k_adapter_down    split partials of H = X A^T and (backward) of dY B
-//   k_adapter_finish  Hs = bf16(s H) and (backward) dHb = bf16(s dY B)
+//   k_adapter_down    split partials of H = X A^T and (backward) of dY B,
+//                     read straight from the fp32 factors
+//   k_adapter_finish  Hs = bf16(s H), (backward) dHb = bf16(s dY B), the block
+//                     scales c_b and the bf16 adapter operand of the GEMM below
+//                     (B forward, A^T backward), one launch
 //   k_fwd_big         Y tile = [X | Hs] [W-hat | Bb]^T: the NF4 weight is decoded
 //                     into LDS step by step, the adapter term is 64-deep extra
 //                     reduction steps on the same accumulators
@@ -131,82 +132,26 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_dx_big(DxParams p, Nf4Tables
     store_bf16<Cfg, true>(acc, static_cast<__bf16 *>(p.dX), p.K, p.M, p.K, m0, k0, 1.0f);
 }
 
-// ------------------------------------------------ adapter pre-work
+// ------------------------------------------------ adapter down-projection
 //
-// k_adapter_prep (elementwise, one launch) writes, each in one segment:
-//   cs  [nb]      block scales c_b of the NF4 weight (for the GEMMs)
-//   Ab  [rp][K]   bf16(A), rows >= r zero          (operand of H = X A^T)
-//   Bt  [rp][N]   bf16(B^T), rows >= r zero        (operand of dY B; backward)
-//   Bb  [N][rp]   bf16(B), columns >= r zero       (forward adapter step)
-//   Atb [K][rp]   bf16(A^T), columns >= r zero     (backward adapter step)
-// k_adapter_down then computes 128 x 64 tiles of the split partials of
-// H = X Ab^T and (backward) dY Bt^T with 16-byte bf16 loads on both sides.
-
-using CfgSkinny = TileCfg<128, 64, 2, 2>;
-constexpr int kScaleBlocksPerThread = 4;
-
-struct PrepParams {
-  const int8_t *absmax_q;
-  const float *dq_scale;
-  const float *dq_mean;
-  const float *A, *B;
-  float *cs;
-  __bf16 *Ab, *Bt, *Bb, *Atb;
-  int64_t nb, N, K;
-  int r, rp;
-  int64_t n_cs, n_ab, n_bt, n_bb, n_atb;   // segment lengths (0 when absent)
-};
-
-__global__ __launch_bounds__(256) void k_adapter_prep(PrepParams p) {
-  const int64_t n_cs_items = (p.n_cs + kScaleBlocksPerThread - 1) / kScaleBlocksPerThread;
-  const int64_t total = n_cs_items + p.n_ab + p.n_bt + p.n_bb + p.n_atb;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    int64_t e = i;
-    if (e < n_cs_items) {
-      const float mu = p.dq_mean[0];
-#pragma unroll
-      for (int u = 0; u < kScaleBlocksPerThread; ++u) {
-        const int64_t b = e * kScaleBlocksPerThread + u;
-        if (b < p.nb) {
-          const float kd = __fdiv_rn(p.dq_scale[b / kDqBlock], 127.0f);
-          p.cs[b] = __fadd_rn(__fmul_rn(static_cast<float>(p.absmax_q[b]), kd), mu);
-        }
-      }
-      continue;
-    }
-    e -= n_cs_items;
-    if (e < p.n_ab) {   // Ab[j][k]
-      const int64_t j = e / p.K, k = e % p.K;
-      p.Ab[e] = static_cast<__bf16>(j < p.r ? p.A[j * p.K + k] : 0.0f);
-      continue;
-    }
-    e -= p.n_ab;
-    if (e < p.n_bt) {   // Bt[j][n]
-      const int64_t j = e / p.N, n = e % p.N;
-      p.Bt[e] = static_cast<__bf16>(j < p.r ? p.B[n * p.r + j] : 0.0f);
-      continue;
-    }
-    e -= p.n_bt;
-    if (e < p.n_bb) {   // Bb[n][j]
-      const int64_t n = e / p.rp, j = e % p.rp;
-      p.Bb[e] = static_cast<__bf16>(j < p.r ? p.B[n * p.r + j] : 0.0f);
-      continue;
-    }
-    e -= p.n_bb;        // Atb[k][j]
-    const int64_t k = e / p.rp, j = e % p.rp;
-    p.Atb[e] = static_cast<__bf16>(j < p.r ? p.A[j * p.K + k] : 0.0f);
-  }
-}
+// k_adapter_down computes split partials of H = X A^T and (backward) of
+// dY B straight from the fp32 adapter factors; k_adapter_finish then sums
+// them and, in the same launch, writes the other small operands of the big
+// GEMMs:
+//   Hs  [M][rp]   bf16(s H), columns >= r zero          (forward adapter step)
+//   dHb [M][rp]   bf16(s dY B), columns >= r zero       (backward adapter step)
+//   cs  [nb]      block scales c_b of the NF4 weight
+//   Bb  [N][rp]   bf16(B), columns >= r zero            (forward adapter step)
+//   Atb [K][rp]   bf16(A^T), columns >= r zero          (backward adapter step)
 
 struct DownParams {
   const void *X, *dY;
-  const __bf16 *Ab, *Bt;
+  const float *A, *B;        // fp32 A [r][K], B [N][r]
   float *h_part, *dh_part;   // [splits][M][rp]
   int64_t M, N, K;
-  int rp;
+  int r, rp;
   int jt;                    // rp / 64 column tiles
-  int mt;                    // M / 128 row tiles (rounded up)
+  int mt;                    // row tiles of kDownRows (rounded up)
   int h_splits, h_steps, dh_splits, dh_steps;
 };
 
@@ -217,21 +162,84 @@ struct DownParams {
 // reduction is processed in chunks of CS 64-deep steps, and within a chunk
 // lane (row i = lane % 32, half h = lane / 32) holds the contiguous run
 // k = h * 32 CS + 8 s .. + 7 for slices s = 0 .. 4 CS - 1. The Q operand is
-// staged in LDS as [64][264] bf16 (rows padded by 16 bytes, so that the 32
-// rows a fragment read touches start in different banks) and read with the
-// same permutation of k, so each MFMA pairs equal k.
+// rounded to bf16 and staged in LDS as [64][264] (rows padded by 16 bytes, so
+// that the 32 rows a fragment read touches start in different banks) and read
+// with the same permutation of k, so each MFMA pairs equal k.
 constexpr int kDownWaves = 4;
 constexpr int kDownRows = 32 * kDownWaves;
 constexpr int kDownThreads = 64 * kDownWaves;
-constexpr int kDownLd = 256 + 8;      // LDS row of the Q chunk (bf16)
+constexpr int kDownLd = 256 + 8;         // LDS row of the Q chunk (bf16)
 constexpr int kDownLds = 64 * kDownLd;   // bf16 per Q buffer
 
+// fp32 source of the Q operand: rows j0 .. j0 + 63 of Q, rows >= r zero.
+struct QSrc {
+  const float *src;
+  int64_t ld;
+  int r;
+  int j0;
+};
+
+// Q = A (row j of Q is row j of A [r][K]): 8-element runs of a row, two
+// 16-byte loads each, consecutive threads along the row.
 template <int CS>
+struct QFromRows {
+  static constexpr int kRuns = 64 * 8 * CS / kDownThreads;
+  float4 v[2 * kRuns];
+  __device__ __forceinline__ void load(const QSrc &q, int64_t kc) {
+#pragma unroll
+    for (int u = 0; u < kRuns; ++u) {
+      const int idx = threadIdx.x + u * kDownThreads, j = idx / (8 * CS), c = idx % (8 * CS);
+      const float *p = q.src + static_cast<int64_t>(min(q.j0 + j, q.r - 1)) * q.ld + kc + 8 * c;
+      v[2 * u] = *reinterpret_cast<const float4 *>(p);
+      v[2 * u + 1] = *reinterpret_cast<const float4 *>(p + 4);
+    }
+  }
+  __device__ __forceinline__ void stage(const QSrc &q, __bf16 *lds) const {
+#pragma unroll
+    for (int u = 0; u < kRuns; ++u) {
+      const int idx = threadIdx.x + u * kDownThreads, j = idx / (8 * CS), c = idx % (8 * CS);
+      const bool ok = q.j0 + j < q.r;
+      const float4 a = v[2 * u], b = v[2 * u + 1];
+      const uint4 w = make_uint4(ok ? pack_bf16x2(a.x, a.y) : 0u, ok ? pack_bf16x2(a.z, a.w) : 0u,
+                                 ok ? pack_bf16x2(b.x, b.y) : 0u, ok ? pack_bf16x2(b.z, b.w) : 0u);
+      *reinterpret_cast<uint4 *>(lds + j * kDownLd + 8 * c) = w;
+    }
+  }
+};
+
+// Q = B^T (row j of Q is column j of B [N][r]): lane j of a wave reads
+// B[n][j0 + j], so one load covers a row of B; wave w takes the pairs of
+// reduction indices n = kc + 2 (w + 4 i), + 1 and writes each pair as one
+// 4-byte LDS store.
+template <int CS>
+struct QFromCols {
+  static constexpr int kPairs = 64 * CS / 2 / kDownWaves;
+  float v[2 * kPairs];
+  __device__ __forceinline__ void load(const QSrc &q, int64_t kc) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const float *p = q.src + min(q.j0 + lane, q.r - 1);
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+      const int64_t n = kc + 2 * (w + kDownWaves * i);
+      v[2 * i] = p[n * q.ld];
+      v[2 * i + 1] = p[(n + 1) * q.ld];
+    }
+  }
+  __device__ __forceinline__ void stage(const QSrc &q, __bf16 *lds) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const bool ok = q.j0 + lane < q.r;
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i)
+      *reinterpret_cast<uint32_t *>(lds + lane * kDownLd + 2 * (w + kDownWaves * i)) =
+          ok ? pack_bf16x2(v[2 * i], v[2 * i + 1]) : 0u;
+  }
+};
+
+template <int CS, template <int> class QL>
 struct DownChunk {
-  static constexpr int kSlices = 4 * CS;                 // 16-deep MFMA slices
-  static constexpr int kQLoads = 64 * 8 * CS / kDownThreads;
+  static constexpr int kSlices = 4 * CS;   // 16-deep MFMA slices
   uint4 x[kSlices];
-  uint4 q[kQLoads];
+  QL<CS> q;
   __device__ __forceinline__ const char *xptr(const char *xrow, int64_t kc, int h) const {
     return xrow + (kc + h * 32 * CS) * 2;
   }
@@ -239,20 +247,6 @@ struct DownChunk {
     const char *px = xptr(xrow, kc, h);
 #pragma unroll
     for (int s = 0; s < kSlices; ++s) x[s] = *reinterpret_cast<const uint4 *>(px + 16 * s);
-  }
-  __device__ __forceinline__ void load_q(const __bf16 *Q, int64_t ldq, int64_t kc) {
-#pragma unroll
-    for (int u = 0; u < kQLoads; ++u) {
-      const int idx = threadIdx.x + u * kDownThreads, j = idx / (8 * CS), c = idx % (8 * CS);
-      q[u] = *reinterpret_cast<const uint4 *>(Q + j * ldq + kc + 8 * c);
-    }
-  }
-  __device__ __forceinline__ void stage(__bf16 *lds) const {
-#pragma unroll
-    for (int u = 0; u < kQLoads; ++u) {
-      const int idx = threadIdx.x + u * kDownThreads, j = idx / (8 * CS), c = idx % (8 * CS);
-      *reinterpret_cast<uint4 *>(lds + j * kDownLd + 8 * c) = q[u];
-    }
   }
   // MFMAs of the staged chunk; with NEXT, slice s of the next chunk (at px)
   // is loaded into x[s] as soon as slice s has been consumed.
@@ -275,28 +269,55 @@ struct DownChunk {
 // `n` chunks of CS steps from reduction offset k0. The Q chunk alternates
 // between the two LDS buffers, one barrier per chunk; the P operand streams
 // through the registers slice by slice. On entry and on exit the LDS is free.
-template <int CS>
-__device__ __forceinline__ void down_chunks(f32x16 (&acc)[2], const char *xrow, const __bf16 *Q, int64_t ldq,
-                                            int64_t k0, int n, __bf16 *lds) {
+template <int CS, template <int> class QL>
+__device__ __forceinline__ void down_chunks(f32x16 (&acc)[2], const char *xrow, const QSrc &qs, int64_t k0,
+                                            int n, __bf16 *lds) {
   if (n <= 0) return;
   const int lane = threadIdx.x & 63, h = lane >> 5;
   constexpr int64_t kLen = 64 * CS;
-  DownChunk<CS> c;
+  DownChunk<CS, QL> c;
   c.load_x(xrow, k0, h);
-  c.load_q(Q, ldq, k0);
+  c.q.load(qs, k0);
   for (int i = 0; i < n; ++i) {
     __bf16 *buf = lds + (i & 1) * kDownLds;
-    c.stage(buf);
+    c.q.stage(qs, buf);
     __syncthreads();
     const int64_t kn = k0 + (i + 1) * kLen;
     if (i + 1 < n) {
-      c.load_q(Q, ldq, kn);
+      c.q.load(qs, kn);
       c.template mma<true>(acc, buf, lane, c.xptr(xrow, kn, h));
     } else {
       c.template mma<false>(acc, buf, lane, nullptr);
     }
   }
   __syncthreads();
+}
+
+template <template <int> class QL>
+__device__ __forceinline__ void down_tile(const char *P, int64_t L, int64_t M, const QSrc &qs, int64_t m0,
+                                          int s0, int steps, float *part, int rp, __bf16 *lds) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // rows past M read row M - 1 (always valid) and are not stored
+  const int64_t row = min(m0 + 32 * w + (lane & 31), M - 1);
+  const char *xrow = P + row * L * 2;
+  f32x16 acc[2];
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[jb][v] = 0.0f;
+  const int64_t k0 = static_cast<int64_t>(s0) * kBK;
+  down_chunks<2, QL>(acc, xrow, qs, k0, steps / 2, lds);
+  down_chunks<1, QL>(acc, xrow, qs, k0 + (steps / 2) * 2 * kBK, steps % 2, lds);
+  const int h = lane >> 5;
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb) {
+    const int64_t col = qs.j0 + jb * 32 + (lane & 31);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t r = m0 + 32 * w + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (r < M) part[r * rp + col] = acc[jb][v];
+    }
+  }
 }
 
 __global__ __launch_bounds__(kDownThreads, 2) void k_adapter_down(DownParams p) {
@@ -306,36 +327,20 @@ __global__ __launch_bounds__(kDownThreads, 2) void k_adapter_down(DownParams p) 
   const bool is_h = g < per * p.h_splits;
   if (!is_h) g -= per * p.h_splits;
   const int z = g / per, t = g % per;
-  const int64_t j0 = static_cast<int64_t>(t % p.jt) * 64;
+  const int j0 = (t % p.jt) * 64;
   const int64_t m0 = static_cast<int64_t>(t / p.jt) * kDownRows;
-  const char *P = static_cast<const char *>(is_h ? p.X : p.dY);
-  const __bf16 *Q = (is_h ? p.Ab : p.Bt) + j0 * (is_h ? p.K : p.N);
   const int64_t L = is_h ? p.K : p.N;
   const int steps_per = is_h ? p.h_steps : p.dh_steps;
-  float *part = (is_h ? p.h_part : p.dh_part) + static_cast<int64_t>(z) * p.M * p.rp;
   const int total = static_cast<int>(L / kBK);
   const int s0 = z * steps_per, steps = min(steps_per, total - s0);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // rows past M read row M - 1 (always valid) and are not stored
-  const int64_t row = min(m0 + 32 * w + (lane & 31), p.M - 1);
-  const char *xrow = P + row * L * 2;
-  f32x16 acc[2];
-#pragma unroll
-  for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[jb][v] = 0.0f;
-  const int64_t k0 = static_cast<int64_t>(s0) * kBK;
-  down_chunks<4>(acc, xrow, Q, L, k0, steps / 4, lds);
-  down_chunks<1>(acc, xrow, Q, L, k0 + (steps / 4) * 4 * kBK, steps % 4, lds);
-  const int h = lane >> 5;
-#pragma unroll
-  for (int jb = 0; jb < 2; ++jb) {
-    const int64_t col = j0 + jb * 32 + (lane & 31);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t r = m0 + 32 * w + 8 * (v >> 2) + 4 * h + (v & 3);
-      if (r < p.M) part[r * p.rp + col] = acc[jb][v];
-    }
+  if (is_h) {
+    const QSrc qs{p.A, p.K, p.r, j0};
+    down_tile<QFromRows>(static_cast<const char *>(p.X), L, p.M, qs, m0, s0, steps,
+                         p.h_part + static_cast<int64_t>(z) * p.M * p.rp, p.rp, lds);
+  } else {
+    const QSrc qs{p.B, p.r, p.r, j0};
+    down_tile<QFromCols>(static_cast<const char *>(p.dY), L, p.M, qs, m0, s0, steps,
+                         p.dh_part + static_cast<int64_t>(z) * p.M * p.rp, p.rp, lds);
   }
 }
 
@@ -355,29 +360,101 @@ __device__ __forceinline__ float split_sum(const float *part, int64_t plane, int
   return v;
 }
 
-// k_adapter_finish sums the split partials into the bf16 operands of the
-// adapter steps: Hs [M][rp] = bf16(s * sum_z h_part) and (backward)
-// dHb [M][rp] = bf16(s * sum_z dh_part), in a fixed order.
+// The same sum for four consecutive elements (16-byte loads).
+__device__ __forceinline__ float4 split_sum4(const float *part, int64_t plane, int64_t e, int splits) {
+  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int z0 = 0; z0 < splits; z0 += 8) {
+    float4 t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      t[u] = *reinterpret_cast<const float4 *>(part + static_cast<int64_t>(min(z0 + u, splits - 1)) * plane + e);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (z0 + u < splits) {
+        v.x += t[u].x;
+        v.y += t[u].y;
+        v.z += t[u].z;
+        v.w += t[u].w;
+      }
+  }
+  return v;
+}
+
+// k_adapter_finish: one launch, its workgroups split into segments (each
+// workgroup in one segment, one work item per thread):
+//   Hs, dHb   fixed-order split sums, 4 elements per item, times s, to bf16
+//   cs        4 block scales per item: c_b = fp32(fp32(absmax_q * fp32(d / 127)) + mean)
+//   Bb / Atb  8 adapter columns of one row per item (one 16-byte store)
+constexpr int kScaleBlocksPerThread = 4;
+
 struct FinishParams {
-  const float *h_part, *dh_part;
+  const float *h_part, *dh_part;   // [splits][M][rp]
   __bf16 *Hs, *dHb;
-  int64_t n;        // M * rp
+  int64_t M;
   int r, rp, h_splits, dh_splits;
   float scale;
-  bool backward;
+  const int8_t *absmax_q;
+  const float *dq_scale, *dq_mean;
+  float *cs;
+  int64_t nb;
+  const float *A, *B;
+  __bf16 *Bb, *Atb;                // one of them written (the other null)
+  int64_t N, K;
+  int64_t g_h, g_dh, g_cs, g_op;   // workgroups per segment
 };
 
 __global__ __launch_bounds__(256) void k_adapter_finish(FinishParams p) {
-  const int64_t total = p.backward ? 2 * p.n : p.n;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const bool second = i >= p.n;
-    const int64_t e = second ? i - p.n : i;
-    const float *part = second ? p.dh_part : p.h_part;
-    const int splits = second ? p.dh_splits : p.h_splits;
-    const float v = static_cast<int>(e % p.rp) < p.r ? split_sum(part, p.n, e, splits) : 0.0f;
-    (second ? p.dHb : p.Hs)[e] = static_cast<__bf16>(p.scale * v);
+  int64_t g = blockIdx.x;
+  if (g < p.g_h + p.g_dh) {   // split sums
+    const bool second = g >= p.g_h;
+    if (second) g -= p.g_h;
+    const int64_t e = (g * 256 + threadIdx.x) * 4, n = p.M * p.rp;
+    if (e >= n) return;
+    const float4 v = split_sum4(second ? p.dh_part : p.h_part, n, e, second ? p.dh_splits : p.h_splits);
+    const uint2 w = make_uint2(pack_bf16x2(p.scale * v.x, p.scale * v.y), pack_bf16x2(p.scale * v.z, p.scale * v.w));
+    *reinterpret_cast<uint2 *>((second ? p.dHb : p.Hs) + e) = w;
+    return;
   }
+  g -= p.g_h + p.g_dh;
+  if (g < p.g_cs) {           // block scales
+    const int64_t b0 = (g * 256 + threadIdx.x) * kScaleBlocksPerThread;
+    const float mu = p.dq_mean[0];
+#pragma unroll
+    for (int u = 0; u < kScaleBlocksPerThread; ++u) {
+      const int64_t b = b0 + u;
+      if (b < p.nb) {
+        const float kd = __fdiv_rn(p.dq_scale[b / kDqBlock], 127.0f);
+        p.cs[b] = __fadd_rn(__fmul_rn(static_cast<float>(p.absmax_q[b]), kd), mu);
+      }
+    }
+    return;
+  }
+  g -= p.g_cs;
+  const int64_t i = g * 256 + threadIdx.x;
+  const int q8 = p.rp / 8;
+  float v[8];
+  __bf16 *dst;
+  if (p.Bb) {                 // Bb[n][8 jq ..] = bf16(B[n][8 jq ..])
+    if (i >= p.N * q8) return;
+    const int64_t n = i / q8;
+    const int j = static_cast<int>(i % q8) * 8;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = p.B[n * p.r + min(j + t, p.r - 1)];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = j + t < p.r ? v[t] : 0.0f;
+    dst = p.Bb + n * p.rp + j;
+  } else {                    // Atb[k][8 jq ..] = bf16(A[8 jq ..][k]); consecutive threads take consecutive k
+    if (i >= p.K * q8) return;
+    const int64_t k = i % p.K;
+    const int j = static_cast<int>(i / p.K) * 8;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = p.A[static_cast<int64_t>(min(j + t, p.r - 1)) * p.K + k];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = j + t < p.r ? v[t] : 0.0f;
+    dst = p.Atb + k * p.rp + j;
+  }
+  *reinterpret_cast<uint4 *>(dst) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                               pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
 }
 
 // ------------------------------------------------ adapter gradient products
@@ -503,8 +580,6 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int r) {
 
 struct Buffers {
   float *cs;
-  __bf16 *Ab;
-  __bf16 *Bt;
   float *down_part;
   __bf16 *Hs;
   __bf16 *Bb;
@@ -522,8 +597,6 @@ Buffers carve(void *ws, const Plan &pl, int64_t M, int64_t N, int64_t K, size_t 
   const int rp = pl.rp;
   b.cs = c.take<float>(nb);
   if (rp > 0) {
-    b.Ab = c.take<__bf16>(static_cast<size_t>(rp) * K);
-    b.Bt = c.take<__bf16>(static_cast<size_t>(rp) * N);
     b.down_part = c.take<float>(static_cast<size_t>(pl.down.splits) * M * rp);
     b.Hs = c.take<__bf16>(static_cast<size_t>(M) * rp);
     b.Bb = c.take<__bf16>(static_cast<size_t>(N) * rp);
@@ -537,74 +610,62 @@ Buffers carve(void *ws, const Plan &pl, int64_t M, int64_t N, int64_t K, size_t 
   return b;
 }
 
-// Block scales and the bf16 adapter layouts (one elementwise launch).
-hipError_t run_adapter_prep(const LinearArgs &a, const Plan &pl, const Buffers &b, const float *A,
-                            const float *B, bool backward, hipStream_t s) {
-  PrepParams pp{};
-  pp.absmax_q = a.absmax_q;
-  pp.dq_scale = a.dq_scale;
-  pp.dq_mean = a.dq_mean;
-  pp.A = A;
-  pp.B = B;
-  pp.cs = b.cs;
-  pp.Ab = b.Ab;
-  pp.Bt = b.Bt;
-  pp.Bb = b.Bb;
-  pp.Atb = b.Atb;
-  pp.nb = ceil_div(a.N * a.K, kBlock);
-  pp.N = a.N;
-  pp.K = a.K;
-  pp.r = a.r;
-  pp.rp = pl.rp;
-  pp.n_cs = pp.nb;
+// The work before a big GEMM: the split partials of H = X A^T and (backward)
+// dY B, then one launch with their sums, the block scales and the bf16 adapter
+// operand of the GEMM (Bb forward, Atb backward).
+hipError_t run_adapter_pre(const LinearArgs &a, const Plan &pl, const Buffers &b, const void *X,
+                           const void *dY, const float *A, const float *B, bool backward, hipStream_t s) {
   const bool lora = pl.rp > 0;
-  pp.n_ab = lora ? static_cast<int64_t>(pl.rp) * a.K : 0;
-  pp.n_bt = (lora && backward) ? static_cast<int64_t>(pl.rp) * a.N : 0;
-  pp.n_bb = (lora && !backward) ? a.N * pl.rp : 0;
-  pp.n_atb = (lora && backward) ? a.K * pl.rp : 0;
-  const int64_t total = ceil_div(pp.n_cs, kScaleBlocksPerThread) + pp.n_ab + pp.n_bt + pp.n_bb + pp.n_atb;
-  const int64_t grid = std::min<int64_t>(grid_blocks(total, 256), 8192);
-  hipLaunchKernelGGL(k_adapter_prep, dim3(grid), dim3(256), 0, s, pp);
-  return hipGetLastError();
-}
-
-// H partials and (backward) dY B partials (one launch), then their sums.
-hipError_t run_adapter_down_finish(const LinearArgs &a, const Plan &pl, const Buffers &b, const void *X,
-                                   const void *dY, bool backward, hipStream_t s) {
-  DownParams dp{};
-  dp.X = X;
-  dp.dY = dY;
-  dp.Ab = b.Ab;
-  dp.Bt = b.Bt;
-  dp.h_part = b.down_part;
-  dp.dh_part = b.dh_part;
-  dp.M = a.M;
-  dp.N = a.N;
-  dp.K = a.K;
-  dp.rp = pl.rp;
-  dp.jt = pl.rp / 64;
-  dp.mt = static_cast<int>(ceil_div(a.M, kDownRows));
-  dp.h_splits = pl.down.splits;
-  dp.h_steps = pl.down.steps_per_split;
-  dp.dh_splits = backward ? pl.dh.splits : 0;
-  dp.dh_steps = pl.dh.steps_per_split;
-  const int64_t groups = static_cast<int64_t>(dp.jt) * dp.mt * (dp.h_splits + dp.dh_splits);
-  hipLaunchKernelGGL(k_adapter_down, dim3(groups), dim3(kDownThreads), 0, s, dp);
+  if (lora) {
+    DownParams dp{};
+    dp.X = X;
+    dp.dY = dY;
+    dp.A = A;
+    dp.B = B;
+    dp.h_part = b.down_part;
+    dp.dh_part = b.dh_part;
+    dp.M = a.M;
+    dp.N = a.N;
+    dp.K = a.K;
+    dp.r = a.r;
+    dp.rp = pl.rp;
+    dp.jt = pl.rp / 64;
+    dp.mt = static_cast<int>(ceil_div(a.M, kDownRows));
+    dp.h_splits = pl.down.splits;
+    dp.h_steps = pl.down.steps_per_split;
+    dp.dh_splits = backward ? pl.dh.splits : 0;
+    dp.dh_steps = pl.dh.steps_per_split;
+    const int64_t groups = static_cast<int64_t>(dp.jt) * dp.mt * (dp.h_splits + dp.dh_splits);
+    hipLaunchKernelGGL(k_adapter_down, dim3(groups), dim3(kDownThreads), 0, s, dp);
+  }
   FinishParams fp{};
   fp.h_part = b.down_part;
   fp.dh_part = b.dh_part;
   fp.Hs = b.Hs;
   fp.dHb = b.dHb;
-  fp.n = a.M * pl.rp;
+  fp.M = a.M;
   fp.r = a.r;
   fp.rp = pl.rp;
   fp.h_splits = pl.down.splits;
   fp.dh_splits = pl.dh.splits;
   fp.scale = a.scale;
-  fp.backward = backward;
-  const int64_t total = backward ? 2 * fp.n : fp.n;
-  hipLaunchKernelGGL(k_adapter_finish, dim3(std::min<int64_t>(grid_blocks(total, 256), 4096)), dim3(256), 0,
-                     s, fp);
+  fp.absmax_q = a.absmax_q;
+  fp.dq_scale = a.dq_scale;
+  fp.dq_mean = a.dq_mean;
+  fp.cs = b.cs;
+  fp.nb = ceil_div(a.N * a.K, kBlock);
+  fp.A = A;
+  fp.B = B;
+  fp.Bb = (lora && !backward) ? b.Bb : nullptr;
+  fp.Atb = (lora && backward) ? b.Atb : nullptr;
+  fp.N = a.N;
+  fp.K = a.K;
+  const int64_t sums = lora ? grid_blocks(a.M * pl.rp / 4, 256) : 0;
+  fp.g_h = sums;
+  fp.g_dh = backward ? sums : 0;
+  fp.g_cs = grid_blocks(ceil_div(fp.nb, kScaleBlocksPerThread), 256);
+  fp.g_op = lora ? grid_blocks((backward ? a.K : a.N) * (pl.rp / 8), 256) : 0;
+  hipLaunchKernelGGL(k_adapter_finish, dim3(fp.g_h + fp.g_dh + fp.g_cs + fp.g_op), dim3(256), 0, s, fp);
   return hipGetLastError();
 }
 
@@ -623,12 +684,8 @@ hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const 
   const Plan pl = make_plan(a.M, a.N, a.K, a.r);
   if (pl.small) return launch_gemv(a, X, A, B, Y, ws, s);
   const Buffers b = carve(ws, pl, a.M, a.N, a.K, nullptr);
-  hipError_t err = run_adapter_prep(a, pl, b, A, B, false, s);
+  hipError_t err = run_adapter_pre(a, pl, b, X, nullptr, A, B, false, s);
   if (err != hipSuccess) return err;
-  if (pl.rp > 0) {
-    err = run_adapter_down_finish(a, pl, b, X, nullptr, false, s);
-    if (err != hipSuccess) return err;
-  }
   FwdParams fp{X, a.codes, b.cs, b.Hs, b.Bb, Y, a.M, a.N, a.K, pl.rp};
   dim3 g(grid_blocks(a.N, 256) * grid_blocks(a.M, 256), 1, 1);
   prof_begin(kProfFwdGemm, s);
@@ -642,12 +699,8 @@ hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const 
   const Plan pl = make_plan(a.M, a.N, a.K, a.r);
   const Buffers b = carve(ws, pl, a.M, a.N, a.K, nullptr);
   const Nf4Tables &tab = nf4_tables();
-  hipError_t err = run_adapter_prep(a, pl, b, A, B, true, s);
+  hipError_t err = run_adapter_pre(a, pl, b, X, dY, A, B, true, s);
   if (err != hipSuccess) return err;
-  if (pl.rp > 0) {
-    err = run_adapter_down_finish(a, pl, b, X, dY, true, s);
-    if (err != hipSuccess) return err;
-  }
   {
     DxParams dp{dY, a.codes, b.cs, b.dHb, b.Atb, dX, a.M, a.N, a.K, pl.rp};
     dim3 g(grid_blocks(a.K, 256) * grid_blocks(a.M, 256), 1, 1);
