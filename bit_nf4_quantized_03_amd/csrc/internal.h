@@ -37,8 +37,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- quantize
-// Workspace: fp32 absmax [nb] | fp64 tree partial sums, one level after
-// another (nd + ceil(nd/256) + ... entries).
+// Workspace: fp32 absmax [nb] | one fp64 tree partial sum per DQ block [nd].
 size_t quantize_ws_bytes(int64_t n);
 hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, uint8_t *codes,
                            int8_t *absmax_q, float *dq_scale, float *dq_mean,

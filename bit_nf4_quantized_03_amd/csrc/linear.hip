@@ -293,7 +293,7 @@ __device__ __forceinline__ void down_chunks(f32x16 (&acc)[2], const char *xrow, 
   __syncthreads();
 }
 
-template <template <int> class QL>
+template <template <int> class QL, int CS>
 __device__ __forceinline__ void down_tile(const char *P, int64_t L, int64_t M, const QSrc &qs, int64_t m0,
                                           int s0, int steps, float *part, int rp, __bf16 *lds) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -306,8 +306,8 @@ __device__ __forceinline__ void down_tile(const char *P, int64_t L, int64_t M, c
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[jb][v] = 0.0f;
   const int64_t k0 = static_cast<int64_t>(s0) * kBK;
-  down_chunks<2, QL>(acc, xrow, qs, k0, steps / 2, lds);
-  down_chunks<1, QL>(acc, xrow, qs, k0 + (steps / 2) * 2 * kBK, steps % 2, lds);
+  down_chunks<CS, QL>(acc, xrow, qs, k0, steps / CS, lds);
+  if (CS > 1) down_chunks<1, QL>(acc, xrow, qs, k0 + (steps / CS) * CS * kBK, steps % CS, lds);
   const int h = lane >> 5;
 #pragma unroll
   for (int jb = 0; jb < 2; ++jb) {
@@ -335,11 +335,11 @@ __global__ __launch_bounds__(kDownThreads, 2) void k_adapter_down(DownParams p) 
   const int s0 = z * steps_per, steps = min(steps_per, total - s0);
   if (is_h) {
     const QSrc qs{p.A, p.K, p.r, j0};
-    down_tile<QFromRows>(static_cast<const char *>(p.X), L, p.M, qs, m0, s0, steps,
+    down_tile<QFromRows, 4>(static_cast<const char *>(p.X), L, p.M, qs, m0, s0, steps,
                          p.h_part + static_cast<int64_t>(z) * p.M * p.rp, p.rp, lds);
   } else {
     const QSrc qs{p.B, p.r, p.r, j0};
-    down_tile<QFromCols>(static_cast<const char *>(p.dY), L, p.M, qs, m0, s0, steps,
+    down_tile<QFromCols, 2>(static_cast<const char *>(p.dY), L, p.M, qs, m0, s0, steps,
                          p.dh_part + static_cast<int64_t>(z) * p.M * p.rp, p.rp, lds);
   }
 }
