@@ -17,11 +17,14 @@
 //                   16-byte loads, per-64 absmax by DPP lane exchanges, nearest-level codes, packed stores, fp32 absmax
 //                   to the workspace and the fp64 tree sum of the DQ block's
 //                   256 constants.
-//   k_tree_mean     one workgroup completes the fp64 tree over the per-DQ-block
-//                   partials, pairwise level by level in LDS, and writes the mean.
-//   k_dq_codes      one workgroup per DQ block: per-block scale and int8 codes.
+//   k_dq_codes      up to 256 workgroups, each of which first completes the
+//                   same fp64 tree over the per-DQ-block partials (the mean),
+//                   then takes DQ blocks in turn: per-block scale, int8 codes.
 //   k_dequant       one workgroup per DQ block: per-block scales in LDS, then
 //                   4-byte code loads expanded to fp32 or bf16 stores.
+#include <algorithm>
+#include <cstring>
+
 #include "internal.h"
 
 namespace qnf4 {
@@ -50,23 +53,35 @@ __device__ __forceinline__ int code_from_y(float y, const Nf4Tables &t) {
 // within the cell or 2^-13 of it (thresholds are more than 9 apart in z).
 // Entry: (tz or +inf, base count as int bits). The code is base + (z > tz);
 // when z is within 2^-14 of tz the element is recomputed with a correctly
-// rounded division instead.
-__device__ void build_lut(float2 *lut, const Nf4Tables &t) {
-  for (int c = threadIdx.x; c < kCells; c += blockDim.x) {
-    const int iz = c - 128;
-    const float lo = static_cast<float>(iz > 0 ? iz : iz - 1);
-    const float hi = static_cast<float>(iz < 0 ? iz : iz + 1);
-    const float win = 0x1p-13f;
-    int base = 0;
-    float tc = __builtin_huge_valf();
-#pragma unroll
-    for (int i = 0; i < 15; ++i) {
-      const float tz = t.thr[i] * 128.0f;  // exact (power-of-two scaling)
-      base += tz < lo - win ? 1 : 0;
-      tc = (tz >= lo - win && tz < hi + win) ? tz : tc;
+// rounded division instead. The table is built once on the host (every
+// quantity in it is exact in fp32) and passed by value.
+struct CodeLut {
+  float2 cell[kCells];
+};
+
+const CodeLut &code_lut() {
+  static const CodeLut lut = [] {
+    CodeLut l{};
+    const Nf4Tables &t = nf4_tables();
+    for (int c = 0; c < kCells; ++c) {
+      const int iz = c - 128;
+      const float lo = static_cast<float>(iz > 0 ? iz : iz - 1);
+      const float hi = static_cast<float>(iz < 0 ? iz : iz + 1);
+      const float win = 0x1p-13f;
+      int base = 0;
+      float tc = __builtin_huge_valf();
+      for (int i = 0; i < 15; ++i) {
+        const float tz = t.thr[i] * 128.0f;  // exact (power-of-two scaling)
+        base += tz < lo - win ? 1 : 0;
+        tc = (tz >= lo - win && tz < hi + win) ? tz : tc;
+      }
+      float base_bits;
+      std::memcpy(&base_bits, &base, sizeof(base_bits));
+      l.cell[c] = make_float2(tc, base_bits);
     }
-    lut[c] = make_float2(tc, __int_as_float(base));
-  }
+    return l;
+  }();
+  return lut;
 }
 
 template <bool kBf16>
@@ -174,7 +189,8 @@ __global__ __launch_bounds__(kThreads) void k_absmax_codes(const uint8_t *__rest
                                                            uint8_t *__restrict__ codes,
                                                            float *__restrict__ absmax_ws,
                                                            double *__restrict__ partial,
-                                                           int64_t nb, int64_t nd, Nf4Tables tab) {
+                                                           int64_t nb, int64_t nd, Nf4Tables tab,
+                                                           CodeLut code_tab) {
   using IT = InTraits<kBf16>;
   constexpr int kEpl = IT::kEpl;                    // elements per lane
   constexpr int kLpb = kBlock / kEpl;               // lanes per 64-block
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_absmax_codes(const uint8_t *__rest
   int64_t d = blockIdx.x;
   uint4 raw[kPasses];
   if (d < nd) load(d, raw);
-  build_lut(lut, tab);
+  for (int c = tid; c < kCells; c += kThreads) lut[c] = code_tab.cell[c];
   __syncthreads();  // table ready
 
   for (; d < nd; d += gridDim.x) {
@@ -248,16 +264,17 @@ __global__ __launch_bounds__(kThreads) void k_absmax_codes(const uint8_t *__rest
   }
 }
 
-// One workgroup: the sum of all per-DQ-block fp64 partials. The partials are
+// The sum of all per-DQ-block fp64 partials. The partials are
 // the 256-leaf subtrees of the perfect binary tree over all absmax constants
 // (zero padded), so the tree is completed in the same shape: aligned chunks
 // of up to kTreeChunk partials, where thread t first sums its aligned run of
 // S = top / 256 partials pairwise in registers and the 256 run sums are
 // combined by xor butterflies inside each wave, then (w0 + w1) + (w2 + w3);
-// the chunk sums are combined the same way. Writes mean = fp32(sum / nb).
+// the chunk sums are combined the same way.
 constexpr int kTreeChunk = 8192;
 constexpr int kTreeRun = kTreeChunk / kThreads;   // 32
 constexpr int kTreeMaxChunks = kThreads * kTreeRun;
+constexpr int64_t kDqCodeGroups = 256;   // workgroups of k_dq_codes (each recomputes the mean)
 
 // Sum of the perfect binary tree over top leaves (top a power of two <= kTreeChunk)
 // src[base + i], zero past limit. Every thread gets the result.
@@ -286,10 +303,11 @@ __device__ double tree_sum(const double *src, int64_t base, int64_t limit, int t
   return (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
 }
 
-__global__ __launch_bounds__(kThreads) void k_tree_mean(const double *__restrict__ partial, int64_t nd,
-                                                        int64_t nb, float *__restrict__ dq_mean) {
-  __shared__ double wsum[kThreads / 64];
-  __shared__ double csum[kTreeMaxChunks];
+// The DQ mean: every workgroup completes the same fp64 tree over the
+// per-DQ-block partials (so all of them hold the same bits) and workgroup 0
+// stores mean = fp32(sum / nb).
+__device__ float tree_mean(const double *__restrict__ partial, int64_t nd, int64_t nb, double *wsum,
+                           double *csum) {
   const int tid = threadIdx.x;
   const int64_t nchunks = (nd + kTreeChunk - 1) / kTreeChunk;
   int top = 1;
@@ -307,36 +325,43 @@ __global__ __launch_bounds__(kThreads) void k_tree_mean(const double *__restrict
     while (ctop < nchunks) ctop *= 2;
     total = tree_sum(csum, 0, nchunks, ctop, wsum);
   }
-  if (tid == 0) dq_mean[0] = static_cast<float>(total / static_cast<double>(nb));
+  return static_cast<float>(total / static_cast<double>(nb));
 }
 
-// One workgroup per DQ block: scale s2 = max |fp32(a - mean)| and int8 codes.
-__global__ __launch_bounds__(kThreads) void k_dq_codes(const float *__restrict__ absmax_ws, int64_t nb,
-                                                       const float *__restrict__ dq_mean,
+// Workgroups take DQ blocks d = blockIdx.x + i * gridDim.x: scale
+// s2 = max |fp32(a - mean)| over the block and the int8 codes.
+__global__ __launch_bounds__(kThreads) void k_dq_codes(const float *__restrict__ absmax_ws,
+                                                       const double *__restrict__ partial, int64_t nb,
+                                                       int64_t nd, float *__restrict__ dq_mean,
                                                        int8_t *__restrict__ absmax_q,
                                                        float *__restrict__ dq_scale) {
+  __shared__ double wsum[kThreads / 64];
+  __shared__ double csum[kTreeMaxChunks];
   __shared__ float wmax[kThreads / 64];
   const int tid = threadIdx.x;
-  const int64_t d = blockIdx.x;
-  const int64_t b = d * kDqBlock + tid;
-  const bool valid = b < nb;
-  const float a = valid ? absmax_ws[b] : 0.0f;
-  const float mu = dq_mean[0];
-  const float dv = valid ? __fsub_rn(a, mu) : 0.0f;
-  float m = fabsf(dv);
+  const float mu = tree_mean(partial, nd, nb, wsum, csum);
+  if (blockIdx.x == 0 && tid == 0) dq_mean[0] = mu;
+  for (int64_t d = blockIdx.x; d < nd; d += gridDim.x) {
+    const int64_t b = d * kDqBlock + tid;
+    const bool valid = b < nb;
+    const float a = valid ? absmax_ws[b] : 0.0f;
+    const float dv = valid ? __fsub_rn(a, mu) : 0.0f;
+    float m = fabsf(dv);
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((tid & 63) == 0) wmax[tid >> 6] = m;
-  __syncthreads();
-  const float s2 = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  int q = 0;
-  if (s2 > 0.0f) {
-    const float u = __fmul_rn(__fdiv_rn(dv, s2), 127.0f);
-    q = static_cast<int>(rintf(u));
-    q = min(max(q, -127), 127);
+    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    __syncthreads();   // wmax free
+    if ((tid & 63) == 0) wmax[tid >> 6] = m;
+    __syncthreads();
+    const float s2 = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    int q = 0;
+    if (s2 > 0.0f) {
+      const float u = __fmul_rn(__fdiv_rn(dv, s2), 127.0f);
+      q = static_cast<int>(rintf(u));
+      q = min(max(q, -127), 127);
+    }
+    if (valid) absmax_q[b] = static_cast<int8_t>(q);
+    if (tid == 0) dq_scale[d] = s2;
   }
-  if (valid) absmax_q[b] = static_cast<int8_t>(q);
-  if (tid == 0) dq_scale[d] = s2;
 }
 
 // ------------------------------------------------------------ dequantize
@@ -442,21 +467,22 @@ hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, uint8_t *codes
   float *absmax_ws = static_cast<float *>(ws);
   double *part = reinterpret_cast<double *>(static_cast<char *>(ws) +
                                             align_up(static_cast<size_t>(nb) * 4, 256));
+  if (ceil_div(nd, kTreeChunk) > kTreeMaxChunks) return hipErrorInvalidValue;   // > 2^37 elements
   const Nf4Tables &tab = nf4_tables();
+  const CodeLut &lut = code_lut();
   prof_begin(kProfQuantize, s);
   const int64_t grid = nd;   // one DQ block per workgroup
   if (w_bf16)
     hipLaunchKernelGGL(k_absmax_codes<true>, dim3(grid), dim3(kThreads), 0, s,
-                       static_cast<const uint8_t *>(W), n, codes, absmax_ws, part, nb, nd, tab);
+                       static_cast<const uint8_t *>(W), n, codes, absmax_ws, part, nb, nd, tab, lut);
   else
     hipLaunchKernelGGL(k_absmax_codes<false>, dim3(grid), dim3(kThreads), 0, s,
-                       static_cast<const uint8_t *>(W), n, codes, absmax_ws, part, nb, nd, tab);
+                       static_cast<const uint8_t *>(W), n, codes, absmax_ws, part, nb, nd, tab, lut);
   prof_end(kProfQuantize, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (ceil_div(nd, kTreeChunk) > kTreeMaxChunks) return hipErrorInvalidValue;   // > 2^37 elements
-  hipLaunchKernelGGL(k_tree_mean, dim3(1), dim3(kThreads), 0, s, part, nd, nb, dq_mean);
-  hipLaunchKernelGGL(k_dq_codes, dim3(nd), dim3(kThreads), 0, s, absmax_ws, nb, dq_mean, absmax_q, dq_scale);
+  hipLaunchKernelGGL(k_dq_codes, dim3(std::min<int64_t>(nd, kDqCodeGroups)), dim3(kThreads), 0, s, absmax_ws,
+                     part, nb, nd, dq_mean, absmax_q, dq_scale);
   return hipGetLastError();
 }
 
