@@ -227,10 +227,27 @@ __global__ __launch_bounds__(kThreads) void k_absmax_codes(const uint8_t *__rest
     }
   };
 
+  // the table's loads go out before the weights', so that writing it to LDS
+  // does not wait for the weights
+  static_assert(kCells <= 2 * kThreads, "two table cells per thread at most");
+  const float2 cell0 = code_tab.cell[tid];
+  const float2 cell1 = code_tab.cell[min(tid + kThreads, kCells - 1)];
+  auto write_lut = [&]() {
+    lut[tid] = cell0;
+    if (tid + kThreads < kCells) lut[tid + kThreads] = cell1;
+  };
   int64_t d = blockIdx.x;
   uint4 raw[kPasses];
-  if (d < nd) load(d, raw);
-  for (int c = tid; c < kCells; c += kThreads) lut[c] = code_tab.cell[c];
+  // (the table is written inside each branch: where the branches meet, the
+  // compiler would wait for every load before the LDS store)
+  if (d < nd && full(d)) {
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) raw[p] = *reinterpret_cast<const uint4 *>(W + elem(d, p) * kEsz);
+    write_lut();
+  } else {
+    if (d < nd) load(d, raw);
+    write_lut();
+  }
   __syncthreads();  // table ready
 
   for (; d < nd; d += gridDim.x) {
