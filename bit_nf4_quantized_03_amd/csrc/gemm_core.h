@@ -160,6 +160,50 @@ __device__ __forceinline__ void mainloop(Acc<Cfg> &acc, LA &la, LB &lb, int64_t 
   __syncthreads();
 }
 
+// Main loop with two register stages: while step s runs on the MFMAs, the
+// global reads of steps s + 1 and s + 2 are in flight (loaders la0 / lb0 and
+// la1 / lb1 alternate). The loop runs an even number of steps with no
+// branches inside; the loaders must read rows at or past red0 + 64 steps as
+// zero (their reduction bound), so the steps past the end add nothing. Same
+// LDS layout and entry / exit conditions as mainloop.
+template <class Cfg, class LA, class LB>
+__device__ __forceinline__ void mainloop2(Acc<Cfg> &acc, LA &la0, LA &la1, LB &lb0, LB &lb1, int64_t red0,
+                                          int steps, __bf16 *smem) {
+  if (steps <= 0) return;
+  __bf16 *sA0 = smem, *sA1 = smem + Cfg::kLdsA;
+  __bf16 *sB0 = smem + 2 * Cfg::kLdsA, *sB1 = sB0 + Cfg::kLdsB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int wm = w / Cfg::WAVES_N, wn = w % Cfg::WAVES_N;
+  const FragAddr<Cfg::WTM> fa(wm * Cfg::WTM, lane);
+  const FragAddr<Cfg::WTN> fb(wn * Cfg::WTN, lane);
+  auto red = [&](int s) { return red0 + static_cast<int64_t>(s) * kBK; };
+  la0.load(red(0));
+  lb0.load(red(0));
+  la1.load(red(1));
+  lb1.load(red(1));
+  la0.store(sA0);
+  lb0.store(sB0);
+  __syncthreads();
+  for (int s = 0; s < steps; s += 2) {
+    // buffer 0: step s; stage 1: step s + 1 in flight
+    la0.load(red(s + 2));
+    lb0.load(red(s + 2));
+    mma_step<Cfg>(acc, sA0, sB0, fa, fb);
+    la1.store(sA1);
+    lb1.store(sB1);
+    __syncthreads();
+    // buffer 1: step s + 1; stage 0: step s + 2 in flight
+    la1.load(red(s + 3));
+    lb1.load(red(s + 3));
+    mma_step<Cfg>(acc, sA1, sB1, fa, fb);
+    la0.store(sA0);
+    lb0.store(sB0);
+    __syncthreads();
+  }
+}
+
 // ----------------------------------------------------------------- loaders
 // Each loader covers ROWS output rows of one operand and a 64-deep reduction
 // step. load() issues the global reads into registers, store() writes the
@@ -266,21 +310,25 @@ struct TransBf16 {
   using U = TransUnits<ROWS, T>;
   const __bf16 *src;
   int64_t ld, nred, ncols, col0;
+  int64_t red_in = 0;   // red0 of the registers' contents
   uint4 reg[U::CH][8];
   __device__ TransBf16(const void *s, int64_t ld_, int64_t nred_, int64_t ncols_, int64_t col0_)
       : src(static_cast<const __bf16 *>(s)), ld(ld_), nred(nred_), ncols(ncols_), col0(col0_) {}
+  // Out-of-range elements: a clamped (valid) address is read here and the
+  // value replaced by 0 in store(), so the loads need no branches and nothing
+  // waits for them before the store.
   __device__ __forceinline__ void load(int64_t red0) {
+    red_in = red0;
 #pragma unroll
     for (int u = 0; u < U::CH; ++u) {
       const int idx = threadIdx.x + u * T;
       if (!U::active(idx)) continue;
       const int cc = U::cc(idx), rg = U::rg(idx);
-      const int64_t c = col0 + cc * 8;
+      const int64_t cl = min(col0 + cc * 8, ncols - 8);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int64_t t = red0 + rg * 8 + i;
-        reg[u][i] = (t < nred && c < ncols) ? *reinterpret_cast<const uint4 *>(src + t * ld + c)
-                                            : make_uint4(0, 0, 0, 0);
+        reg[u][i] = *reinterpret_cast<const uint4 *>(src + min(t, nred - 1) * ld + cl);
       }
     }
   }
@@ -290,13 +338,15 @@ struct TransBf16 {
       const int idx = threadIdx.x + u * T;
       if (!U::active(idx)) continue;
       const int cc = U::cc(idx), rg = U::rg(idx);
+      const bool col_ok = col0 + cc * 8 < ncols;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint32_t w[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const uint4 &v = reg[u][i];
-          w[i] = q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+          const bool ok = col_ok && red_in + rg * 8 + i < nred;
+          w[i] = ok ? (q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w) : 0u;
         }
         // output rows 2q (low halves) and 2q+1 (high halves), 8 reduction values each
         uint4 even = make_uint4(lo16x2(w[0], w[1]), lo16x2(w[2], w[3]), lo16x2(w[4], w[5]),
@@ -358,6 +408,53 @@ struct TransF32 {
                              pack_bf16x2(reg[u][4][j], reg[u][5][j]), pack_bf16x2(reg[u][6][j], reg[u][7][j]));
         *reinterpret_cast<uint4 *>(lds + lds_off(cc * 8 + j, rg)) = v;
       }
+    }
+  }
+};
+
+// Transposed bf16 source S[t][col] for small tiles (UNITS = 4 ROWS a multiple
+// of T): units of 8 reduction rows x 2 output rows, one 4-byte load per
+// reduction row, so every thread has whole units and the loads need no
+// branches. ncols (the source's column count) is even; reduction rows >= nred
+// read as 0 (a clamped, valid row is loaded and replaced in store()).
+template <int ROWS, int T>
+struct TransBf16Narrow {
+  static constexpr int UPR = ROWS / 2;          // column pairs
+  static constexpr int UNITS = UPR * 8;         // x 8 reduction-row groups
+  static constexpr int CH = UNITS / T;
+  static_assert(UNITS % T == 0, "whole units per thread");
+  const __bf16 *src;
+  int64_t ld, nred, col0;
+  int64_t red_in = 0;   // red0 of the registers' contents
+  uint32_t reg[CH][8];
+  __device__ TransBf16Narrow(const void *s, int64_t ld_, int64_t nred_, int64_t col0_)
+      : src(static_cast<const __bf16 *>(s)), ld(ld_), nred(nred_), col0(col0_) {}
+  __device__ __forceinline__ void load(int64_t red0) {
+    red_in = red0;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int idx = threadIdx.x + u * T;
+      const int cp = idx % UPR, rg = idx / UPR;
+      const int64_t c = col0 + 2 * cp;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t t = red0 + rg * 8 + i;
+        reg[u][i] = *reinterpret_cast<const uint32_t *>(src + min(t, nred - 1) * ld + c);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(__bf16 *lds) const {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int idx = threadIdx.x + u * T;
+      const int cp = idx % UPR, rg = idx / UPR;
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = red_in + rg * 8 + i < nred ? reg[u][i] : 0u;
+      const uint4 lo = make_uint4(lo16x2(w[0], w[1]), lo16x2(w[2], w[3]), lo16x2(w[4], w[5]), lo16x2(w[6], w[7]));
+      const uint4 hi = make_uint4(hi16x2(w[0], w[1]), hi16x2(w[2], w[3]), hi16x2(w[4], w[5]), hi16x2(w[6], w[7]));
+      *reinterpret_cast<uint4 *>(lds + lds_off(2 * cp, rg)) = lo;
+      *reinterpret_cast<uint4 *>(lds + lds_off(2 * cp + 1, rg)) = hi;
     }
   }
 };

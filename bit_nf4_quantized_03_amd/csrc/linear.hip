@@ -485,23 +485,25 @@ __global__ __launch_bounds__(256) void k_grad(GradParams p) {
   const int z = g / tiles, t = g % tiles;
   const int total = static_cast<int>((p.M + kBK - 1) / kBK);
   const int s0 = z * per, steps = min(per, total - s0);
+  // rows of this split's range only: the two-stage loop reads past its end
+  const int64_t red_end = min(p.M, static_cast<int64_t>(s0 + steps) * kBK);
   if (is_a) {
     const int64_t c0 = static_cast<int64_t>(t % tiles_c) * 256;
     const int64_t r0 = static_cast<int64_t>(t / tiles_c) * 64;
     Acc<CfgGradA> acc;
     acc.zero();
-    TransBf16<64, 256> la(p.dHb, p.rp, p.M, p.rp, r0);
-    TransBf16<256, 256> lb(p.X, p.K, p.M, p.K, c0);
-    mainloop<CfgGradA>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
+    TransBf16Narrow<64, 256> la(p.dHb, p.rp, red_end, r0), la1 = la;
+    TransBf16<256, 256> lb(p.X, p.K, red_end, p.K, c0), lb1 = lb;
+    mainloop2<CfgGradA>(acc, la, la1, lb, lb1, static_cast<int64_t>(s0) * kBK, steps, smem);
     store_f32<CfgGradA>(acc, p.a_part + static_cast<int64_t>(z) * p.rp * p.K, p.K, p.rp, p.K, r0, c0);
   } else {
     const int64_t c0 = static_cast<int64_t>(t % tiles_c) * 64;
     const int64_t r0 = static_cast<int64_t>(t / tiles_c) * 256;
     Acc<CfgGradB> acc;
     acc.zero();
-    TransBf16<256, 256> la(p.dY, p.N, p.M, p.N, r0);
-    TransBf16<64, 256> lb(p.Hs, p.rp, p.M, p.rp, c0);
-    mainloop<CfgGradB>(acc, la, lb, static_cast<int64_t>(s0) * kBK, steps, smem);
+    TransBf16<256, 256> la(p.dY, p.N, red_end, p.N, r0), la1 = la;
+    TransBf16Narrow<64, 256> lb(p.Hs, p.rp, red_end, c0), lb1 = lb;
+    mainloop2<CfgGradB>(acc, la, la1, lb, lb1, static_cast<int64_t>(s0) * kBK, steps, smem);
     store_f32<CfgGradB>(acc, p.b_part + static_cast<int64_t>(z) * p.N * p.rp, p.rp, p.N, p.rp, r0, c0);
   }
 }
