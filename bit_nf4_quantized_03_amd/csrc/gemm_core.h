@@ -109,63 +109,13 @@ __device__ __forceinline__ void mma_step(Acc<Cfg> &acc, const __bf16 *sA, const 
   }
 }
 
-// Pipelined main loop over `steps` reduction steps starting at `red0`, stride
-// 64. smem holds the double-buffered tiles [A0 | A1 | B0 | B1]. One barrier
-// per step; the loop is unrolled by two so both buffers are addressed with
-// immediates, and the last step is peeled. On entry the caller has
-// synchronized (LDS free); on exit all LDS reads are complete.
-template <class Cfg, class LA, class LB>
-__device__ __forceinline__ void mainloop(Acc<Cfg> &acc, LA &la, LB &lb, int64_t red0, int steps,
-                                         __bf16 *smem) {
-  if (steps <= 0) return;
-  __bf16 *sA0 = smem, *sA1 = smem + Cfg::kLdsA;
-  __bf16 *sB0 = smem + 2 * Cfg::kLdsA, *sB1 = sB0 + Cfg::kLdsB;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int wm = w / Cfg::WAVES_N, wn = w % Cfg::WAVES_N;
-  const FragAddr<Cfg::WTM> fa(wm * Cfg::WTM, lane);
-  const FragAddr<Cfg::WTN> fb(wn * Cfg::WTN, lane);
-  la.load(red0);
-  lb.load(red0);
-  la.store(sA0);
-  lb.store(sB0);
-  __syncthreads();
-  int s = 0;
-  for (; s + 2 < steps; s += 2) {
-    la.load(red0 + static_cast<int64_t>(s + 1) * kBK);
-    lb.load(red0 + static_cast<int64_t>(s + 1) * kBK);
-    mma_step<Cfg>(acc, sA0, sB0, fa, fb);
-    la.store(sA1);
-    lb.store(sB1);
-    __syncthreads();
-    la.load(red0 + static_cast<int64_t>(s + 2) * kBK);
-    lb.load(red0 + static_cast<int64_t>(s + 2) * kBK);
-    mma_step<Cfg>(acc, sA1, sB1, fa, fb);
-    la.store(sA0);
-    lb.store(sB0);
-    __syncthreads();
-  }
-  if (s + 1 < steps) {  // two steps left: the last one is in buffer 1
-    la.load(red0 + static_cast<int64_t>(s + 1) * kBK);
-    lb.load(red0 + static_cast<int64_t>(s + 1) * kBK);
-    mma_step<Cfg>(acc, sA0, sB0, fa, fb);
-    la.store(sA1);
-    lb.store(sB1);
-    __syncthreads();
-    mma_step<Cfg>(acc, sA1, sB1, fa, fb);
-  } else {
-    mma_step<Cfg>(acc, sA0, sB0, fa, fb);
-  }
-  __syncthreads();
-}
-
 // Main loop with two register stages: while step s runs on the MFMAs, the
 // global reads of steps s + 1 and s + 2 are in flight (loaders la0 / lb0 and
 // la1 / lb1 alternate). The loop runs an even number of steps with no
 // branches inside; the loaders must read rows at or past red0 + 64 steps as
-// zero (their reduction bound), so the steps past the end add nothing. Same
-// LDS layout and entry / exit conditions as mainloop.
+// zero (their reduction bound), so the steps past the end add nothing. smem
+// holds the double-buffered tiles [A0 | A1 | B0 | B1]. On entry the caller has
+// synchronized (LDS free); on exit every LDS read is complete.
 template <class Cfg, class LA, class LB>
 __device__ __forceinline__ void mainloop2(Acc<Cfg> &acc, LA &la0, LA &la1, LB &lb0, LB &lb1, int64_t red0,
                                           int steps, __bf16 *smem) {
@@ -208,80 +158,6 @@ __device__ __forceinline__ void mainloop2(Acc<Cfg> &acc, LA &la0, LA &la1, LB &l
 // Each loader covers ROWS output rows of one operand and a 64-deep reduction
 // step. load() issues the global reads into registers, store() writes the
 // LDS tile [ROWS][64].
-
-// bf16 source S[row][t] (t contiguous), row stride ld, rows >= nrows read as 0
-// (GUARD = false: the caller guarantees every row of the tile exists). The
-// per-lane part of each address is a 32-bit byte offset computed once; a step
-// only moves the uniform base pointer.
-template <int ROWS, int T, bool GUARD = true>
-struct RowBf16 {
-  static constexpr int CH = ROWS * 8 / T;
-  static_assert(ROWS * 8 % T == 0, "tile/threads mismatch");
-  const char *base;
-  uint32_t off[CH];
-  bool ok[CH];
-  uint4 reg[CH];
-  __device__ RowBf16(const void *s, int64_t ld, int64_t nrows, int64_t row0)
-      : base(static_cast<const char *>(s) + row0 * ld * 2) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int idx = threadIdx.x + i * T;
-      const int64_t r = row0 + (idx >> 3);
-      ok[i] = !GUARD || r < nrows;
-      const int64_t rc = (!GUARD || r < nrows) ? r : nrows - 1;   // clamped: always safe to read
-      off[i] = static_cast<uint32_t>(((rc - row0) * ld + (idx & 7) * 8) * 2);
-    }
-  }
-  __device__ __forceinline__ void load(int64_t red0) {
-    const char *p = base + red0 * 2;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      uint4 v = *reinterpret_cast<const uint4 *>(p + off[i]);
-      if (GUARD) v = make_uint4(ok[i] ? v.x : 0u, ok[i] ? v.y : 0u, ok[i] ? v.z : 0u, ok[i] ? v.w : 0u);
-      reg[i] = v;
-    }
-  }
-  __device__ __forceinline__ void store(__bf16 *lds) const {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int idx = threadIdx.x + i * T;
-      *reinterpret_cast<uint4 *>(lds + lds_off(idx >> 3, idx & 7)) = reg[i];
-    }
-  }
-};
-
-// fp32 source S[row][t], row stride ld (multiple of 4), rows >= nrows read as 0.
-template <int ROWS, int T>
-struct RowF32 {
-  static constexpr int CH = ROWS * 8 / T;       // 8-element (two float4) chunks
-  static_assert(ROWS * 8 % T == 0, "tile/threads mismatch");
-  const float *src;
-  int64_t ld, nrows, row0;
-  float4 reg[CH][2];
-  __device__ RowF32(const void *s, int64_t ld_, int64_t nrows_, int64_t row0_)
-      : src(static_cast<const float *>(s)), ld(ld_), nrows(nrows_), row0(row0_) {}
-  __device__ __forceinline__ void load(int64_t red0) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int idx = threadIdx.x + i * T;
-      const int64_t r = row0 + (idx >> 3);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        reg[i][h] = (r < nrows)
-                        ? *reinterpret_cast<const float4 *>(src + r * ld + red0 + (idx & 7) * 8 + 4 * h)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-  __device__ __forceinline__ void store(__bf16 *lds) const {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int idx = threadIdx.x + i * T;
-      uint4 v = make_uint4(pack_bf16x2(reg[i][0].x, reg[i][0].y), pack_bf16x2(reg[i][0].z, reg[i][0].w),
-                           pack_bf16x2(reg[i][1].x, reg[i][1].y), pack_bf16x2(reg[i][1].z, reg[i][1].w));
-      *reinterpret_cast<uint4 *>(lds + lds_off(idx >> 3, idx & 7)) = v;
-    }
-  }
-};
 
 // Units of the transposed loaders: 8 reduction rows x 8 output rows. For a
 // tile of ROWS output rows there are UPR = ROWS / 8 column groups cc and 8
@@ -360,58 +236,6 @@ struct TransBf16 {
   }
 };
 
-// Transposed fp32 source S[t][col] with any row stride: scalar loads, rounded
-// to bf16. Out-of-range elements read as 0.
-template <int ROWS, int T>
-struct TransF32 {
-  using U = TransUnits<ROWS, T>;
-  const float *src;
-  int64_t ld, nred, ncols, col0;
-  float reg[U::CH][8][8];
-  __device__ TransF32(const void *s, int64_t ld_, int64_t nred_, int64_t ncols_, int64_t col0_)
-      : src(static_cast<const float *>(s)), ld(ld_), nred(nred_), ncols(ncols_), col0(col0_) {}
-  __device__ __forceinline__ void load(int64_t red0) {
-    const bool vec = (ld & 3) == 0;   // rows 16-byte aligned: vector loads
-#pragma unroll
-    for (int u = 0; u < U::CH; ++u) {
-      const int idx = threadIdx.x + u * T;
-      if (!U::active(idx)) continue;
-      const int cc = U::cc(idx), rg = U::rg(idx);
-      const int64_t c0 = col0 + cc * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t t = red0 + rg * 8 + i;
-        if (vec && t < nred && c0 + 8 <= ncols) {
-          const float4 lo = *reinterpret_cast<const float4 *>(src + t * ld + c0);
-          const float4 hi = *reinterpret_cast<const float4 *>(src + t * ld + c0 + 4);
-          reg[u][i][0] = lo.x; reg[u][i][1] = lo.y; reg[u][i][2] = lo.z; reg[u][i][3] = lo.w;
-          reg[u][i][4] = hi.x; reg[u][i][5] = hi.y; reg[u][i][6] = hi.z; reg[u][i][7] = hi.w;
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int64_t c = c0 + j;
-            reg[u][i][j] = (t < nred && c < ncols) ? src[t * ld + c] : 0.0f;
-          }
-        }
-      }
-    }
-  }
-  __device__ __forceinline__ void store(__bf16 *lds) const {
-#pragma unroll
-    for (int u = 0; u < U::CH; ++u) {
-      const int idx = threadIdx.x + u * T;
-      if (!U::active(idx)) continue;
-      const int cc = U::cc(idx), rg = U::rg(idx);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint4 v = make_uint4(pack_bf16x2(reg[u][0][j], reg[u][1][j]), pack_bf16x2(reg[u][2][j], reg[u][3][j]),
-                             pack_bf16x2(reg[u][4][j], reg[u][5][j]), pack_bf16x2(reg[u][6][j], reg[u][7][j]));
-        *reinterpret_cast<uint4 *>(lds + lds_off(cc * 8 + j, rg)) = v;
-      }
-    }
-  }
-};
-
 // Transposed bf16 source S[t][col] for small tiles (UNITS = 4 ROWS a multiple
 // of T): units of 8 reduction rows x 2 output rows, one 4-byte load per
 // reduction row, so every thread has whole units and the loads need no
@@ -458,199 +282,6 @@ struct TransBf16Narrow {
     }
   }
 };
-
-// Transposed fp32 source S[t][col] for small tiles: units of 8 reduction rows
-// x 2 output rows (one 8-byte load per reduction row), so that every thread
-// of the group has a unit. Out-of-range elements read as 0.
-template <int ROWS, int T>
-struct TransF32Narrow {
-  static constexpr int UPR = ROWS / 2;          // column pairs
-  static constexpr int UNITS = UPR * 8;         // x 8 reduction-row groups
-  static constexpr int CH = (UNITS + T - 1) / T;
-  const float *src;
-  int64_t ld, nred, ncols, col0;
-  float2 reg[CH][8];
-  __device__ TransF32Narrow(const void *s, int64_t ld_, int64_t nred_, int64_t ncols_, int64_t col0_)
-      : src(static_cast<const float *>(s)), ld(ld_), nred(nred_), ncols(ncols_), col0(col0_) {}
-  __device__ __forceinline__ void load(int64_t red0) {
-    const bool vec = (ld & 1) == 0;
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int idx = threadIdx.x + u * T;
-      if (UNITS % T != 0 && idx >= UNITS) continue;
-      const int cp = idx % UPR, rg = idx / UPR;
-      const int64_t c = col0 + 2 * cp;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t t = red0 + rg * 8 + i;
-        if (vec && t < nred && c + 2 <= ncols) {
-          reg[u][i] = *reinterpret_cast<const float2 *>(src + t * ld + c);
-        } else {
-          reg[u][i].x = (t < nred && c < ncols) ? src[t * ld + c] : 0.0f;
-          reg[u][i].y = (t < nred && c + 1 < ncols) ? src[t * ld + c + 1] : 0.0f;
-        }
-      }
-    }
-  }
-  __device__ __forceinline__ void store(__bf16 *lds) const {
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int idx = threadIdx.x + u * T;
-      if (UNITS % T != 0 && idx >= UNITS) continue;
-      const int cp = idx % UPR, rg = idx / UPR;
-      const uint4 lo = make_uint4(pack_bf16x2(reg[u][0].x, reg[u][1].x), pack_bf16x2(reg[u][2].x, reg[u][3].x),
-                                  pack_bf16x2(reg[u][4].x, reg[u][5].x), pack_bf16x2(reg[u][6].x, reg[u][7].x));
-      const uint4 hi = make_uint4(pack_bf16x2(reg[u][0].y, reg[u][1].y), pack_bf16x2(reg[u][2].y, reg[u][3].y),
-                                  pack_bf16x2(reg[u][4].y, reg[u][5].y), pack_bf16x2(reg[u][6].y, reg[u][7].y));
-      *reinterpret_cast<uint4 *>(lds + lds_off(2 * cp, rg)) = lo;
-      *reinterpret_cast<uint4 *>(lds + lds_off(2 * cp + 1, rg)) = hi;
-    }
-  }
-};
-
-// NF4 + DQ weight W [N][K] decoded along its rows: output row = n, reduction
-// over k. K is a multiple of 64, so a 64-step of one row is exactly one
-// quantization block with scale cs[(n*K + k0)/64]. lv2: LDS table of the level
-// pairs (level[b >> 4], level[b & 15]) for every code byte b.
-template <int ROWS, int T, bool GUARD = true>
-struct Nf4Row {
-  static constexpr int CH = ROWS * 2 / T;       // 16-byte code chunks per thread
-  static_assert(ROWS * 2 % T == 0, "tile/threads mismatch");
-  const uint8_t *cbase;
-  const float *sbase;
-  const float2 *lv2;
-  uint32_t coff[CH], soff[CH];
-  bool ok[CH];
-  uint4 reg[CH];
-  float sc[CH];
-  __device__ Nf4Row(const uint8_t *c, const float *s, const float2 *lv2_, int64_t N, int64_t K,
-                    int64_t row0)
-      : cbase(c + row0 * K / 2), sbase(s + row0 * K / kBlock), lv2(lv2_) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int idx = threadIdx.x + i * T;
-      const int64_t n = row0 + (idx >> 1);
-      ok[i] = !GUARD || n < N;
-      const int64_t nc = (!GUARD || n < N) ? n : N - 1;
-      coff[i] = static_cast<uint32_t>((nc - row0) * K / 2 + (idx & 1) * 16);
-      soff[i] = static_cast<uint32_t>((nc - row0) * K / kBlock);
-    }
-  }
-  __device__ __forceinline__ void load(int64_t red0) {
-    const uint8_t *cp = cbase + red0 / 2;
-    const float *sp = sbase + red0 / kBlock;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      reg[i] = *reinterpret_cast<const uint4 *>(cp + coff[i]);
-      const float c = sp[soff[i]];
-      sc[i] = (!GUARD || ok[i]) ? c : 0.0f;     // rows past the end decode to 0
-    }
-  }
-  __device__ __forceinline__ void store(__bf16 *lds) const {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int idx = threadIdx.x + i * T;
-      const uint32_t w[4] = {reg[i].x, reg[i].y, reg[i].z, reg[i].w};
-      const int row = idx >> 1;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t ow[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const float2 pr = lv2[(w[q] >> (8 * b)) & 0xFFu];
-          ow[b] = pack_bf16x2(__fmul_rn(pr.x, sc[i]), __fmul_rn(pr.y, sc[i]));
-        }
-        *reinterpret_cast<uint4 *>(lds + lds_off(row, (idx & 1) * 4 + q)) =
-            make_uint4(ow[0], ow[1], ow[2], ow[3]);
-      }
-    }
-  }
-};
-
-// NF4 + DQ weight W [N][K] decoded transposed: output row = k, reduction over
-// n (N is a multiple of 64, so every reduction row of a step exists). A unit
-// is 8 rows n x 8 columns k: one 32-bit word of codes per row, inside one
-// quantization block. With twice as many threads as units, the two threads of
-// a unit read the same words and each decodes four of its eight output rows.
-// Columns k >= K decode to 0 (GUARD = false: the tile lies inside K).
-template <int ROWS, int T, bool GUARD = true>
-struct Nf4Trans {
-  using U = TransUnits<ROWS, T>;
-  static constexpr bool kSplit = (T == 2 * U::UNITS);
-  static constexpr int CH = kSplit ? 1 : U::CH;
-  static constexpr int JN = kSplit ? 4 : 8;     // output rows decoded per thread and unit
-  const uint8_t *cbase;
-  const float *sbase;
-  const float2 *lv2;
-  int64_t K;
-  uint32_t coff[CH], soff[CH];
-  bool ok[CH];
-  uint32_t reg[CH][8];
-  float sc[CH][8];
-  __device__ __forceinline__ int unit(int u) const {
-    return kSplit ? (threadIdx.x % U::UNITS) : static_cast<int>(threadIdx.x) + u * T;
-  }
-  __device__ Nf4Trans(const uint8_t *c, const float *s, const float2 *lv2_, int64_t N, int64_t K_,
-                      int64_t col0)
-      : cbase(c + col0 / 2), sbase(s + col0 / kBlock), lv2(lv2_), K(K_) {
-    (void)N;
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int idx = unit(u);
-      const int cc = U::cc(idx), rg = U::rg(idx);
-      const int64_t k = col0 + cc * 8;
-      ok[u] = !GUARD || k < K;
-      const int64_t kc = (!GUARD || k < K) ? k : K - 8;
-      coff[u] = static_cast<uint32_t>((rg * 8) * K / 2 + (kc - col0) / 2);
-      soff[u] = static_cast<uint32_t>((rg * 8) * K / kBlock + (kc - col0) / kBlock);
-    }
-  }
-  __device__ __forceinline__ void load(int64_t red0) {
-    const uint8_t *cp = cbase + red0 * K / 2;
-    const float *sp = sbase + red0 * K / kBlock;
-    const uint32_t rowc = static_cast<uint32_t>(K / 2), rows = static_cast<uint32_t>(K / kBlock);
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int idx = unit(u);
-      if (!kSplit && !U::active(idx)) continue;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        reg[u][i] = *reinterpret_cast<const uint32_t *>(cp + coff[u] + i * rowc);
-        const float c = sp[soff[u] + i * rows];
-        sc[u][i] = (!GUARD || ok[u]) ? c : 0.0f;
-      }
-    }
-  }
-  __device__ __forceinline__ void store(__bf16 *lds) const {
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int idx = unit(u);
-      if (!kSplit && !U::active(idx)) continue;
-      const int cc = U::cc(idx), rg = U::rg(idx);
-      const int j0 = kSplit ? 4 * (static_cast<int>(threadIdx.x) / U::UNITS) : 0;
-#pragma unroll
-      for (int jb = 0; jb < JN / 2; ++jb) {
-        // one code byte per row gives output rows j and j + 1
-        const int j = j0 + 2 * jb;
-        float v0[8], v1[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float2 pr = lv2[(reg[u][i] >> (4 * j)) & 0xFFu];
-          v0[i] = __fmul_rn(pr.x, sc[u][i]);
-          v1[i] = __fmul_rn(pr.y, sc[u][i]);
-        }
-        *reinterpret_cast<uint4 *>(lds + lds_off(cc * 8 + j, rg)) =
-            make_uint4(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v0[4], v0[5]),
-                       pack_bf16x2(v0[6], v0[7]));
-        *reinterpret_cast<uint4 *>(lds + lds_off(cc * 8 + j + 1, rg)) =
-            make_uint4(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]), pack_bf16x2(v1[4], v1[5]),
-                       pack_bf16x2(v1[6], v1[7]));
-      }
-    }
-  }
-};
-
-// ----------------------------------------------------------------- epilogues
 
 // bf16 C[row][col] = bf16(alpha * acc), rows < nrows, cols < ncols (checked
 // only when GUARD).
