@@ -372,6 +372,27 @@ def main():
     del Ws, qs, outs
     torch.cuda.empty_cache()
 
+    # Context, not part of the path: the dense bf16 library GEMM (torch.matmul,
+    # hipBLASLt) on the dequantized weight at the same shapes, i.e. what an
+    # unfused "dequantize, then GEMM" forward and dX would cost.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    library = {}
+    for key, fn, fl in (("fwd_x_wt", lambda: torch.matmul(X, Wdq.t()), 2.0 * M * N * K),
+                        ("dx_dy_w", lambda: torch.matmul(dY, Wdq), 2.0 * M * N * K)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(10):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / 10
+        library[key] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12,
+                        "plus_dequantize_us": us + rows["dequantize_bf16"]["us"]}
+        log(f"library bf16 GEMM {key}: {us:.1f} us ({library[key]['tflops']:.0f} TFLOP/s); "
+            f"+ dequantize {library[key]['plus_dequantize_us']:.1f} us")
+
     # ---------------------------------------------- decode (skinny M) GEMV
     decode = {}
     if not args.no_decode:
@@ -581,6 +602,7 @@ def main():
                    "step_flops": fwd_flops + bwd_flops},
         "roofline": roofline,
         "rows": rows,
+        "library_gemm_context": library,
         "decode": decode,
         "mlp65b": mlp,
         "dequant_solo": dq_solo,

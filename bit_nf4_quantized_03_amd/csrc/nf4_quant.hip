@@ -17,9 +17,11 @@
 //                   16-byte loads, per-64 absmax by DPP lane exchanges, nearest-level codes, packed stores, fp32 absmax
 //                   to the workspace and the fp64 tree sum of the DQ block's
 //                   256 constants.
-//   k_dq_codes      up to 256 workgroups, each of which first completes the
-//                   same fp64 tree over the per-DQ-block partials (the mean),
-//                   then takes DQ blocks in turn: per-block scale, int8 codes.
+//   k_dq_codes_mean up to 1024 DQ blocks: 256 workgroups, each of which first
+//                   completes the same fp64 tree over the per-DQ-block partials
+//                   (the mean), then takes DQ blocks in turn: scale, int8 codes.
+//   k_tree_mean     larger tensors: one workgroup completes the tree (the mean),
+//   k_dq_codes      then one workgroup per DQ block: scale and int8 codes.
 //   k_dequant       one workgroup per DQ block: per-block scales in LDS, then
 //                   4-byte code loads expanded to fp32 or bf16 stores.
 #include <algorithm>
@@ -291,7 +293,8 @@ __global__ __launch_bounds__(kThreads) void k_absmax_codes(const uint8_t *__rest
 constexpr int kTreeChunk = 8192;
 constexpr int kTreeRun = kTreeChunk / kThreads;   // 32
 constexpr int kTreeMaxChunks = kThreads * kTreeRun;
-constexpr int64_t kDqCodeGroups = 256;   // workgroups of k_dq_codes (each recomputes the mean)
+constexpr int64_t kDqCodeGroups = 256;       // workgroups of k_dq_codes_mean (each recomputes the mean)
+constexpr int64_t kDqFusedMaxBlocks = 1024;  // larger tensors take k_tree_mean + k_dq_codes
 
 // Sum of the perfect binary tree over top leaves (top a power of two <= kTreeChunk)
 // src[base + i], zero past limit. Every thread gets the result.
@@ -345,40 +348,65 @@ __device__ float tree_mean(const double *__restrict__ partial, int64_t nd, int64
   return static_cast<float>(total / static_cast<double>(nb));
 }
 
-// Workgroups take DQ blocks d = blockIdx.x + i * gridDim.x: scale
-// s2 = max |fp32(a - mean)| over the block and the int8 codes.
-__global__ __launch_bounds__(kThreads) void k_dq_codes(const float *__restrict__ absmax_ws,
-                                                       const double *__restrict__ partial, int64_t nb,
-                                                       int64_t nd, float *__restrict__ dq_mean,
-                                                       int8_t *__restrict__ absmax_q,
-                                                       float *__restrict__ dq_scale) {
+// DQ scale s2 = max |fp32(a - mean)| over DQ block d and its int8 codes, one
+// thread per absmax constant.
+__device__ __forceinline__ void dq_block(const float *__restrict__ absmax_ws, int64_t nb, int64_t d, float mu,
+                                         int8_t *__restrict__ absmax_q, float *__restrict__ dq_scale,
+                                         float *wmax) {
+  const int tid = threadIdx.x;
+  const int64_t b = d * kDqBlock + tid;
+  const bool valid = b < nb;
+  const float a = valid ? absmax_ws[b] : 0.0f;
+  const float dv = valid ? __fsub_rn(a, mu) : 0.0f;
+  float m = fabsf(dv);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __syncthreads();   // wmax free
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  const float s2 = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  int q = 0;
+  if (s2 > 0.0f) {
+    const float u = __fmul_rn(__fdiv_rn(dv, s2), 127.0f);
+    q = static_cast<int>(rintf(u));
+    q = min(max(q, -127), 127);
+  }
+  if (valid) absmax_q[b] = static_cast<int8_t>(q);
+  if (tid == 0) dq_scale[d] = s2;
+}
+
+// Up to a few thousand DQ blocks: every workgroup completes the mean itself
+// (the partials come from L2) and takes DQ blocks d = blockIdx.x + i *
+// gridDim.x; workgroup 0 stores the mean. One launch instead of two.
+__global__ __launch_bounds__(kThreads) void k_dq_codes_mean(const float *__restrict__ absmax_ws,
+                                                            const double *__restrict__ partial, int64_t nb,
+                                                            int64_t nd, float *__restrict__ dq_mean,
+                                                            int8_t *__restrict__ absmax_q,
+                                                            float *__restrict__ dq_scale) {
   __shared__ double wsum[kThreads / 64];
   __shared__ double csum[kTreeMaxChunks];
   __shared__ float wmax[kThreads / 64];
-  const int tid = threadIdx.x;
   const float mu = tree_mean(partial, nd, nb, wsum, csum);
-  if (blockIdx.x == 0 && tid == 0) dq_mean[0] = mu;
-  for (int64_t d = blockIdx.x; d < nd; d += gridDim.x) {
-    const int64_t b = d * kDqBlock + tid;
-    const bool valid = b < nb;
-    const float a = valid ? absmax_ws[b] : 0.0f;
-    const float dv = valid ? __fsub_rn(a, mu) : 0.0f;
-    float m = fabsf(dv);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-    __syncthreads();   // wmax free
-    if ((tid & 63) == 0) wmax[tid >> 6] = m;
-    __syncthreads();
-    const float s2 = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    int q = 0;
-    if (s2 > 0.0f) {
-      const float u = __fmul_rn(__fdiv_rn(dv, s2), 127.0f);
-      q = static_cast<int>(rintf(u));
-      q = min(max(q, -127), 127);
-    }
-    if (valid) absmax_q[b] = static_cast<int8_t>(q);
-    if (tid == 0) dq_scale[d] = s2;
-  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) dq_mean[0] = mu;
+  for (int64_t d = blockIdx.x; d < nd; d += gridDim.x) dq_block(absmax_ws, nb, d, mu, absmax_q, dq_scale, wmax);
+}
+
+// Larger tensors: one workgroup completes the mean ...
+__global__ __launch_bounds__(kThreads) void k_tree_mean(const double *__restrict__ partial, int64_t nd,
+                                                        int64_t nb, float *__restrict__ dq_mean) {
+  __shared__ double wsum[kThreads / 64];
+  __shared__ double csum[kTreeMaxChunks];
+  const float mu = tree_mean(partial, nd, nb, wsum, csum);
+  if (threadIdx.x == 0) dq_mean[0] = mu;
+}
+
+// ... and one workgroup per DQ block reads it.
+__global__ __launch_bounds__(kThreads) void k_dq_codes(const float *__restrict__ absmax_ws, int64_t nb,
+                                                       const float *__restrict__ dq_mean,
+                                                       int8_t *__restrict__ absmax_q,
+                                                       float *__restrict__ dq_scale) {
+  __shared__ float wmax[kThreads / 64];
+  dq_block(absmax_ws, nb, blockIdx.x, dq_mean[0], absmax_q, dq_scale, wmax);
 }
 
 // ------------------------------------------------------------ dequantize
@@ -498,8 +526,13 @@ hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, uint8_t *codes
   prof_end(kProfQuantize, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_dq_codes, dim3(std::min<int64_t>(nd, kDqCodeGroups)), dim3(kThreads), 0, s, absmax_ws,
-                     part, nb, nd, dq_mean, absmax_q, dq_scale);
+  if (nd <= kDqFusedMaxBlocks) {
+    hipLaunchKernelGGL(k_dq_codes_mean, dim3(std::min<int64_t>(nd, kDqCodeGroups)), dim3(kThreads), 0, s,
+                       absmax_ws, part, nb, nd, dq_mean, absmax_q, dq_scale);
+  } else {
+    hipLaunchKernelGGL(k_tree_mean, dim3(1), dim3(kThreads), 0, s, part, nd, nb, dq_mean);
+    hipLaunchKernelGGL(k_dq_codes, dim3(nd), dim3(kThreads), 0, s, absmax_ws, nb, dq_mean, absmax_q, dq_scale);
+  }
   return hipGetLastError();
 }
 
