@@ -164,43 +164,52 @@ struct Nf4RowBigT {
 using Nf4RowBig = Nf4RowBigT<kBigThreads>;
 
 // Input-gradient B operand: NF4 decoded transposed (output row k, reduction
-// along n). One unit of 8 rows n x 8 columns k per thread (see TransUnits);
-// quarter q decodes output rows 8 cc + 2q and 8 cc + 2q + 1.
-struct Nf4TransBig {
-  using U = TransUnits<kBigRows, kBigThreads>;
+// along n), in units of 8 rows n x 8 columns k (see TransUnits). With 256
+// threads a thread decodes a whole unit; with 512, thread t takes rows
+// 4 (t / 256) .. + 3 of unit t % 256 (so a wave's lanes hold eight whole
+// units' halves and its 8-byte stores still land on distinct chunk slots).
+// Quarter q decodes output rows 8 cc + 2q and 8 cc + 2q + 1.
+template <int T>
+struct Nf4TransBigT {
+  static_assert(T == 256 || T == 512, "256 or 512 threads");
+  static constexpr int R = 8 * 256 / T;   // rows n per thread
+  using U = TransUnits<kBigRows, 256>;
   const uint8_t *cbase;
   const float *sbase;
-  uint32_t coff, soff, rowc, rows;
-  uint32_t reg[8];
-  float sc[8];
-  __device__ Nf4TransBig(const uint8_t *c, const float *s, int64_t K, int64_t col0)
+  // byte offset of the thread's first code word from cbase; the scale index
+  // of that word's block is coff / 32 (K is a multiple of 64, so n K / 2 is a
+  // multiple of 32 and the column part cc * 4 < 128 adds cc / 8)
+  uint32_t coff;
+  uint32_t reg[R];
+  float sc[R];
+  __device__ Nf4TransBigT(const uint8_t *c, const float *s, int64_t K, int64_t col0)
       : cbase(c + col0 / 2), sbase(s + col0 / kBlock) {
-    const int idx = threadIdx.x;
+    const int idx = threadIdx.x & 255, hh = threadIdx.x >> 8;
     const int cc = U::cc(idx), rg = U::rg(idx);
     int64_t k = col0 + cc * 8;
     if (k >= K) k = K - 8;
-    coff = static_cast<uint32_t>((rg * 8) * K / 2 + (k - col0) / 2);
-    soff = static_cast<uint32_t>((rg * 8) * K / kBlock + (k - col0) / kBlock);
-    rowc = static_cast<uint32_t>(K / 2);
-    rows = static_cast<uint32_t>(K / kBlock);
+    const int64_t n = rg * 8 + hh * R;
+    coff = static_cast<uint32_t>(n * K / 2 + (k - col0) / 2);
   }
   __device__ __forceinline__ void load(int64_t red0, int64_t K) {
+    // the row parts of the addresses are wave-uniform
     const uint8_t *cp = cbase + red0 * K / 2;
     const float *sp = sbase + red0 * K / kBlock;
+    const uint32_t so = coff >> 5;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      reg[i] = *reinterpret_cast<const uint32_t *>(cp + coff + i * rowc);
-      sc[i] = sp[soff + i * rows];
+    for (int i = 0; i < R; ++i) {
+      reg[i] = *reinterpret_cast<const uint32_t *>(cp + i * (K / 2) + coff);
+      sc[i] = (sp + i * (K / kBlock))[so];
     }
   }
-  static constexpr int kLoads = 16;
+  static constexpr int kLoads = 2 * R;
   static constexpr int kWrites = 2;
   struct Pairs {
-    float2 pr[8];
+    float2 pr[R];
   };
   __device__ __forceinline__ void lookup(Pairs &p, const float2 *lv2, int q) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p.pr[i] = lv2[((reg[i] >> (8 * q)) & 0xFFu) * kLvCopies];
+    for (int i = 0; i < R; ++i) p.pr[i] = lv2[((reg[i] >> (8 * q)) & 0xFFu) * kLvCopies];
   }
   __device__ __forceinline__ void store_part(__bf16 *lds, const float2 *lv2, int q) const {
     Pairs p;
@@ -208,22 +217,31 @@ struct Nf4TransBig {
     finish(lds, p, q);
   }
   __device__ __forceinline__ void finish(__bf16 *lds, const Pairs &p, int q) const {
-    const int idx = threadIdx.x;
+    const int idx = threadIdx.x & 255, hh = threadIdx.x >> 8;
     const int cc = U::cc(idx), rg = U::rg(idx);
-    float v0[8], v1[8];
+    float v0[R], v1[R];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < R; ++i) {
       v0[i] = __fmul_rn(p.pr[i].x, sc[i]);
       v1[i] = __fmul_rn(p.pr[i].y, sc[i]);
     }
-    *reinterpret_cast<uint4 *>(lds + lds_off(cc * 8 + 2 * q, rg)) =
-        make_uint4(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v0[4], v0[5]),
-                   pack_bf16x2(v0[6], v0[7]));
-    *reinterpret_cast<uint4 *>(lds + lds_off(cc * 8 + 2 * q + 1, rg)) =
-        make_uint4(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]), pack_bf16x2(v1[4], v1[5]),
-                   pack_bf16x2(v1[6], v1[7]));
+    // rows 8 cc + j have swz = j ^ (cc & 3), so logical chunk rg of row
+    // 8 cc + j sits at chunk rg ^ (cc & 3) ^ j
+    const int x = rg ^ (cc & 3);
+    __bf16 *d0 = lds + (cc * 8 + 2 * q) * kLDK + ((x ^ (2 * q)) << 3) + hh * R;
+    __bf16 *d1 = lds + (cc * 8 + 2 * q + 1) * kLDK + ((x ^ (2 * q + 1)) << 3) + hh * R;
+    if (R == 8) {
+      *reinterpret_cast<uint4 *>(d0) = make_uint4(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                                                  pack_bf16x2(v0[4], v0[5]), pack_bf16x2(v0[6], v0[7]));
+      *reinterpret_cast<uint4 *>(d1) = make_uint4(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]),
+                                                  pack_bf16x2(v1[4], v1[5]), pack_bf16x2(v1[6], v1[7]));
+    } else {
+      *reinterpret_cast<uint2 *>(d0) = make_uint2(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]));
+      *reinterpret_cast<uint2 *>(d1) = make_uint2(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]));
+    }
   }
 };
+using Nf4TransBig = Nf4TransBigT<kBigThreads>;
 
 // Fragments of one 16-deep slice for a wave's WTM x WTN block.
 template <class Cfg>

@@ -87,6 +87,8 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void k_fwd_big(FwdParams p, Nf4Ta
 
 // ------------------------------------------------------------- backward dX
 
+using CfgDx = CfgBig8;
+
 struct DxParams {
   const void *dY;       // bf16 [M, N]
   const uint8_t *codes; // NF4 codes of W [N, K]
@@ -98,11 +100,13 @@ struct DxParams {
   int rp;
 };
 
-// Input gradient: one 256 x 256 tile of dX per workgroup of four waves
-// (XCD-aware order). Eight waves, as in the forward, ran slower here: the
-// transposed decode needs more registers than two waves per SIMD leave.
-__global__ __launch_bounds__(kBigThreads, 1) void k_dx_big(DxParams p, Nf4Tables tab) {
-  using Cfg = CfgBig;
+// Input gradient: one 256 x 256 tile of dX per workgroup (XCD-aware order),
+// run with eight waves as the forward is: the transposed decode gives each
+// thread half an 8 x 8 unit (four rows n), which keeps the kernel within the
+// registers two waves per SIMD leave.
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::kThreads, 1) void k_dx_big(DxParams p, Nf4Tables tab) {
+  constexpr int T = Cfg::kThreads;
   __shared__ __attribute__((aligned(16))) __bf16 sa0[Cfg::kLdsA], sa1[Cfg::kLdsA];
   __shared__ __attribute__((aligned(16))) __bf16 sb0[Cfg::kLdsB], sb1[Cfg::kLdsB];
   const BigSmem smem{sa0, sa1, sb0, sb1};
@@ -116,14 +120,14 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_dx_big(DxParams p, Nf4Tables
   Acc<Cfg> acc;
   acc.zero();
   {
-    DirectRows da(p.dY, p.N, p.M, m0);
-    Nf4TransBig l0(p.codes, p.cs, p.K, k0), l1 = l0;
+    DirectRowsT<T> da(p.dY, p.N, p.M, m0);
+    Nf4TransBigT<T> l0(p.codes, p.cs, p.K, k0), l1 = l0;
     const int64_t K = p.K;
-    auto load = [K](Nf4TransBig &l, int s) { l.load(static_cast<int64_t>(s) * kBK, K); };
+    auto load = [K](Nf4TransBigT<T> &l, int s) { l.load(static_cast<int64_t>(s) * kBK, K); };
     big_mainloop_nf4<Cfg>(acc, da, l0, l1, load, static_cast<int>(p.N / kBK), smem, lv);
   }
   if (p.rp > 0) {
-    DirectRows da(p.dHb, p.rp, p.M, m0), db(p.Atb, p.rp, p.K, k0);
+    DirectRowsT<T> da(p.dHb, p.rp, p.M, m0), db(p.Atb, p.rp, p.K, k0);
     big_mainloop_dense<Cfg>(acc, da, db, p.rp / kBK, smem);
   }
   if (m0 + 256 <= p.M && k0 + 256 <= p.K)
@@ -707,7 +711,7 @@ hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const 
     DxParams dp{dY, a.codes, b.cs, b.dHb, b.Atb, dX, a.M, a.N, a.K, pl.rp};
     dim3 g(grid_blocks(a.K, 256) * grid_blocks(a.M, 256), 1, 1);
     prof_begin(kProfBwdDx, s);
-    hipLaunchKernelGGL(k_dx_big, g, dim3(kBigThreads), 0, s, dp, tab);
+    hipLaunchKernelGGL(k_dx_big<CfgDx>, g, dim3(CfgDx::kThreads), 0, s, dp, tab);
     prof_end(kProfBwdDx, s);
   }
   if (pl.rp > 0) {
