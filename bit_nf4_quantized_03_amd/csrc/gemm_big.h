@@ -1,10 +1,11 @@
 // Large-tile main loop for the two dequant-GEMMs (forward Y and input
 // gradient dX): a 256 x 256 output tile per workgroup, built on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulators in registers. Two layouts:
-// four waves of 128 x 128 (CfgBig, one wave per SIMD, 256 accumulation
-// registers each) and eight waves of 128 x 64 (CfgBig8, two waves per SIMD,
-// 128 accumulators each, so one wave's waits are covered by the other's
-// MFMAs).
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulators in registers. Both kernels
+// run eight waves of 128 x 64 (CfgBig8, two waves per SIMD, 128 accumulators
+// each, so one wave's waits are covered by the other's MFMAs); the loaders
+// and the main loop also take the four-wave layout of 128 x 128 per wave
+// (256 threads, one wave per SIMD, 256 accumulators), which ran 5-10 %
+// slower.
 //
 // Per 64-deep reduction step s:
 //   * the dense operand (X, dY or an adapter factor) of step s + 1 is copied
@@ -24,16 +25,13 @@
 
 namespace qnf4 {
 
-constexpr int kBigThreads = 256;    // four waves: 128 x 128 per wave
-constexpr int kBig8Threads = 512;   // eight waves: 128 x 64 per wave, two waves per SIMD
 // Copies of the 256-entry level-pair table in LDS, interleaved entry by entry
 // (entry e of copy c at e * kLvCopies + c); lane l reads copy l % kLvCopies,
 // so two lanes of one 32-lane LDS pass meet in a bank only when they share a
 // copy and their entries have the same parity.
 constexpr int kLvCopies = 16;
 constexpr int kBigRows = 256;
-using CfgBig = TileCfg<256, 256, 2, 2>;
-using CfgBig8 = TileCfg<256, 256, 2, 4>;
+using CfgBig8 = TileCfg<256, 256, 2, 4>;   // eight waves: 128 x 64 per wave
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -95,7 +93,6 @@ struct DirectRowsT {
     asm volatile("" ::: "memory");
   }
 };
-using DirectRows = DirectRowsT<kBigThreads>;
 
 // Forward B operand: NF4 rows n (reduction along k). Thread t decodes the
 // 16-byte code chunks of rows t/2 + (T/2) i (i < 512/T), half t&1 of the
@@ -161,7 +158,6 @@ struct Nf4RowBigT {
     finish(lds, p, q);
   }
 };
-using Nf4RowBig = Nf4RowBigT<kBigThreads>;
 
 // Input-gradient B operand: NF4 decoded transposed (output row k, reduction
 // along n), in units of 8 rows n x 8 columns k (see TransUnits). With 256
@@ -241,7 +237,6 @@ struct Nf4TransBigT {
     }
   }
 };
-using Nf4TransBig = Nf4TransBigT<kBigThreads>;
 
 // Fragments of one 16-deep slice for a wave's WTM x WTN block.
 template <class Cfg>
