@@ -96,6 +96,19 @@ def test_ragged_m_and_rank(qb, cb, M, r):
     _bwd(qb, c, f"ragged M={M} r={r}")
 
 
+@pytest.mark.parametrize("M", [1, 130, 300])
+def test_max_rank(qb, cb, M):
+    """r = 256, the largest rank the boundary accepts: four 64-column adapter
+    tiles in the down-projection, the gradient tiles and the GEMMs' adapter
+    steps, with ragged M, N = 320 and K = 448 (reduction lengths of 5 and 7
+    steps of 64)."""
+    wl = synth.make_linear_workload("maxrank", M=M, N=320, K=448, r=256, alpha=16.0,
+                                    seed=7000 + M, w_dtype="bf16")
+    c = Case(qb, wl, cb)
+    _fwd(qb, c, f"max rank M={M}")
+    _bwd(qb, c, f"max rank M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 7, 16, 23, 32])
 @pytest.mark.parametrize("r", [0, 8, 72])
 def test_decode_split_k_ragged(qb, cb, M, r):
