@@ -142,8 +142,8 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void k_dx_big(DxParams p, Nf4Tabl
 // dY B straight from the fp32 adapter factors; k_adapter_finish then sums
 // them and, in the same launch, writes the other small operands of the big
 // GEMMs:
-//   Hs  [M][rp]   bf16(s H), columns >= r zero          (forward adapter step)
-//   dHb [M][rp]   bf16(s dY B), columns >= r zero       (backward adapter step)
+//   Hs  [M][rp]   bf16(s H), columns >= r zero          (forward adapter step; dB)
+//   dHb [M][rp]   bf16(s dY B), columns >= r zero       (backward adapter step; dA)
 //   cs  [nb]      block scales c_b of the NF4 weight
 //   Bb  [N][rp]   bf16(B), columns >= r zero            (forward adapter step)
 //   Atb [K][rp]   bf16(A^T), columns >= r zero          (backward adapter step)
