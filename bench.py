@@ -36,6 +36,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -61,14 +62,23 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank space (a comment edit does not
+    change the kernel)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(kernel: str) -> str:
-    """Hash of the sources a kernel is built from."""
+    """Hash of the code (comments and spacing removed) of the sources a kernel
+    is built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_nf4_quantized_03_amd", "csrc")
     for name in sorted(KERNEL_SOURCES[kernel]):
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
