@@ -17,9 +17,9 @@
 //                   16-byte loads, per-64 absmax by DPP lane exchanges, nearest-level codes, packed stores, fp32 absmax
 //                   to the workspace and the fp64 tree sum of the DQ block's
 //                   256 constants.
-//   k_dq_codes_mean up to 1024 DQ blocks: 256 workgroups, each of which first
-//                   completes the same fp64 tree over the per-DQ-block partials
-//                   (the mean), then takes DQ blocks in turn: scale, int8 codes.
+//   k_dq_codes_mean up to 1024 DQ blocks: one workgroup per DQ block, each of
+//                   which completes the same fp64 tree over the per-DQ-block
+//                   partials (the mean), then the block's scale and int8 codes.
 //   k_tree_mean     larger tensors: one workgroup completes the tree (the mean),
 //   k_dq_codes      then one workgroup per DQ block: scale and int8 codes.
 //   k_dequant       one workgroup per DQ block: per-block scales in LDS, then
@@ -293,8 +293,8 @@ __global__ __launch_bounds__(kThreads) void k_absmax_codes(const uint8_t *__rest
 constexpr int kTreeChunk = 8192;
 constexpr int kTreeRun = kTreeChunk / kThreads;   // 32
 constexpr int kTreeMaxChunks = kThreads * kTreeRun;
-constexpr int64_t kDqCodeGroups = 256;       // workgroups of k_dq_codes_mean (each recomputes the mean)
 constexpr int64_t kDqFusedMaxBlocks = 1024;  // larger tensors take k_tree_mean + k_dq_codes
+static_assert(kDqFusedMaxBlocks <= kTreeChunk, "the fused mean is a single-chunk tree");
 
 // Sum of the perfect binary tree over top leaves (top a power of two <= kTreeChunk)
 // src[base + i], zero past limit. Every thread gets the result.
@@ -323,9 +323,8 @@ __device__ double tree_sum(const double *src, int64_t base, int64_t limit, int t
   return (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
 }
 
-// The DQ mean: every workgroup completes the same fp64 tree over the
-// per-DQ-block partials (so all of them hold the same bits) and workgroup 0
-// stores mean = fp32(sum / nb).
+// The DQ mean fp32(sum / nb) from the per-DQ-block partials: the tree over
+// chunks of kTreeChunk partials, then over the chunk sums (csum in LDS).
 __device__ float tree_mean(const double *__restrict__ partial, int64_t nd, int64_t nb, double *wsum,
                            double *csum) {
   const int tid = threadIdx.x;
@@ -350,13 +349,12 @@ __device__ float tree_mean(const double *__restrict__ partial, int64_t nd, int64
 
 // DQ scale s2 = max |fp32(a - mean)| over DQ block d and its int8 codes, one
 // thread per absmax constant.
-__device__ __forceinline__ void dq_block(const float *__restrict__ absmax_ws, int64_t nb, int64_t d, float mu,
-                                         int8_t *__restrict__ absmax_q, float *__restrict__ dq_scale,
-                                         float *wmax) {
+// a = absmax_ws[d * 256 + thread] (0 past nb), loaded by the caller.
+__device__ __forceinline__ void dq_block(float a, int64_t nb, int64_t d, float mu, int8_t *__restrict__ absmax_q,
+                                         float *__restrict__ dq_scale, float *wmax) {
   const int tid = threadIdx.x;
   const int64_t b = d * kDqBlock + tid;
   const bool valid = b < nb;
-  const float a = valid ? absmax_ws[b] : 0.0f;
   const float dv = valid ? __fsub_rn(a, mu) : 0.0f;
   float m = fabsf(dv);
 #pragma unroll
@@ -375,20 +373,25 @@ __device__ __forceinline__ void dq_block(const float *__restrict__ absmax_ws, in
   if (tid == 0) dq_scale[d] = s2;
 }
 
-// Up to a few thousand DQ blocks: every workgroup completes the mean itself
-// (the partials come from L2) and takes DQ blocks d = blockIdx.x + i *
-// gridDim.x; workgroup 0 stores the mean. One launch instead of two.
+// Up to kDqFusedMaxBlocks DQ blocks, one per workgroup: every workgroup
+// completes the same single-chunk fp64 tree over the per-DQ-block partials
+// (the partials come from L2; the same tree as k_tree_mean) and workgroup 0
+// stores the mean. The block's absmax load goes out before the tree's.
 __global__ __launch_bounds__(kThreads) void k_dq_codes_mean(const float *__restrict__ absmax_ws,
                                                             const double *__restrict__ partial, int64_t nb,
                                                             int64_t nd, float *__restrict__ dq_mean,
                                                             int8_t *__restrict__ absmax_q,
                                                             float *__restrict__ dq_scale) {
   __shared__ double wsum[kThreads / 64];
-  __shared__ double csum[kTreeMaxChunks];
   __shared__ float wmax[kThreads / 64];
-  const float mu = tree_mean(partial, nd, nb, wsum, csum);
-  if (blockIdx.x == 0 && threadIdx.x == 0) dq_mean[0] = mu;
-  for (int64_t d = blockIdx.x; d < nd; d += gridDim.x) dq_block(absmax_ws, nb, d, mu, absmax_q, dq_scale, wmax);
+  const int64_t d = blockIdx.x;
+  const int64_t b = d * kDqBlock + threadIdx.x;
+  const float a = b < nb ? absmax_ws[b] : 0.0f;
+  int top = 1;
+  while (top < nd) top *= 2;
+  const float mu = static_cast<float>(tree_sum(partial, 0, nd, top, wsum) / static_cast<double>(nb));
+  if (d == 0 && threadIdx.x == 0) dq_mean[0] = mu;
+  dq_block(a, nb, d, mu, absmax_q, dq_scale, wmax);
 }
 
 // Larger tensors: one workgroup completes the mean ...
@@ -406,7 +409,9 @@ __global__ __launch_bounds__(kThreads) void k_dq_codes(const float *__restrict__
                                                        int8_t *__restrict__ absmax_q,
                                                        float *__restrict__ dq_scale) {
   __shared__ float wmax[kThreads / 64];
-  dq_block(absmax_ws, nb, blockIdx.x, dq_mean[0], absmax_q, dq_scale, wmax);
+  const int64_t b = static_cast<int64_t>(blockIdx.x) * kDqBlock + threadIdx.x;
+  const float a = b < nb ? absmax_ws[b] : 0.0f;
+  dq_block(a, nb, blockIdx.x, dq_mean[0], absmax_q, dq_scale, wmax);
 }
 
 // ------------------------------------------------------------ dequantize
@@ -527,8 +532,8 @@ hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, uint8_t *codes
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (nd <= kDqFusedMaxBlocks) {
-    hipLaunchKernelGGL(k_dq_codes_mean, dim3(std::min<int64_t>(nd, kDqCodeGroups)), dim3(kThreads), 0, s,
-                       absmax_ws, part, nb, nd, dq_mean, absmax_q, dq_scale);
+    hipLaunchKernelGGL(k_dq_codes_mean, dim3(nd), dim3(kThreads), 0, s, absmax_ws, part, nb, nd, dq_mean, absmax_q,
+                       dq_scale);
   } else {
     hipLaunchKernelGGL(k_tree_mean, dim3(1), dim3(kThreads), 0, s, part, nd, nb, dq_mean);
     hipLaunchKernelGGL(k_dq_codes, dim3(nd), dim3(kThreads), 0, s, absmax_ws, nb, dq_mean, absmax_q, dq_scale);
