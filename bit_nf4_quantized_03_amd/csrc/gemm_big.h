@@ -226,7 +226,7 @@ struct Nf4TransBigT {
     const int x = rg ^ (cc & 3);
     __bf16 *d0 = lds + (cc * 8 + 2 * q) * kLDK + ((x ^ (2 * q)) << 3) + hh * R;
     __bf16 *d1 = lds + (cc * 8 + 2 * q + 1) * kLDK + ((x ^ (2 * q + 1)) << 3) + hh * R;
-    if (R == 8) {
+    if constexpr (R == 8) {
       *reinterpret_cast<uint4 *>(d0) = make_uint4(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
                                                   pack_bf16x2(v0[4], v0[5]), pack_bf16x2(v0[6], v0[7]));
       *reinterpret_cast<uint4 *>(d1) = make_uint4(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]),
