@@ -121,13 +121,14 @@ def _counter_per_dispatch(folder: str, counter: str):
     return out
 
 
-def write_traffic(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str):
+def write_traffic(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str, path: str = None):
     """Calibrated HBM bytes per launch of the two dequant-GEMMs of the step
     (the Llama-7B attention shape, M = N = K = 4096, r = 64).
 
     FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch; each is scaled by
     the factor that makes the 1 GiB copy of --calib-copy read (write) exactly
-    1 GiB (the largest dispatch of the calibration run is the copy)."""
+    1 GiB (the largest dispatch of the calibration run is the copy). Writes
+    `path` (default profiles/traffic.json)."""
     gib = 1 << 30
     cal_f = max(v for vals in _counter_per_dispatch(cal_fetch_dir, "FETCH_SIZE").values() for v in vals)
     cal_w = max(v for vals in _counter_per_dispatch(cal_write_dir, "WRITE_SIZE").values() for v in vals)
@@ -159,7 +160,8 @@ def write_traffic(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_
             "algorithmic_write_bytes": out,
             "source_hash": kernel_source_hash(key),
         }
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if path is None:
+        path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
         json.dump(data, f, indent=1)
         f.write("\n")
