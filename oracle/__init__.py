@@ -11,8 +11,9 @@ arrays, fp64 for every matmul, and explicit fp32 operations (NumPy float32
 storage format fixes a float32 result bit for bit.
 
 Modules
-  nf4     codebook derivation, block-wise NF4 quantization, double quantization
-          of the absmax constants, dequantization, storage size.
+  nf4     codebook derivation (NF4, and the FP4 comparison levels), block-wise
+          quantization, double quantization of the absmax constants (or fp32
+          constants without it), dequantization, storage size.
   linear  QLoRA linear forward and backward in fp64.
 
 Sources (the pages the method is taken from):
@@ -22,7 +23,8 @@ Sources (the pages the method is taken from):
     parameter.
   * ai-papercheck review "QLoRA: Efficient Finetuning of Quantized LLMs",
     finding on paper p.5 Section 3: the k-bit type has an exact zero point and
-    uses all 2^k values.
+    uses all 2^k values; findings on paper p.8 Table 4: the NFloat4,
+    NFloat4 + DQ and Float4 rows (the comparison formats: no DQ, FP4 levels).
   * unfragile.ai "QLoRA vs ChatGPT", capability rows on 4-bit NF4 quantization
     (block-wise absmax scaling, LoRA in full precision), double quantization
     (8-bit constants with their own scales), LoRA on the frozen base (rank 8-64)

@@ -38,10 +38,24 @@ What the pages fix, and the reading taken where they are silent:
       c'_b = fp32(fp32(q_b * k_d) + mean)
       w    = fp32(codebook[code] * c'_b)
   and a bf16 output is the round-to-nearest-even of that fp32 value.
+* Comparison formats. The paper's Table 4 (QLoRA review, findings on paper
+  p.8 Table 4: rows NFloat4, NFloat4 + DQ and Float4, and the caption that has
+  FP4 about one point behind) compares NF4 with and without double
+  quantization and a 4-bit float. Without DQ the fp32 absmax constants are
+  stored as they are and w = fp32(codebook[code] * absmax_b). The pages do not
+  define the 4-bit float. Reading: the float with one sign bit, two exponent
+  bits (bias 1, subnormals at exponent 0, no infinities) and one mantissa bit,
+  whose 15 distinct values are +-{0, 1/2, 1, 3/2, 2, 3, 4, 6}; they are divided
+  by 6 so that a block's absmax maps to the largest magnitude, as NF4's levels
+  span [-1, 1]. The table lists the values in ascending order with the zero at
+  index 7, as NF4 does, and repeats +1 at index 15, so the nearest-level rule
+  (ties to the lower index) never yields code 15. Quantization, packing and
+  dequantization are otherwise those of NF4.
 """
 from __future__ import annotations
 
 import dataclasses
+from fractions import Fraction
 
 import mpmath
 import numpy as np
@@ -113,6 +127,34 @@ def round_to_f32(v) -> np.float32:
 def nf4_codebook() -> np.ndarray:
     """The 16 NF4 levels as fp32, ascending; index = 4-bit code."""
     return np.array([round_to_f32(v) for v in nf4_levels_mp()], dtype=np.float32)
+
+
+def e2m1_values():
+    """Every value of the 4-bit float (1 sign, 2 exponent bits with bias 1,
+    1 mantissa bit; exponent field 0 is subnormal), as exact fractions,
+    ascending and without the duplicate zero: 15 values."""
+    vals = set()
+    for sign in (1, -1):
+        for e in range(4):
+            for m in range(2):
+                if e == 0:
+                    mag = Fraction(m, 2)                       # 2^(1 - bias) * (m / 2)
+                else:
+                    mag = Fraction(2) ** (e - 1) * (1 + Fraction(m, 2))
+                vals.add(sign * mag)
+    return sorted(vals)
+
+
+def fp4_codebook() -> np.ndarray:
+    """The 16 FP4 levels as fp32: the 15 values of ``e2m1_values`` divided by
+    the largest one (each rounded once to fp32), ascending, with +1 repeated
+    at index 15 (a code the nearest-level rule never chooses)."""
+    vals = e2m1_values()
+    top = vals[-1]
+    levels = [v / top for v in vals] + [Fraction(1)]
+    with mpmath.workdps(50):
+        return np.array([round_to_f32(mpmath.mpf(v.numerator) / v.denominator) for v in levels],
+                        dtype=np.float32)
 
 
 # ---------------------------------------------------------------------------
@@ -247,24 +289,30 @@ def dq_reconstruct(q: np.ndarray, scale: np.ndarray, mu) -> np.ndarray:
 
 @dataclasses.dataclass
 class NF4Tensor:
-    """NF4 + double-quantized weight of ``shape`` (row-major)."""
+    """4-bit weight of ``shape`` (row-major). With ``dq`` the absmax constants
+    are stored double-quantized (absmax_q, dq_scale, dq_mean) and ``absmax``
+    holds the first-level constants for tests only; without it absmax_q,
+    dq_scale and dq_mean are None and ``absmax`` is the stored fp32 constant."""
     shape: tuple
     codes: np.ndarray      # uint8 [ceil(n/2)]
-    absmax_q: np.ndarray   # int8  [nb]
-    dq_scale: np.ndarray   # f32   [nd]
-    dq_mean: np.float32    # f32 scalar
-    absmax: np.ndarray     # f32 [nb], first-level constants (not stored; for tests)
+    absmax_q: np.ndarray   # int8  [nb], or None without DQ
+    dq_scale: np.ndarray   # f32   [nd], or None without DQ
+    dq_mean: np.float32    # f32 scalar, or None without DQ
+    absmax: np.ndarray     # f32 [nb], first-level constants
+    dq: bool = True
 
     @property
     def n(self) -> int:
         return int(np.prod(self.shape))
 
 
-def quantize(w: np.ndarray, codebook: np.ndarray = None) -> NF4Tensor:
-    """Quantize an fp32-valued weight (bf16 inputs widened exactly) to NF4 + DQ.
+def quantize(w: np.ndarray, codebook: np.ndarray = None, double_quant: bool = True) -> NF4Tensor:
+    """Quantize an fp32-valued weight (bf16 inputs widened exactly) to 4-bit
+    codes of ``codebook`` (NF4 by default), with or without DQ.
 
     The two levels are sequential: codes are chosen with the true fp32 absmax,
-    then the absmax constants are double-quantized.
+    then (with DQ) the absmax constants are double-quantized; so the codes do
+    not depend on ``double_quant``.
     """
     if codebook is None:
         codebook = nf4_codebook()
@@ -272,17 +320,20 @@ def quantize(w: np.ndarray, codebook: np.ndarray = None) -> NF4Tensor:
     if not np.all(np.isfinite(w)):
         raise ValueError("oracle quantize: inputs must be finite")
     codes, a = nf4_codes(w, codebook)
+    if not double_quant:
+        return NF4Tensor(tuple(w.shape), pack_codes(codes), None, None, None, a, dq=False)
     q, scale, mu = double_quantize(a)
     return NF4Tensor(tuple(w.shape), pack_codes(codes), q, scale, mu, a)
 
 
 def dequantize(t: NF4Tensor, codebook: np.ndarray = None) -> np.ndarray:
-    """fp32 reconstruction w = fp32(codebook[code] * c'_block), in ``t.shape``."""
+    """fp32 reconstruction w = fp32(codebook[code] * c'_block), in ``t.shape``;
+    c' is the double-quantized constant, or the stored fp32 absmax without DQ."""
     if codebook is None:
         codebook = nf4_codebook()
     n = t.n
     codes = unpack_codes(t.codes, n)
-    cprime = dq_reconstruct(t.absmax_q, t.dq_scale, t.dq_mean)
+    cprime = dq_reconstruct(t.absmax_q, t.dq_scale, t.dq_mean) if t.dq else np.asarray(t.absmax, np.float32)
     c_el = np.repeat(cprime, NF4_BLOCK)[:n]
     w = (codebook[codes] * c_el).astype(np.float32)
     return w.reshape(t.shape)
@@ -295,20 +346,23 @@ def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
-def storage_bytes(n: int) -> int:
+def storage_bytes(n: int, double_quant: bool = True) -> int:
     """Bytes of the stored format: codes n/2 (rounded up) + int8 per block +
-    fp32 scale per DQ block + one fp32 mean."""
+    fp32 scale per DQ block + one fp32 mean; without DQ, codes + fp32 per block."""
     nb = -(-n // NF4_BLOCK)
+    if not double_quant:
+        return -(-n // 2) + 4 * nb
     nd = -(-nb // DQ_BLOCK)
     return -(-n // 2) + nb + 4 * nd + 4
 
 
-def bits_per_param(n: int) -> float:
-    return 8.0 * storage_bytes(n) / n
+def bits_per_param(n: int, double_quant: bool = True) -> float:
+    return 8.0 * storage_bytes(n, double_quant) / n
 
 
 __all__ = [
     "NF4_BLOCK", "DQ_BLOCK", "ZERO_CODE", "nf4_codebook", "nf4_levels_mp", "round_to_f32",
+    "e2m1_values", "fp4_codebook",
     "nearest_code", "block_absmax", "nf4_codes", "pack_codes", "unpack_codes",
     "tree_sum_f64", "dq_mean", "double_quantize", "dq_reconstruct", "NF4Tensor",
     "quantize", "dequantize", "f32_to_bf16_rne", "storage_bytes", "bits_per_param",
