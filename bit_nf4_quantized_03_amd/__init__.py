@@ -20,6 +20,8 @@ __all__ = [
     "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_workspace_bytes",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_last_error", "EXPORTED_SYMBOLS",
     "qlora_profile_enable", "qlora_profile_read", "qlora_profile_reset",
+    "qlora_weight_storage_bytes", "qlora_format_levels", "format_has_dq",
+    "QLORA_FMT_NF4_DQ", "QLORA_FMT_NF4", "QLORA_FMT_FP4_DQ", "QLORA_FMT_FP4",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora_nf4.so")
@@ -32,6 +34,7 @@ EXPORTED_SYMBOLS = (
     "qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_workspace_bytes",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_last_error",
     "qlora_profile_enable", "qlora_profile_read", "qlora_profile_reset",
+    "qlora_weight_storage_bytes", "qlora_format_levels",
 )
 
 
@@ -46,6 +49,7 @@ class _Weight(ctypes.Structure):
         ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
         ("codes", ctypes.c_void_p), ("absmax_q", ctypes.c_void_p),
         ("dq_scale", ctypes.c_void_p), ("dq_mean", ctypes.c_void_p),
+        ("absmax", ctypes.c_void_p), ("format", ctypes.c_int32),
     ]
 
 
@@ -64,6 +68,8 @@ def _load():
     sigs = {
         "qlora_nf4_storage_bytes": (sz, [i64, i64]),
         "qlora_nf4_codebook": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
+        "qlora_weight_storage_bytes": (sz, [i64, i64, ctypes.c_int]),
+        "qlora_format_levels": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_float)]),
         "qlora_nf4_quantize_workspace_bytes": (sz, [i64, i64]),
         "qlora_nf4_quantize": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, wp, vp, sz, vp]),
         "qlora_nf4_dequantize": (ctypes.c_int, [wp, vp, ctypes.c_int, vp]),
@@ -103,6 +109,28 @@ def qlora_nf4_codebook():
     """The library's 16 NF4 levels as a list of Python floats (fp32 values)."""
     buf = (ctypes.c_float * 16)()
     _check("qlora_nf4_codebook", lib.qlora_nf4_codebook(buf))
+    return [buf[i] for i in range(16)]
+
+
+# weight formats (qlora_format): bit 0 = no double quantization, bit 1 = FP4 levels
+QLORA_FMT_NF4_DQ = 0
+QLORA_FMT_NF4 = 1
+QLORA_FMT_FP4_DQ = 2
+QLORA_FMT_FP4 = 3
+
+
+def format_has_dq(fmt: int) -> bool:
+    return (fmt & 1) == 0
+
+
+def qlora_weight_storage_bytes(rows: int, cols: int, fmt: int) -> int:
+    return int(lib.qlora_weight_storage_bytes(rows, cols, fmt))
+
+
+def qlora_format_levels(fmt: int):
+    """The 16 levels of weight format ``fmt`` as a list of Python floats (fp32 values)."""
+    buf = (ctypes.c_float * 16)()
+    _check("qlora_format_levels", lib.qlora_format_levels(fmt, buf))
     return [buf[i] for i in range(16)]
 
 
@@ -164,37 +192,45 @@ def _need_cuda(name, t, dtype=None):
 
 @dataclasses.dataclass
 class NF4Weight:
-    """NF4 + double-quantized weight [rows, cols] held in device tensors."""
+    """4-bit weight [rows, cols] held in device tensors, in format ``fmt``
+    (NF4 + DQ by default). With DQ: absmax_q, dq_scale, dq_mean; without:
+    the fp32 block constants ``absmax`` (the other three are None)."""
     rows: int
     cols: int
     codes: "object"      # uint8 [ceil(n/2)]
-    absmax_q: "object"   # int8 [nb]
-    dq_scale: "object"   # float32 [nd]
-    dq_mean: "object"    # float32 [1]
+    absmax_q: "object"   # int8 [nb], or None
+    dq_scale: "object"   # float32 [nd], or None
+    dq_mean: "object"    # float32 [1], or None
+    absmax: "object" = None   # float32 [nb] without DQ
+    fmt: int = QLORA_FMT_NF4_DQ
 
     @staticmethod
-    def empty(rows: int, cols: int, device) -> "NF4Weight":
+    def empty(rows: int, cols: int, device, fmt: int = QLORA_FMT_NF4_DQ) -> "NF4Weight":
         torch = _torch()
         n = rows * cols
         nb = -(-n // 64)
         nd = -(-nb // 256)
-        return NF4Weight(rows, cols,
-                         torch.empty((n + 1) // 2, dtype=torch.uint8, device=device),
+        codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=device)
+        if not format_has_dq(fmt):
+            return NF4Weight(rows, cols, codes, None, None, None,
+                             torch.empty(nb, dtype=torch.float32, device=device), fmt)
+        return NF4Weight(rows, cols, codes,
                          torch.empty(nb, dtype=torch.int8, device=device),
                          torch.empty(nd, dtype=torch.float32, device=device),
-                         torch.empty(1, dtype=torch.float32, device=device))
+                         torch.empty(1, dtype=torch.float32, device=device), None, fmt)
 
     def c_struct(self) -> _Weight:
         return _Weight(self.rows, self.cols, _ptr(self.codes), _ptr(self.absmax_q),
-                       _ptr(self.dq_scale), _ptr(self.dq_mean))
+                       _ptr(self.dq_scale), _ptr(self.dq_mean), _ptr(self.absmax), self.fmt)
 
     @property
     def device(self):
         return self.codes.device
 
 
-def qlora_nf4_quantize(W, out: Optional[NF4Weight] = None, ws=None) -> NF4Weight:
-    """Quantize a 2-D fp32 or bf16 CUDA tensor to NF4 + DQ."""
+def qlora_nf4_quantize(W, out: Optional[NF4Weight] = None, ws=None, fmt: Optional[int] = None) -> NF4Weight:
+    """Quantize a 2-D fp32 or bf16 CUDA tensor to 4-bit codes in format ``fmt``
+    (``out.fmt`` when ``out`` is given, else NF4 + DQ)."""
     torch = _torch()
     _need_cuda("W", W)
     if W.dim() != 2:
@@ -207,14 +243,17 @@ def qlora_nf4_quantize(W, out: Optional[NF4Weight] = None, ws=None) -> NF4Weight
         raise TypeError(f"W must be float32 or bfloat16, got {W.dtype}")
     rows, cols = W.shape
     if out is None:
-        out = NF4Weight.empty(rows, cols, W.device)
-    need = qlora_nf4_quantize_workspace_bytes(rows, cols)
-    if ws is None:
+        out = NF4Weight.empty(rows, cols, W.device, QLORA_FMT_NF4_DQ if fmt is None else fmt)
+    elif fmt is not None and fmt != out.fmt:
+        raise ValueError(f"fmt {fmt} differs from out.fmt {out.fmt}")
+    if ws is None and format_has_dq(out.fmt):
+        need = qlora_nf4_quantize_workspace_bytes(rows, cols)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=W.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = out.c_struct()
     _check("qlora_nf4_quantize",
            lib.qlora_nf4_quantize(_ptr(W), dt, rows, cols, ctypes.byref(st), _ptr(ws),
-                                  ws.numel() * ws.element_size(), _stream_ptr(W.device)))
+                                  ws_bytes, _stream_ptr(W.device)))
     return out
 
 

@@ -37,16 +37,26 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
+bool valid_format(int format) { return format >= 0 && format < qnf4::kFormats; }
+
 int check_weight(const qlora_nf4_weight *w, const char *fn) {
   if (!w) return fail(QLORA_ERR_NULL, "%s: weight struct is NULL", fn);
   if (w->rows <= 0 || w->cols <= 0 || w->rows > kMaxElems / w->cols)
     return fail(QLORA_ERR_SHAPE, "%s: invalid weight shape %lld x %lld", fn,
                 static_cast<long long>(w->rows), static_cast<long long>(w->cols));
-  if (!w->codes || !w->absmax_q || !w->dq_scale || !w->dq_mean)
-    return fail(QLORA_ERR_NULL, "%s: a weight buffer is NULL", fn);
-  if (!aligned16(w->codes) || !aligned16(w->absmax_q) || !aligned16(w->dq_scale) ||
-      !aligned16(w->dq_mean))
-    return fail(QLORA_ERR_ALIGN, "%s: weight buffers must be 16-byte aligned", fn);
+  if (!valid_format(w->format))
+    return fail(QLORA_ERR_FORMAT, "%s: format %d is not a qlora_format", fn, static_cast<int>(w->format));
+  if (qnf4::fmt_dq(w->format)) {
+    if (!w->codes || !w->absmax_q || !w->dq_scale || !w->dq_mean)
+      return fail(QLORA_ERR_NULL, "%s: a weight buffer is NULL", fn);
+    if (!aligned16(w->codes) || !aligned16(w->absmax_q) || !aligned16(w->dq_scale) ||
+        !aligned16(w->dq_mean))
+      return fail(QLORA_ERR_ALIGN, "%s: weight buffers must be 16-byte aligned", fn);
+  } else {
+    if (!w->codes || !w->absmax) return fail(QLORA_ERR_NULL, "%s: a weight buffer is NULL", fn);
+    if (!aligned16(w->codes) || !aligned16(w->absmax))
+      return fail(QLORA_ERR_ALIGN, "%s: weight buffers must be 16-byte aligned", fn);
+  }
   return QLORA_OK;
 }
 
@@ -75,10 +85,12 @@ qnf4::LinearArgs make_args(int64_t M, const qlora_nf4_weight *W, int32_t r, floa
   a.K = W->cols;
   a.r = r;
   a.scale = scale;
+  a.format = W->format;
   a.codes = W->codes;
   a.absmax_q = W->absmax_q;
   a.dq_scale = W->dq_scale;
   a.dq_mean = W->dq_mean;
+  a.absmax = W->absmax;
   return a;
 }
 
@@ -101,6 +113,23 @@ int qlora_nf4_codebook(float *out) {
   return ok();
 }
 
+size_t qlora_weight_storage_bytes(int64_t rows, int64_t cols, int format) {
+  if (!valid_format(format)) return 0;
+  if (qnf4::fmt_dq(format)) return qlora_nf4_storage_bytes(rows, cols);
+  if (rows <= 0 || cols <= 0 || rows > kMaxElems / cols) return 0;
+  const int64_t n = rows * cols;
+  return static_cast<size_t>((n + 1) / 2 + 4 * qnf4::ceil_div(n, QLORA_NF4_BLOCK));
+}
+
+int qlora_format_levels(int format, float *out) {
+  if (!out) return fail(QLORA_ERR_NULL, "qlora_format_levels: out is NULL");
+  if (!valid_format(format))
+    return fail(QLORA_ERR_FORMAT, "qlora_format_levels: format %d is not a qlora_format", format);
+  const qnf4::Nf4Tables &t = qnf4::format_tables(format);
+  std::memcpy(out, t.lv, sizeof(t.lv));
+  return ok();
+}
+
 size_t qlora_nf4_quantize_workspace_bytes(int64_t rows, int64_t cols) {
   if (rows <= 0 || cols <= 0 || rows > kMaxElems / cols) return 0;
   return qnf4::quantize_ws_bytes(rows * cols);
@@ -119,14 +148,17 @@ int qlora_nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols,
                 static_cast<long long>(out->rows), static_cast<long long>(out->cols),
                 static_cast<long long>(rows), static_cast<long long>(cols));
   if (!aligned16(W)) return fail(QLORA_ERR_ALIGN, "%s: W must be 16-byte aligned", fn);
-  const size_t need = qnf4::quantize_ws_bytes(rows * cols);
-  if (!ws || ws_bytes < need)
-    return fail(QLORA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need,
-                ws ? ws_bytes : size_t(0));
-  if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
-  hipError_t e = qnf4::launch_quantize(W, w_dtype == QLORA_BF16, rows * cols, out->codes,
-                                       out->absmax_q, out->dq_scale, out->dq_mean, ws,
-                                       static_cast<hipStream_t>(stream));
+  const bool dq = qnf4::fmt_dq(out->format);
+  if (dq) {   // without DQ no workspace is used
+    const size_t need = qnf4::quantize_ws_bytes(rows * cols);
+    if (!ws || ws_bytes < need)
+      return fail(QLORA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need,
+                  ws ? ws_bytes : size_t(0));
+    if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  }
+  hipError_t e = qnf4::launch_quantize(W, w_dtype == QLORA_BF16, rows * cols, out->format, out->codes,
+                                       out->absmax_q, out->dq_scale, out->dq_mean, out->absmax,
+                                       dq ? ws : nullptr, static_cast<hipStream_t>(stream));
   return hip_status(e, fn);
 }
 
@@ -138,8 +170,8 @@ int qlora_nf4_dequantize(const qlora_nf4_weight *q, void *out, int out_dtype, vo
   if (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16)
     return fail(QLORA_ERR_DTYPE, "%s: out_dtype %d is not QLORA_F32 or QLORA_BF16", fn, out_dtype);
   if (!aligned16(out)) return fail(QLORA_ERR_ALIGN, "%s: out must be 16-byte aligned", fn);
-  hipError_t e = qnf4::launch_dequantize(q->codes, q->absmax_q, q->dq_scale, q->dq_mean,
-                                         q->rows * q->cols, out, out_dtype == QLORA_BF16,
+  hipError_t e = qnf4::launch_dequantize(q->codes, q->format, q->absmax_q, q->dq_scale, q->dq_mean,
+                                         q->absmax, q->rows * q->cols, out, out_dtype == QLORA_BF16,
                                          static_cast<hipStream_t>(stream));
   return hip_status(e, fn);
 }

@@ -41,6 +41,33 @@ float round_down_f32(double v) {
   return f;
 }
 
+void set_thresholds(Nf4Tables &t) {
+  for (int i = 0; i < 15; ++i) {
+    // the sum of two fp32 values of magnitude <= 1 is exact in double
+    double mid = (static_cast<double>(t.lv[i]) + static_cast<double>(t.lv[i + 1])) * 0.5;
+    t.thr[i] = round_down_f32(mid);
+  }
+}
+
+// The 4-bit float with one sign bit, two exponent bits (bias 1, exponent
+// field 0 subnormal) and one mantissa bit, divided by its largest magnitude
+// (6) so that a block's absmax maps to +-1; the FP4 comparison format of the
+// paper's Table 4 (QLoRA review, findings on paper p.8 Table 4), whose levels
+// the pages leave open. The zero appears once (index 7) and +1 is repeated at
+// index 15.
+Nf4Tables derive_fp4() {
+  long double mag[8];
+  for (int e = 0; e < 4; ++e)
+    for (int m = 0; m < 2; ++m)
+      mag[2 * e + m] = e == 0 ? 0.5L * m : ldexpl(1.0L + 0.5L * m, e - 1);
+  Nf4Tables t;
+  for (int i = 0; i < 7; ++i) t.lv[i] = static_cast<float>(-mag[7 - i] / mag[7]);
+  for (int i = 0; i < 8; ++i) t.lv[7 + i] = static_cast<float>(mag[i] / mag[7]);
+  t.lv[15] = 1.0f;
+  set_thresholds(t);
+  return t;
+}
+
 Nf4Tables derive() {
   const long double p_max = 1.0L - (1.0L / 32.0L + 1.0L / 30.0L) / 2.0L;
   const long double z_max = normal_quantile(p_max);
@@ -58,11 +85,7 @@ Nf4Tables derive() {
   std::sort(v, v + 16);
   Nf4Tables t;
   for (int i = 0; i < 16; ++i) t.lv[i] = static_cast<float>(v[i]);
-  for (int i = 0; i < 15; ++i) {
-    // the sum of two fp32 values of magnitude <= 1 is exact in double
-    double mid = (static_cast<double>(t.lv[i]) + static_cast<double>(t.lv[i + 1])) * 0.5;
-    t.thr[i] = round_down_f32(mid);
-  }
+  set_thresholds(t);
   return t;
 }
 
@@ -72,6 +95,13 @@ const Nf4Tables &nf4_tables() {
   static Nf4Tables tables;
   static std::once_flag once;
   std::call_once(once, [] { tables = derive(); });
+  return tables;
+}
+
+const Nf4Tables &fp4_tables() {
+  static Nf4Tables tables;
+  static std::once_flag once;
+  std::call_once(once, [] { tables = derive_fp4(); });
   return tables;
 }
 

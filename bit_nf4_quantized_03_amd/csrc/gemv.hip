@@ -50,9 +50,10 @@ constexpr int kFinCols = 16 * kFinWaves;
 struct GemvParams {
   const __bf16 *X;        // [M][K]
   const uint8_t *codes;   // [N][K/2]
-  const int8_t *absmax_q; // [N*K/64]
+  const int8_t *absmax_q; // [N*K/64] (with DQ)
   const float *dq_scale;  // [nd]
   const float *dq_mean;   // [1]
+  const float *absmax;    // [N*K/64] fp32 block constants (without DQ)
   const float *A;         // [r][K] fp32, or null when r == 0
   const float *B;         // [N][r] fp32, or null when r == 0
   float *part;            // [splits][M][N] fp32
@@ -99,7 +100,8 @@ template <> struct CodeWords<4> {
 // across lanes once at the end. BD = 1, 2, 4 serve M <= 16, 8, 4: larger BD
 // reads 16 or 32 contiguous bytes per lane and fewer X fragments.
 // kAligned: K is a multiple of 256, so each lane's absmax bytes are whole dwords.
-template <int BD, bool kAligned>
+// kDq: block scales decoded from int8 codes + DQ; else the stored fp32 constants.
+template <int BD, bool kAligned, bool kDq>
 __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
   constexpr int NB = kGvMaxBlocks;
   constexpr int NS = NB / BD;                       // super-blocks per split
@@ -148,8 +150,14 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
   }
   QNF4_XLOAD(0, x0) QNF4_XLOAD(1, x1) QNF4_XLOAD(2, x2) QNF4_XLOAD(3, x3)
 #undef QNF4_XLOAD
-  uint32_t am[kAligned ? NB / 4 : NB];   // absmax bytes: packed dwords, or one per entry
-  if constexpr (kAligned) {
+  // absmax bytes (packed dwords, or one per entry) with DQ; without it the
+  // fp32 constant of this lane's block in each super-block
+  uint32_t am[kDq ? (kAligned ? NB / 4 : NB) : 1];
+  float af[kDq ? 1 : NS];
+  if constexpr (!kDq) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) af[s] = p.absmax[b0 + min(s * BD + bg, nblk - 1)];
+  } else if constexpr (kAligned) {
     const uint32_t *ap = reinterpret_cast<const uint32_t *>(p.absmax_q + b0);
 #pragma unroll
     for (int i = 0; i < NB / 4; ++i) am[i] = ap[min(i, nblk / 4 - 1)];
@@ -158,9 +166,9 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
     for (int j = 0; j < NB; ++j) am[j] = static_cast<uint8_t>(p.absmax_q[b0 + min(j, nblk - 1)]);
   }
   const int64_t d0 = b0 / kDqBlock;                // a split spans at most two DQ blocks
-  const float s0 = p.dq_scale[d0];
-  const float s1 = p.dq_scale[(b0 + nblk - 1) / kDqBlock];
-  const float mu = p.dq_mean[0];
+  const float s0 = kDq ? p.dq_scale[d0] : 0.0f;
+  const float s1 = kDq ? p.dq_scale[(b0 + nblk - 1) / kDqBlock] : 0.0f;
+  const float mu = kDq ? p.dq_mean[0] : 0.0f;
   // thread t holds A[jr, k0 + 2t .. +1] of rows jr0 and jr0 + gx (last: only
   // the H partials at the end use them)
   const int ka = min(2 * tid, kc - 2);
@@ -208,20 +216,24 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int j = s * BD + bg;
-    const float kd = (b0 + j) / kDqBlock == d0 ? kd0 : kd1;
-    int q;
-    if constexpr (kAligned) {
-      uint32_t word = am[0];
-#pragma unroll
-      for (int i = 1; i < NB / 4; ++i) word = (j >> 2) == i ? am[i] : word;
-      q = static_cast<int8_t>(word >> (8 * (j & 3)));
+    if constexpr (!kDq) {
+      cs[s] = j < nblk ? af[s] : 0.0f;
     } else {
-      uint32_t byte = am[0];
+      const float kd = (b0 + j) / kDqBlock == d0 ? kd0 : kd1;
+      int q;
+      if constexpr (kAligned) {
+        uint32_t word = am[0];
 #pragma unroll
-      for (int i = 1; i < NB; ++i) byte = j == i ? am[i] : byte;
-      q = static_cast<int8_t>(byte);
+        for (int i = 1; i < NB / 4; ++i) word = (j >> 2) == i ? am[i] : word;
+        q = static_cast<int8_t>(word >> (8 * (j & 3)));
+      } else {
+        uint32_t byte = am[0];
+#pragma unroll
+        for (int i = 1; i < NB; ++i) byte = j == i ? am[i] : byte;
+        q = static_cast<int8_t>(byte);
+      }
+      cs[s] = j < nblk ? __fadd_rn(__fmul_rn(static_cast<float>(q), kd), mu) : 0.0f;
     }
-    cs[s] = j < nblk ? __fadd_rn(__fmul_rn(static_cast<float>(q), kd), mu) : 0.0f;
   }
   // ---- decode + MFMA, one super-block at a time, P super-blocks of code
   // words in flight. The A operand of lane (row rho, group g) is X row
@@ -437,6 +449,17 @@ GemvSplit gemv_split(int64_t N, int64_t K) {
   return {static_cast<int>(ceil_div(K / kBlock, kGvMaxBlocks)), kGvMaxBlocks};
 }
 
+template <int BD>
+void launch_stream(bool aligned, bool dq, dim3 grid, hipStream_t s, const GemvParams &p) {
+  if (dq) {
+    if (aligned) hipLaunchKernelGGL((k_gemv<BD, true, true>), grid, dim3(kGvThreads), 0, s, p);
+    else hipLaunchKernelGGL((k_gemv<BD, false, true>), grid, dim3(kGvThreads), 0, s, p);
+  } else {
+    if (aligned) hipLaunchKernelGGL((k_gemv<BD, true, false>), grid, dim3(kGvThreads), 0, s, p);
+    else hipLaunchKernelGGL((k_gemv<BD, false, false>), grid, dim3(kGvThreads), 0, s, p);
+  }
+}
+
 size_t part_bytes(int64_t N, int64_t K) {
   return align_up(static_cast<size_t>(gemv_split(N, K).splits * kGvRows * N) * sizeof(float), 256);
 }
@@ -455,13 +478,14 @@ hipError_t launch_gemv(const LinearArgs &a, const void *X, const float *A, const
   p.absmax_q = a.absmax_q;
   p.dq_scale = a.dq_scale;
   p.dq_mean = a.dq_mean;
+  p.absmax = a.absmax;
   p.A = A;
   p.B = B;
   p.N = a.N;
   p.K = a.K;
   p.r = a.r;
   p.scale = a.scale;
-  p.tab = nf4_tables();
+  p.tab = format_tables(a.format);
   const GemvSplit sp = gemv_split(a.N, a.K);
   p.splits = sp.splits;
   p.split_blocks = sp.blocks;
@@ -469,22 +493,15 @@ hipError_t launch_gemv(const LinearArgs &a, const void *X, const float *A, const
   p.hpart = reinterpret_cast<float *>(static_cast<char *>(ws) + part_bytes(a.N, a.K));
   const dim3 grid(static_cast<unsigned>(ceil_div(a.N, kGvCols)), static_cast<unsigned>(p.splits));
   // passes of up to 16 rows, in order on the stream (they share the workspace)
-  const bool aligned = a.K % 256 == 0;
+  const bool aligned = a.K % 256 == 0, dq = fmt_dq(a.format);
   for (int64_t row0 = 0; row0 < a.M; row0 += kGvRows) {
     p.M = std::min<int64_t>(kGvRows, a.M - row0);
     p.X = static_cast<const __bf16 *>(X) + row0 * a.K;
     p.Y = static_cast<__bf16 *>(Y) + row0 * a.N;
     prof_begin(kProfFwdGemm, s);
-    if (p.M <= 4) {
-      if (aligned) hipLaunchKernelGGL((k_gemv<4, true>), grid, dim3(kGvThreads), 0, s, p);
-      else hipLaunchKernelGGL((k_gemv<4, false>), grid, dim3(kGvThreads), 0, s, p);
-    } else if (p.M <= 8) {
-      if (aligned) hipLaunchKernelGGL((k_gemv<2, true>), grid, dim3(kGvThreads), 0, s, p);
-      else hipLaunchKernelGGL((k_gemv<2, false>), grid, dim3(kGvThreads), 0, s, p);
-    } else {
-      if (aligned) hipLaunchKernelGGL((k_gemv<1, true>), grid, dim3(kGvThreads), 0, s, p);
-      else hipLaunchKernelGGL((k_gemv<1, false>), grid, dim3(kGvThreads), 0, s, p);
-    }
+    if (p.M <= 4) launch_stream<4>(aligned, dq, grid, s, p);
+    else if (p.M <= 8) launch_stream<2>(aligned, dq, grid, s, p);
+    else launch_stream<1>(aligned, dq, grid, s, p);
     prof_end(kProfFwdGemm, s);
     hipLaunchKernelGGL(k_gemv_finish, dim3(static_cast<unsigned>(ceil_div(a.N, kFinCols))), dim3(kFinThreads), 0,
                        s, p);

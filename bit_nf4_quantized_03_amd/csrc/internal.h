@@ -24,6 +24,20 @@ struct Nf4Tables {
 // fp32). Thread-safe.
 const Nf4Tables &nf4_tables();
 
+// The weight formats: bit 0 = the absmax constants are stored as fp32 (no
+// double quantization), bit 1 = FP4 levels instead of NF4.
+constexpr int kFmtNoDq = 1;
+constexpr int kFmtFp4 = 2;
+constexpr int kFormats = 4;
+inline bool fmt_dq(int format) { return (format & kFmtNoDq) == 0; }
+// The 4-bit float (1 sign, 2 exponent, 1 mantissa bit) divided by its largest
+// magnitude: 15 distinct levels ascending, zero at index 7 and +1 repeated at
+// index 15 (never chosen by the nearest-level rule); thresholds as for NF4.
+const Nf4Tables &fp4_tables();
+inline const Nf4Tables &format_tables(int format) {
+  return (format & kFmtFp4) ? fp4_tables() : nf4_tables();
+}
+
 // ------------------------------------------------------------- profiling
 enum ProfKind { kProfFwdGemm = 0, kProfBwdDx = 1, kProfQuantize = 2, kProfDequantize = 3, kProfKinds = 4 };
 bool prof_enabled();
@@ -38,25 +52,31 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- quantize
 // Workspace: fp32 absmax [nb] | one fp64 tree partial sum per DQ block [nd].
+// Without DQ (absmax != null) the fp32 constants go straight to `absmax` and
+// no workspace is used.
 size_t quantize_ws_bytes(int64_t n);
-hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, uint8_t *codes,
-                           int8_t *absmax_q, float *dq_scale, float *dq_mean,
+hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, int format, uint8_t *codes,
+                           int8_t *absmax_q, float *dq_scale, float *dq_mean, float *absmax,
                            void *ws, hipStream_t s);
 
 // -------------------------------------------------------------- dequantize
-hipError_t launch_dequantize(const uint8_t *codes, const int8_t *absmax_q,
-                             const float *dq_scale, const float *dq_mean, int64_t n,
-                             void *out, bool out_bf16, hipStream_t s);
+// With DQ the block scales come from absmax_q, dq_scale and dq_mean, without
+// it from the fp32 `absmax`.
+hipError_t launch_dequantize(const uint8_t *codes, int format, const int8_t *absmax_q,
+                             const float *dq_scale, const float *dq_mean, const float *absmax,
+                             int64_t n, void *out, bool out_bf16, hipStream_t s);
 
 // ------------------------------------------------------------------ linear
 struct LinearArgs {
   int64_t M, N, K;
   int r;
   float scale;
+  int format;
   const uint8_t *codes;
-  const int8_t *absmax_q;
+  const int8_t *absmax_q;   // with DQ
   const float *dq_scale;
   const float *dq_mean;
+  const float *absmax;      // without DQ: the fp32 block constants
 };
 
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int r);

@@ -616,6 +616,10 @@ Buffers carve(void *ws, const Plan &pl, int64_t M, int64_t N, int64_t K, size_t 
   return b;
 }
 
+// The fp32 block scales the big GEMMs read: decoded into the workspace with
+// DQ, the stored constants without it.
+const float *block_scales(const LinearArgs &a, const Buffers &b) { return fmt_dq(a.format) ? b.cs : a.absmax; }
+
 // The work before a big GEMM: the split partials of H = X A^T and (backward)
 // dY B, then one launch with their sums, the block scales and the bf16 adapter
 // operand of the GEMM (Bb forward, Atb backward).
@@ -669,9 +673,11 @@ hipError_t run_adapter_pre(const LinearArgs &a, const Plan &pl, const Buffers &b
   const int64_t sums = lora ? grid_blocks(a.M * pl.rp / 4, 256) : 0;
   fp.g_h = sums;
   fp.g_dh = backward ? sums : 0;
-  fp.g_cs = grid_blocks(ceil_div(fp.nb, kScaleBlocksPerThread), 256);
+  // without DQ the stored fp32 constants are the block scales themselves
+  fp.g_cs = fmt_dq(a.format) ? grid_blocks(ceil_div(fp.nb, kScaleBlocksPerThread), 256) : 0;
   fp.g_op = lora ? grid_blocks((backward ? a.K : a.N) * (pl.rp / 8), 256) : 0;
-  hipLaunchKernelGGL(k_adapter_finish, dim3(fp.g_h + fp.g_dh + fp.g_cs + fp.g_op), dim3(256), 0, s, fp);
+  const int64_t groups = fp.g_h + fp.g_dh + fp.g_cs + fp.g_op;
+  if (groups > 0) hipLaunchKernelGGL(k_adapter_finish, dim3(groups), dim3(256), 0, s, fp);
   return hipGetLastError();
 }
 
@@ -692,10 +698,10 @@ hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const 
   const Buffers b = carve(ws, pl, a.M, a.N, a.K, nullptr);
   hipError_t err = run_adapter_pre(a, pl, b, X, nullptr, A, B, false, s);
   if (err != hipSuccess) return err;
-  FwdParams fp{X, a.codes, b.cs, b.Hs, b.Bb, Y, a.M, a.N, a.K, pl.rp};
+  FwdParams fp{X, a.codes, block_scales(a, b), b.Hs, b.Bb, Y, a.M, a.N, a.K, pl.rp};
   dim3 g(grid_blocks(a.N, 256) * grid_blocks(a.M, 256), 1, 1);
   prof_begin(kProfFwdGemm, s);
-  hipLaunchKernelGGL(k_fwd_big<CfgBig8>, g, dim3(CfgBig8::kThreads), 0, s, fp, nf4_tables());
+  hipLaunchKernelGGL(k_fwd_big<CfgBig8>, g, dim3(CfgBig8::kThreads), 0, s, fp, format_tables(a.format));
   prof_end(kProfFwdGemm, s);
   return hipGetLastError();
 }
@@ -704,11 +710,11 @@ hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const 
                       const float *B, void *dX, float *dA, float *dB, void *ws, hipStream_t s) {
   const Plan pl = make_plan(a.M, a.N, a.K, a.r);
   const Buffers b = carve(ws, pl, a.M, a.N, a.K, nullptr);
-  const Nf4Tables &tab = nf4_tables();
+  const Nf4Tables &tab = format_tables(a.format);
   hipError_t err = run_adapter_pre(a, pl, b, X, dY, A, B, true, s);
   if (err != hipSuccess) return err;
   {
-    DxParams dp{dY, a.codes, b.cs, b.dHb, b.Atb, dX, a.M, a.N, a.K, pl.rp};
+    DxParams dp{dY, a.codes, block_scales(a, b), b.dHb, b.Atb, dX, a.M, a.N, a.K, pl.rp};
     dim3 g(grid_blocks(a.K, 256) * grid_blocks(a.M, 256), 1, 1);
     prof_begin(kProfBwdDx, s);
     hipLaunchKernelGGL(k_dx_big<CfgDx>, g, dim3(CfgDx::kThreads), 0, s, dp, tab);

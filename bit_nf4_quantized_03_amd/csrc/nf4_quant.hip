@@ -52,38 +52,55 @@ __device__ __forceinline__ int code_from_y(float y, const Nf4Tables &t) {
 // the cells of trunc(z) (cell t covers [t, t + 1) for t > 0, (t - 1, t] for
 // t < 0 and (-1, 1) for t = 0) gives the number of thresholds certainly below
 // any z of the cell and the one threshold tz (scaled by 128) that may lie
-// within the cell or 2^-13 of it (thresholds are more than 9 apart in z).
-// Entry: (tz or +inf, base count as int bits). The code is base + (z > tz);
-// when z is within 2^-14 of tz the element is recomputed with a correctly
-// rounded division instead. The table is built once on the host (every
-// quantity in it is exact in fp32) and passed by value.
+// within the cell or 2^-13 of it (the NF4 and FP4 thresholds are more than 10
+// apart in z; the host checks that no cell window holds two). Entry: (tz or
+// +inf, base count as int bits). The code is base + (z > tz); when z is within
+// 2^-14 of tz the element is recomputed with a correctly rounded division
+// instead. The table is built once per codebook on the host (every quantity
+// in it is exact in fp32) and passed by value.
 struct CodeLut {
   float2 cell[kCells];
 };
 
-const CodeLut &code_lut() {
-  static const CodeLut lut = [] {
-    CodeLut l{};
-    const Nf4Tables &t = nf4_tables();
-    for (int c = 0; c < kCells; ++c) {
-      const int iz = c - 128;
-      const float lo = static_cast<float>(iz > 0 ? iz : iz - 1);
-      const float hi = static_cast<float>(iz < 0 ? iz : iz + 1);
-      const float win = 0x1p-13f;
-      int base = 0;
-      float tc = __builtin_huge_valf();
-      for (int i = 0; i < 15; ++i) {
-        const float tz = t.thr[i] * 128.0f;  // exact (power-of-two scaling)
-        base += tz < lo - win ? 1 : 0;
-        tc = (tz >= lo - win && tz < hi + win) ? tz : tc;
+struct CodeLuts {
+  CodeLut lut[2];   // NF4, FP4
+  bool ok;          // at most one threshold in every cell window
+};
+
+CodeLut build_code_lut(const Nf4Tables &t, bool *ok) {
+  CodeLut l{};
+  for (int c = 0; c < kCells; ++c) {
+    const int iz = c - 128;
+    const float lo = static_cast<float>(iz > 0 ? iz : iz - 1);
+    const float hi = static_cast<float>(iz < 0 ? iz : iz + 1);
+    const float win = 0x1p-13f;
+    int base = 0, inside = 0;
+    float tc = __builtin_huge_valf();
+    for (int i = 0; i < 15; ++i) {
+      const float tz = t.thr[i] * 128.0f;  // exact (power-of-two scaling)
+      base += tz < lo - win ? 1 : 0;
+      if (tz >= lo - win && tz < hi + win) {
+        tc = tz;
+        ++inside;
       }
-      float base_bits;
-      std::memcpy(&base_bits, &base, sizeof(base_bits));
-      l.cell[c] = make_float2(tc, base_bits);
     }
+    if (inside > 1) *ok = false;
+    float base_bits;
+    std::memcpy(&base_bits, &base, sizeof(base_bits));
+    l.cell[c] = make_float2(tc, base_bits);
+  }
+  return l;
+}
+
+const CodeLut *code_lut(int format) {
+  static const CodeLuts luts = [] {
+    CodeLuts l{};
+    l.ok = true;
+    l.lut[0] = build_code_lut(nf4_tables(), &l.ok);
+    l.lut[1] = build_code_lut(fp4_tables(), &l.ok);
     return l;
   }();
-  return lut;
+  return luts.ok ? &luts.lut[(format & kFmtFp4) ? 1 : 0] : nullptr;
 }
 
 template <bool kBf16>
@@ -184,12 +201,13 @@ __device__ __forceinline__ float code_lane(const uint4 &raw, int64_t e, int64_t 
 
 // Workgroups loop over DQ blocks d = blockIdx.x + i * gridDim.x (256 absmax
 // blocks = 16384 elements each): absmax and codes of its 256 blocks, the fp32
-// absmax to the workspace and the fp64 tree sum of the 256 constants. The
-// next DQ block's loads are issued before the current one is coded.
-template <bool kBf16>
+// absmax to `absmax_out` (the workspace, or the stored constants without DQ)
+// and, with DQ, the fp64 tree sum of the 256 constants. The next DQ block's
+// loads are issued before the current one is coded.
+template <bool kBf16, bool kDq>
 __global__ __launch_bounds__(kThreads) void k_absmax_codes(const uint8_t *__restrict__ W, int64_t n,
                                                            uint8_t *__restrict__ codes,
-                                                           float *__restrict__ absmax_ws,
+                                                           float *__restrict__ absmax_out,
                                                            double *__restrict__ partial,
                                                            int64_t nb, int64_t nd, Nf4Tables tab,
                                                            CodeLut code_tab) {
@@ -264,20 +282,22 @@ __global__ __launch_bounds__(kThreads) void k_absmax_codes(const uint8_t *__rest
                         : code_lane<kBf16, true>(raw[p], e, n, codes, lut, tab);
       if ((tid % kLpb) == 0) {
         const int64_t blk = e / kBlock;
-        sa[blk - d * kDqBlock] = a;
-        if (blk < nb) absmax_ws[blk] = a;
+        if (kDq) sa[blk - d * kDqBlock] = a;
+        if (blk < nb) absmax_out[blk] = a;
       }
     }
-    __syncthreads();
-    // fp64 tree sum of the 256 constants: xor butterflies give the
-    // adjacent-pair tree inside each wave's 64 leaves, then (w0 + w1) + (w2 + w3).
-    const int64_t myblk = d * kDqBlock + tid;
-    double v = (myblk < nb) ? static_cast<double>(sa[tid]) : 0.0;
+    if constexpr (kDq) {
+      __syncthreads();
+      // fp64 tree sum of the 256 constants: xor butterflies give the
+      // adjacent-pair tree inside each wave's 64 leaves, then (w0 + w1) + (w2 + w3).
+      const int64_t myblk = d * kDqBlock + tid;
+      double v = (myblk < nb) ? static_cast<double>(sa[tid]) : 0.0;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off);
-    if ((tid & 63) == 0) wsum[tid >> 6] = v;
-    __syncthreads();
-    if (tid == 0) partial[d] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+      for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off);
+      if ((tid & 63) == 0) wsum[tid >> 6] = v;
+      __syncthreads();
+      if (tid == 0) partial[d] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    }
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) raw[p] = nxt[p];
   }
@@ -420,11 +440,14 @@ __device__ __forceinline__ float block_scale(int8_t q, float kd, float mu) {
   return __fadd_rn(__fmul_rn(static_cast<float>(q), kd), mu);
 }
 
-template <bool kOutBf16>
+// With kDq the block scales are decoded from the int8 codes, the DQ scales
+// and the mean; without it they are the stored fp32 constants `absmax`.
+template <bool kOutBf16, bool kDq>
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict__ codes,
                                                       const int8_t *__restrict__ absmax_q,
                                                       const float *__restrict__ dq_scale,
-                                                      const float *__restrict__ dq_mean, int64_t n,
+                                                      const float *__restrict__ dq_mean,
+                                                      const float *__restrict__ absmax, int64_t n,
                                                       void *__restrict__ out, Nf4Tables tab) {
   __shared__ float lv[16];
   __shared__ float cs[kDqBlock];
@@ -432,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict_
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const int64_t nbytes = (n + 1) / 2;
   if (tid < 16) lv[tid] = tab.lv[tid];
-  const float mu = dq_mean[0];
+  const float mu = kDq ? dq_mean[0] : 0.0f;
 
   for (int64_t d = blockIdx.x; d * kElemsPerDq < n; d += gridDim.x) {
     // The code loads go out first: they do not depend on the scales, so the
@@ -457,10 +480,16 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict_
       }
     }
     const int64_t b = d * kDqBlock + tid;
-    const float s2 = dq_scale[d];
-    const int8_t q = (b < nb) ? absmax_q[b] : static_cast<int8_t>(0);
+    float c;
+    if constexpr (kDq) {
+      const float s2 = dq_scale[d];
+      const int8_t q = (b < nb) ? absmax_q[b] : static_cast<int8_t>(0);
+      c = block_scale(q, __fdiv_rn(s2, 127.0f), mu);
+    } else {
+      c = (b < nb) ? absmax[b] : 0.0f;
+    }
     __syncthreads();  // previous iteration done with cs
-    cs[tid] = (b < nb) ? block_scale(q, __fdiv_rn(s2, 127.0f), mu) : 0.0f;
+    cs[tid] = (b < nb) ? c : 0.0f;
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
@@ -509,54 +538,59 @@ size_t quantize_ws_bytes(int64_t n) {
   return align_up(static_cast<size_t>(nb) * 4, 256) + static_cast<size_t>(ceil_div(nb, kDqBlock)) * 8;
 }
 
-hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, uint8_t *codes,
-                           int8_t *absmax_q, float *dq_scale, float *dq_mean, void *ws,
+hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, int format, uint8_t *codes,
+                           int8_t *absmax_q, float *dq_scale, float *dq_mean, float *absmax, void *ws,
                            hipStream_t s) {
   const int64_t nb = ceil_div(n, kBlock);
   const int64_t nd = ceil_div(nb, kDqBlock);
-  float *absmax_ws = static_cast<float *>(ws);
-  double *part = reinterpret_cast<double *>(static_cast<char *>(ws) +
-                                            align_up(static_cast<size_t>(nb) * 4, 256));
+  const bool dq = fmt_dq(format);
+  float *absmax_out = dq ? static_cast<float *>(ws) : absmax;
+  double *part = dq ? reinterpret_cast<double *>(static_cast<char *>(ws) + align_up(static_cast<size_t>(nb) * 4, 256))
+                    : nullptr;
   if (ceil_div(nd, kTreeChunk) > kTreeMaxChunks) return hipErrorInvalidValue;   // > 2^37 elements
-  const Nf4Tables &tab = nf4_tables();
-  const CodeLut &lut = code_lut();
+  const Nf4Tables &tab = format_tables(format);
+  const CodeLut *lut = code_lut(format);
+  if (!lut) return hipErrorInvalidValue;
   prof_begin(kProfQuantize, s);
   const int64_t grid = nd;   // one DQ block per workgroup
-  if (w_bf16)
-    hipLaunchKernelGGL(k_absmax_codes<true>, dim3(grid), dim3(kThreads), 0, s,
-                       static_cast<const uint8_t *>(W), n, codes, absmax_ws, part, nb, nd, tab, lut);
-  else
-    hipLaunchKernelGGL(k_absmax_codes<false>, dim3(grid), dim3(kThreads), 0, s,
-                       static_cast<const uint8_t *>(W), n, codes, absmax_ws, part, nb, nd, tab, lut);
+  const uint8_t *w8 = static_cast<const uint8_t *>(W);
+  if (w_bf16) {
+    if (dq) hipLaunchKernelGGL((k_absmax_codes<true, true>), dim3(grid), dim3(kThreads), 0, s, w8, n, codes, absmax_out, part, nb, nd, tab, *lut);
+    else hipLaunchKernelGGL((k_absmax_codes<true, false>), dim3(grid), dim3(kThreads), 0, s, w8, n, codes, absmax_out, part, nb, nd, tab, *lut);
+  } else {
+    if (dq) hipLaunchKernelGGL((k_absmax_codes<false, true>), dim3(grid), dim3(kThreads), 0, s, w8, n, codes, absmax_out, part, nb, nd, tab, *lut);
+    else hipLaunchKernelGGL((k_absmax_codes<false, false>), dim3(grid), dim3(kThreads), 0, s, w8, n, codes, absmax_out, part, nb, nd, tab, *lut);
+  }
   prof_end(kProfQuantize, s);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || !dq) return err;
   if (nd <= kDqFusedMaxBlocks) {
-    hipLaunchKernelGGL(k_dq_codes_mean, dim3(nd), dim3(kThreads), 0, s, absmax_ws, part, nb, nd, dq_mean, absmax_q,
+    hipLaunchKernelGGL(k_dq_codes_mean, dim3(nd), dim3(kThreads), 0, s, absmax_out, part, nb, nd, dq_mean, absmax_q,
                        dq_scale);
   } else {
     hipLaunchKernelGGL(k_tree_mean, dim3(1), dim3(kThreads), 0, s, part, nd, nb, dq_mean);
-    hipLaunchKernelGGL(k_dq_codes, dim3(nd), dim3(kThreads), 0, s, absmax_ws, nb, dq_mean, absmax_q, dq_scale);
+    hipLaunchKernelGGL(k_dq_codes, dim3(nd), dim3(kThreads), 0, s, absmax_out, nb, dq_mean, absmax_q, dq_scale);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize(const uint8_t *codes, const int8_t *absmax_q, const float *dq_scale,
-                             const float *dq_mean, int64_t n, void *out, bool out_bf16,
+hipError_t launch_dequantize(const uint8_t *codes, int format, const int8_t *absmax_q, const float *dq_scale,
+                             const float *dq_mean, const float *absmax, int64_t n, void *out, bool out_bf16,
                              hipStream_t s) {
   const int64_t nd = ceil_div(ceil_div(n, kBlock), kDqBlock);
   const int64_t grid = nd < 8192 ? nd : 8192;
-  const Nf4Tables &tab = nf4_tables();
+  const Nf4Tables &tab = format_tables(format);
+  const bool dq = fmt_dq(format);
   prof_begin(kProfDequantize, s);
-  if (out_bf16)
-    hipLaunchKernelGGL(k_dequant<true>, dim3(grid), dim3(kThreads), 0, s, codes, absmax_q,
-                       dq_scale, dq_mean, n, out, tab);
-  else
-    hipLaunchKernelGGL(k_dequant<false>, dim3(grid), dim3(kThreads), 0, s, codes, absmax_q,
-                       dq_scale, dq_mean, n, out, tab);
+  if (out_bf16) {
+    if (dq) hipLaunchKernelGGL((k_dequant<true, true>), dim3(grid), dim3(kThreads), 0, s, codes, absmax_q, dq_scale, dq_mean, absmax, n, out, tab);
+    else hipLaunchKernelGGL((k_dequant<true, false>), dim3(grid), dim3(kThreads), 0, s, codes, absmax_q, dq_scale, dq_mean, absmax, n, out, tab);
+  } else {
+    if (dq) hipLaunchKernelGGL((k_dequant<false, true>), dim3(grid), dim3(kThreads), 0, s, codes, absmax_q, dq_scale, dq_mean, absmax, n, out, tab);
+    else hipLaunchKernelGGL((k_dequant<false, false>), dim3(grid), dim3(kThreads), 0, s, codes, absmax_q, dq_scale, dq_mean, absmax, n, out, tab);
+  }
   prof_end(kProfDequantize, s);
   return hipGetLastError();
 }
-
 
 }  // namespace qnf4

@@ -57,14 +57,35 @@ typedef enum {
   QLORA_ERR_DTYPE = -3,      /* dtype outside qlora_dtype or not allowed here */
   QLORA_ERR_WORKSPACE = -4,  /* workspace NULL or smaller than required       */
   QLORA_ERR_HIP = -5,        /* a HIP call or kernel launch failed            */
-  QLORA_ERR_ALIGN = -6       /* a device pointer is not 16-byte aligned       */
+  QLORA_ERR_ALIGN = -6,      /* a device pointer is not 16-byte aligned       */
+  QLORA_ERR_FORMAT = -7      /* a weight format outside qlora_format          */
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
 
 /*
- * NF4 + double-quantized weight of `rows x cols` elements, n = rows*cols,
- * flattened row-major. nb = ceil(n/64) blocks, nd = ceil(nb/256) DQ blocks.
+ * Weight formats: the levels and whether the absmax constants are
+ * double-quantized. The default (0) is NF4 + DQ. The other three are the
+ * comparison rows of the paper's Table 4 (QLoRA review, findings on paper p.8
+ * Table 4: NFloat4, NFloat4 + DQ, Float4):
+ *   bit 0 set: no double quantization, the fp32 absmax constants are stored;
+ *   bit 1 set: FP4 levels, the 4-bit float with 1 sign, 2 exponent (bias 1,
+ *              subnormal at exponent 0) and 1 mantissa bit, divided by its
+ *              largest magnitude 6: 15 distinct levels ascending with 0 at
+ *              index 7, and +1 repeated at index 15 (never produced).
+ * Codes, blocks, packing and the nearest-level rule are the same for all.
+ */
+typedef enum {
+  QLORA_FMT_NF4_DQ = 0,
+  QLORA_FMT_NF4 = 1,
+  QLORA_FMT_FP4_DQ = 2,
+  QLORA_FMT_FP4 = 3
+} qlora_format;
+
+/*
+ * 4-bit weight of `rows x cols` elements, n = rows*cols, flattened row-major,
+ * in `format` (a qlora_format; 0 = NF4 + DQ, the layout described here).
+ * nb = ceil(n/64) blocks, nd = ceil(nb/256) DQ blocks.
  *   codes     ceil(n/2) bytes; element 2j is the high nibble of byte j,
  *             element 2j+1 the low nibble; an odd n leaves the last low
  *             nibble 0. A code is the index of an NF4 level (0..15, ascending;
@@ -72,9 +93,14 @@ typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
  *   absmax_q  nb int8 codes in [-127, 127] of the block absmax constants.
  *   dq_scale  nd fp32: per DQ block, the largest |absmax - mean|.
  *   dq_mean   1 fp32 (device): the mean of the nb absmax constants.
+ *   absmax    formats without DQ only: nb fp32 block absmax constants (then
+ *             absmax_q, dq_scale and dq_mean are unused and may be NULL; with
+ *             DQ, absmax is unused and may be NULL).
  * Reconstruction of element i in block b = i/64, DQ block d = b/256:
  *   k_d = fp32(dq_scale[d] / 127); c_b = fp32(fp32(absmax_q[b] * k_d) + mean);
+ *   (without DQ: c_b = absmax[b])
  *   w_i = fp32(level[code_i] * c_b), all round-to-nearest-even, no FMA.
+ * A zero-initialized struct with its buffers set is NF4 + DQ.
  */
 typedef struct {
   int64_t rows, cols;
@@ -82,6 +108,8 @@ typedef struct {
   int8_t *absmax_q;
   float *dq_scale;
   float *dq_mean;
+  float *absmax;
+  int32_t format;
 } qlora_nf4_weight;
 
 /* Bytes of the stored format: ceil(n/2) + nb + 4*nd + 4. Returns 0 if
@@ -95,14 +123,25 @@ size_t qlora_nf4_storage_bytes(int64_t rows, int64_t cols);
  * Returns QLORA_OK or QLORA_ERR_NULL. */
 int qlora_nf4_codebook(float *out);
 
+/* Bytes of the stored format `format`: as qlora_nf4_storage_bytes with DQ,
+ * ceil(n/2) + 4*nb without. Returns 0 for an invalid shape or format.
+ * Host-only. */
+size_t qlora_weight_storage_bytes(int64_t rows, int64_t cols, int format);
+
+/* The 16 levels of `format` (fp32, ascending by code) written to out[16]
+ * (NF4 as qlora_nf4_codebook, or the FP4 levels described at qlora_format).
+ * Host-only. Returns QLORA_OK, QLORA_ERR_NULL or QLORA_ERR_FORMAT. */
+int qlora_format_levels(int format, float *out);
+
 /* Workspace bytes needed by qlora_nf4_quantize for this shape (0 if the shape
- * is invalid). */
+ * is invalid). Formats without DQ use no workspace. */
 size_t qlora_nf4_quantize_workspace_bytes(int64_t rows, int64_t cols);
 
 /*
- * Quantize W [rows, cols] (fp32 or bf16, device) to NF4 + DQ into `out`,
- * whose rows/cols must equal the arguments and whose four buffers must be
- * allocated by the caller with the sizes given above.
+ * Quantize W [rows, cols] (fp32 or bf16, device) into `out` in out->format
+ * (NF4 + DQ by default), whose rows/cols must equal the arguments and whose
+ * buffers for that format must be allocated by the caller with the sizes
+ * given above.
  * Blocks of 64 consecutive flattened elements; absmax a_b = max|x|; each
  * element is coded as the level nearest to fp32(x / a_b) (ties to the lower
  * level; a zero block gets code 7 and a_b = 0). The constants a_b are then
@@ -111,8 +150,11 @@ size_t qlora_nf4_quantize_workspace_bytes(int64_t rows, int64_t cols);
  * fp32(sum/nb)); per 256-block scale s = max|fp32(a - mean)|; code
  * q = clamp(rint(fp32(fp32((a - mean)/s) * 127)), -127, 127), 0 if s = 0.
  * (QLoRA vs ChatGPT page, capabilities "NF4 4-bit quantization" and "double
- * quantization".) Results are bit-identical to that definition.
- * ws: device workspace of at least qlora_nf4_quantize_workspace_bytes().
+ * quantization".) Without DQ the fp32 a_b are stored as they are; with FP4
+ * levels "level" means the FP4 table. Results are bit-identical to that
+ * definition.
+ * ws: device workspace of at least qlora_nf4_quantize_workspace_bytes() with
+ * DQ; unused (may be NULL) without.
  */
 int qlora_nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols,
                        const qlora_nf4_weight *out, void *ws, size_t ws_bytes,
@@ -134,9 +176,10 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
  * QLoRA linear forward (QLoRA vs ChatGPT page, capabilities "LoRA on the
  * quantized base" and "training pipeline"):
  *     Y = X W^T + scale * (X A^T) B^T
- * with W the NF4 + DQ weight [N, K] dequantized block by block on the fly.
+ * with W the 4-bit weight [N, K] (any qlora_format) dequantized block by
+ * block on the fly.
  *   X      bf16 [M, K] (device)
- *   W      NF4 weight with rows = N, cols = K; N and K must be multiples
+ *   W      weight with rows = N, cols = K; N and K must be multiples
  *          of 64
  *   A      fp32 [r, K], B fp32 [N, r] (device); r = 0 with A = B = NULL
  *          means no adapter; 0 <= r <= 256

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(qb.EXPORTED_SYMBOLS) == names
@@ -42,6 +42,41 @@ def test_codebook_matches_oracle_bitwise():
                                        (11008, 4096), (22016, 8192), (7, 11)])
 def test_storage_bytes_match_format(rows, cols):
     assert qb.qlora_nf4_storage_bytes(rows, cols) == nf4.storage_bytes(rows * cols)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_format_levels_match_oracle_bitwise(fmt):
+    got = np.array(qb.qlora_format_levels(fmt), dtype=np.float32)
+    want = nf4.fp4_codebook() if fmt & 2 else nf4.nf4_codebook()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 65), (4096, 4096), (7, 11)])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_format_storage_bytes(rows, cols, fmt):
+    assert qb.qlora_weight_storage_bytes(rows, cols, fmt) == nf4.storage_bytes(rows * cols, double_quant=not fmt & 1)
+
+
+def test_formats_reject_bad_values():
+    buf = (ctypes.c_float * 16)()
+    assert lib.qlora_format_levels(4, buf) == -7
+    assert "not a qlora_format" in qb.qlora_last_error()
+    assert lib.qlora_format_levels(-1, buf) == -7
+    assert lib.qlora_format_levels(0, None) == -1
+    assert qb.qlora_weight_storage_bytes(64, 64, 4) == 0
+    assert qb.qlora_weight_storage_bytes(0, 64, 1) == 0
+    ref = ctypes.byref
+    w = qb._Weight(64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 9)
+    assert lib.qlora_nf4_quantize(FAKE, 0, 64, 64, ref(w), FAKE, 1 << 20, None) == -7
+    assert lib.qlora_nf4_dequantize(ref(w), FAKE, 0, None) == -7
+    # without DQ the fp32 constants are required (the DQ buffers are not)
+    w = qb._Weight(64, 64, FAKE, 0, 0, 0, 0, 1)
+    assert lib.qlora_nf4_quantize(FAKE, 0, 64, 64, ref(w), None, 0, None) == -1
+    w = qb._Weight(64, 64, FAKE, 0, 0, 0, FAKE + 4, 3)
+    assert lib.qlora_nf4_dequantize(ref(w), FAKE, 0, None) == -6
+    # with DQ the fp32 constants are not needed, the DQ buffers are
+    w = qb._Weight(64, 64, FAKE, FAKE, 0, FAKE, 0, 2)
+    assert lib.qlora_nf4_dequantize(ref(w), FAKE, 0, None) == -1
 
 
 def test_sizes_reject_bad_shapes():
