@@ -180,6 +180,8 @@ def main():
     ap.add_argument("--wm-layers", type=int, default=80,
                     help="layers of the 65B-shaped stack in the whole-model round trip")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--no-formats", action="store_true",
+                    help="skip the comparison formats (NF4 without DQ, FP4 with and without)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (the reference kernel for "
@@ -473,6 +475,54 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / reps
 
+    # ---------------- the weight formats at the step's shape (and decode M = 1)
+    # Per format: quantize (bf16 W in), dequantize (bf16 out), the fused
+    # forward and backward at M = 4096, and the decode GEMV at the 7B gate
+    # shape with rotating weights, as in the decode rows above.
+    formats = {}
+    if not args.no_formats:
+        wg = synth.workload("gate7b_m1")
+        Wg = d_bf16(wg.W)
+        Xg = d_bf16(wg.X)
+        Yg = torch.empty((wg.M, wg.N), dtype=torch.bfloat16, device=dev)
+        wsg = torch.empty(qb.qlora_linear_workspace_bytes(wg.M, wg.N, wg.K, r), dtype=torch.uint8, device=dev)
+        for fmt, fname in ((qb.QLORA_FMT_NF4_DQ, "nf4_dq"), (qb.QLORA_FMT_NF4, "nf4"),
+                           (qb.QLORA_FMT_FP4_DQ, "fp4_dq"), (qb.QLORA_FMT_FP4, "fp4")):
+            qf = qb.NF4Weight.empty(N, K, dev, fmt)
+            st = qb.qlora_weight_storage_bytes(N, K, fmt)
+            qz_ms = ev_time(lambda: qb.qlora_nf4_quantize(W, out=qf, ws=ws_q), 10)
+            dq_ms = ev_time(lambda: qb.qlora_nf4_dequantize(qf, torch.bfloat16, out=Wdq), 10)
+            f_ms = ev_time(lambda: qb.qlora_linear_fwd(X, qf, A, B, s, ws=ws_l, out=Y), 10)
+            b_ms = ev_time(lambda: qb.qlora_linear_bwd(dY, X, qf, A, B, s, ws=ws_l, outs=(dX, dA, dB)), 10)
+            stg = qb.qlora_weight_storage_bytes(wg.N, wg.K, fmt)
+            per_set = stg + 4 * r * (wg.K + wg.N)
+            Rd = max(2, ROTATE_BYTES // per_set + 1)
+            qg = [qb.qlora_nf4_quantize(Wg, fmt=fmt) for _ in range(Rd)]
+            Ag = [d_f32(wg.A) for _ in range(Rd)]
+            Bg = [d_f32(wg.B) for _ in range(Rd)]
+            qb.qlora_linear_fwd(Xg, qg[0], Ag[0], Bg[0], wg.s, ws=wsg, out=Yg)
+            torch.cuda.synchronize()
+            R_saved, R = R, Rd
+            g_ms, e_ms = timed(lambda i: qb.qlora_linear_fwd(Xg, qg[i], Ag[i], Bg[i], wg.s, ws=wsg, out=Yg), reps=5)
+            R = R_saved
+            d_ms = g_ms if g_ms is not None else e_ms
+            d_bytes = per_set + 2 * wg.M * wg.K + 2 * wg.M * wg.N
+            formats[fname] = {
+                "format": fmt, "storage_bytes": st, "bits_per_param": 8.0 * st / (N * K),
+                "quantize_us": qz_ms * 1e3, "quantize_gbs": (2 * N * K + st) / (qz_ms * 1e-3) / 1e9,
+                "dequant_bf16_us": dq_ms * 1e3, "dequant_gbs": (st + 2 * N * K) / (dq_ms * 1e-3) / 1e9,
+                "fwd_us": f_ms * 1e3, "fwd_tflops": fwd_flops / (f_ms * 1e-3) / 1e12,
+                "bwd_us": b_ms * 1e3, "bwd_tflops": bwd_flops / (b_ms * 1e-3) / 1e12,
+                "decode_gate7b_m1_us": d_ms * 1e3, "decode_gbs": d_bytes / (d_ms * 1e-3) / 1e9,
+            }
+            log(f"format {fname}: {8.0 * st / (N * K):.3f} bit/param; quantize {qz_ms * 1e3:.1f} us, "
+                f"dequantize {dq_ms * 1e3:.1f} us, fwd {f_ms * 1e3:.1f} us "
+                f"({formats[fname]['fwd_tflops']:.0f} TFLOP/s), bwd {b_ms * 1e3:.1f} us, "
+                f"decode gate7b M=1 {d_ms * 1e3:.2f} us ({formats[fname]['decode_gbs']:.0f} GB/s)")
+            del qf, qg, Ag, Bg
+            torch.cuda.empty_cache()
+        del Wg, Xg, Yg, wsg
+
     mlp = {}
     if not args.no_large:
         for name, (Nm, Km) in (("up65b", (22016, 8192)), ("down65b", (8192, 22016))):
@@ -616,6 +666,7 @@ def main():
         "rows": rows,
         "library_gemm_context": library,
         "decode": decode,
+        "formats": formats,
         "mlp65b": mlp,
         "dequant_solo": dq_solo,
         "whole_model_roundtrip": wm,

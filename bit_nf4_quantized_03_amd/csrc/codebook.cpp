@@ -65,6 +65,11 @@ Nf4Tables derive_fp4() {
   for (int i = 0; i < 8; ++i) t.lv[7 + i] = static_cast<float>(mag[i] / mag[7]);
   t.lv[15] = 1.0f;
   set_thresholds(t);
+  // The threshold between the two +1 entries would sit at exactly 1, where
+  // every block's absmax element lands; no scaled value exceeds 1, so any
+  // threshold above 1 gives the same codes and keeps the quantizer's fast
+  // path away from the exact-division fallback.
+  t.thr[14] = 2.0f;
   return t;
 }
 

@@ -163,17 +163,20 @@ __device__ __forceinline__ float code_lane(const uint4 &raw, int64_t e, int64_t 
   // and the exact path below recomputes every code of the lane.
   const float r128 = (a == 0.0f || !fast_scale) ? 0.0f : __fmul_rn(__builtin_amdgcn_rcpf(a), 128.0f);
   int c[kEpl];
-  bool near = !fast_scale;
+  bool near[kEpl];
 #pragma unroll
   for (int i = 0; i < kEpl; ++i) {
     const float z = __fmul_rn(x[i], r128);
     const float2 en = lut[static_cast<int>(z) + 128];   // truncation: |z| < 129
     c[i] = __float_as_int(en.y) + ((z > en.x) ? 1 : 0);
-    near |= fabsf(__fsub_rn(z, en.x)) <= 0x1p-14f;
+    near[i] = !fast_scale || fabsf(__fsub_rn(z, en.x)) <= 0x1p-14f;
   }
-  if (near) {  // rare: exact division for this lane's elements
+  // Rare: exact division, element by element, so that a wave pays only for
+  // the elements some lane needs (ratios of bf16 values hit a dyadic
+  // threshold such as FP4's 1/8 exactly now and then).
 #pragma unroll
-    for (int i = 0; i < kEpl; ++i) {
+  for (int i = 0; i < kEpl; ++i) {
+    if (near[i]) {
       const float y = (a == 0.0f) ? 0.0f : __fdiv_rn(x[i], a);
       c[i] = code_from_y(y, tab);
     }
