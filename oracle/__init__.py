@@ -15,6 +15,8 @@ Modules
           quantization, double quantization of the absmax constants (or fp32
           constants without it), dequantization, storage size.
   linear  QLoRA linear forward and backward in fp64.
+  merge   merging an adapter into the dequantized base (fp64 rank sum,
+          one rounding to fp32) and requantizing it.
 
 Sources (the pages the method is taken from):
   * Guanaco topic page (chipfoundryservices.com), "Technical Innovations":
@@ -29,9 +31,10 @@ Sources (the pages the method is taken from):
     (block-wise absmax scaling, LoRA in full precision), double quantization
     (8-bit constants with their own scales), LoRA on the frozen base (rank 8-64)
     and the training pipeline (block-wise on-the-fly dequantization, gradients
-    for the LoRA parameters only).
+    for the LoRA parameters only), and adapter composition (adapters merged
+    into the base weights for a standalone model).
 
 Every function whose result is pinned only by its own self-consistency says
 "parity unpinned" in its docstring; at present none does.
 """
-from . import nf4, linear  # noqa: F401
+from . import nf4, linear, merge  # noqa: F401
