@@ -47,6 +47,7 @@ if ROOT not in sys.path:
 METRIC = "QLoRA linear fwd+bwd TFLOP/s & NF4 dequant/GEMV GB/s vs roofline, 7B/65B"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+FP64_PEAK_TFLOPS = 78.6        # MI355X fp64 vector, vendor figure
 ROTATE_BYTES = 640 << 20       # > 2 x (256 MB last-level cache + L2)
 
 
@@ -523,6 +524,22 @@ def main():
             torch.cuda.empty_cache()
         del Wg, Xg, Yg, wsg
 
+    # -------------- adapter merge + requantize at the step's shape (r = 64)
+    merge_row = None
+    if not args.no_formats:
+        wsm = torch.empty(qb.qlora_nf4_merge_workspace_bytes(N, K, r), dtype=torch.uint8, device=dev)
+        qbase = qb.qlora_nf4_quantize(W)
+        qout = qb.NF4Weight.empty(N, K, dev)
+        m_ms = ev_time(lambda: qb.qlora_nf4_merge(qbase, A, B, s, out=qout, ws=wsm), 10)
+        m_flops = 2.0 * N * K * r
+        merge_row = {"N": N, "K": K, "r": r, "us": m_ms * 1e3,
+                     "rank_sum_fp64_tflops": m_flops / (m_ms * 1e-3) / 1e12,
+                     "frac_of_fp64_peak": m_flops / (m_ms * 1e-3) / 1e12 / FP64_PEAK_TFLOPS}
+        log(f"merge attn7b r={r}: {m_ms * 1e3:.1f} us per call (merge + requantize), rank sum "
+            f"{merge_row['rank_sum_fp64_tflops']:.1f} fp64 TFLOP/s over the whole call")
+        del wsm, qbase, qout
+        torch.cuda.empty_cache()
+
     mlp = {}
     if not args.no_large:
         for name, (Nm, Km) in (("up65b", (22016, 8192)), ("down65b", (8192, 22016))):
@@ -667,6 +684,7 @@ def main():
         "library_gemm_context": library,
         "decode": decode,
         "formats": formats,
+        "merge": merge_row,
         "mlp65b": mlp,
         "dequant_solo": dq_solo,
         "whole_model_roundtrip": wm,

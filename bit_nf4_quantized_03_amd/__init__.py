@@ -22,6 +22,7 @@ __all__ = [
     "qlora_profile_enable", "qlora_profile_read", "qlora_profile_reset",
     "qlora_weight_storage_bytes", "qlora_format_levels", "format_has_dq",
     "QLORA_FMT_NF4_DQ", "QLORA_FMT_NF4", "QLORA_FMT_FP4_DQ", "QLORA_FMT_FP4",
+    "qlora_nf4_merge_workspace_bytes", "qlora_nf4_merge",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora_nf4.so")
@@ -35,6 +36,7 @@ EXPORTED_SYMBOLS = (
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_last_error",
     "qlora_profile_enable", "qlora_profile_read", "qlora_profile_reset",
     "qlora_weight_storage_bytes", "qlora_format_levels",
+    "qlora_nf4_merge_workspace_bytes", "qlora_nf4_merge",
 )
 
 
@@ -76,6 +78,8 @@ def _load():
         "qlora_linear_workspace_bytes": (sz, [i64, i64, i64, i32]),
         "qlora_linear_fwd": (ctypes.c_int, [vp, i64, wp, vp, vp, i32, f32, vp, vp, sz, vp]),
         "qlora_linear_bwd": (ctypes.c_int, [vp, vp, i64, wp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
+        "qlora_nf4_merge_workspace_bytes": (sz, [i64, i64, i32]),
+        "qlora_nf4_merge": (ctypes.c_int, [wp, vp, vp, i32, f32, wp, vp, sz, vp]),
         "qlora_last_error": (ctypes.c_char_p, []),
         "qlora_profile_enable": (ctypes.c_int, [ctypes.c_int]),
         "qlora_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
@@ -272,6 +276,34 @@ def qlora_nf4_dequantize(q: NF4Weight, dtype=None, out=None):
     st = q.c_struct()
     _check("qlora_nf4_dequantize",
            lib.qlora_nf4_dequantize(ctypes.byref(st), _ptr(out), dt, _stream_ptr(q.device)))
+    return out
+
+
+def qlora_nf4_merge_workspace_bytes(rows: int, cols: int, r: int) -> int:
+    return int(lib.qlora_nf4_merge_workspace_bytes(rows, cols, r))
+
+
+def qlora_nf4_merge(W: NF4Weight, A=None, B=None, scale: float = 0.0, out: Optional[NF4Weight] = None,
+                    ws=None, fmt: Optional[int] = None) -> NF4Weight:
+    """Merge s * B A into the quantized base W and quantize the result again
+    into ``out`` (a new weight in format ``fmt``, default W's format)."""
+    torch = _torch()
+    r = 0
+    if A is not None or B is not None:
+        _need_cuda("A", A, torch.float32)
+        _need_cuda("B", B, torch.float32)
+        r = A.shape[0]
+        if A.shape != (r, W.cols) or B.shape != (W.rows, r):
+            raise ValueError(f"A must be [r, {W.cols}] and B [{W.rows}, r]")
+    if out is None:
+        out = NF4Weight.empty(W.rows, W.cols, W.device, W.fmt if fmt is None else fmt)
+    need = qlora_nf4_merge_workspace_bytes(W.rows, W.cols, r)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=W.device)
+    sw, so = W.c_struct(), out.c_struct()
+    _check("qlora_nf4_merge",
+           lib.qlora_nf4_merge(ctypes.byref(sw), _ptr(A), _ptr(B), r, float(scale), ctypes.byref(so), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream_ptr(W.device)))
     return out
 
 

@@ -224,6 +224,38 @@ int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qlora_nf4_w
   return hip_status(e, fn);
 }
 
+size_t qlora_nf4_merge_workspace_bytes(int64_t rows, int64_t cols, int32_t r) {
+  if (rows <= 0 || cols <= 0 || rows > kMaxElems / cols || r < 0 || r > 256) return 0;
+  return qnf4::merge_ws_bytes(rows, cols, r);
+}
+
+int qlora_nf4_merge(const qlora_nf4_weight *W, const float *A, const float *B, int32_t r, float scale,
+                    const qlora_nf4_weight *out, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "qlora_nf4_merge";
+  int st = check_weight(W, fn);
+  if (st != QLORA_OK) return st;
+  st = check_weight(out, fn);
+  if (st != QLORA_OK) return st;
+  if (out->rows != W->rows || out->cols != W->cols)
+    return fail(QLORA_ERR_SHAPE, "%s: out is %lld x %lld but W is %lld x %lld", fn,
+                static_cast<long long>(out->rows), static_cast<long long>(out->cols),
+                static_cast<long long>(W->rows), static_cast<long long>(W->cols));
+  if (r < 0 || r > 256) return fail(QLORA_ERR_SHAPE, "%s: r = %d out of [0, 256]", fn, r);
+  if (r > 0 && (!A || !B)) return fail(QLORA_ERR_NULL, "%s: r > 0 needs A and B", fn);
+  if (r == 0 && (A || B)) return fail(QLORA_ERR_SHAPE, "%s: r = 0 needs A = B = NULL", fn);
+  if ((A && !aligned16(A)) || (B && !aligned16(B)))
+    return fail(QLORA_ERR_ALIGN, "%s: A and B must be 16-byte aligned", fn);
+  const size_t need = qnf4::merge_ws_bytes(W->rows, W->cols, r);
+  if (!ws || ws_bytes < need)
+    return fail(QLORA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need,
+                ws ? ws_bytes : size_t(0));
+  if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  hipError_t e = qnf4::launch_merge(make_args(0, W, r, scale), A, B, out->format, out->codes, out->absmax_q,
+                                    out->dq_scale, out->dq_mean, out->absmax, ws,
+                                    static_cast<hipStream_t>(stream));
+  return hip_status(e, fn);
+}
+
 int qlora_profile_enable(int on) {
   qnf4::prof_set(on != 0);
   return ok();

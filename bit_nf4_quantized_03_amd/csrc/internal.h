@@ -86,6 +86,15 @@ hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const 
                       const float *B, void *dX, float *dA, float *dB, void *ws,
                       hipStream_t s);
 
+// ------------------------------------------------------------------- merge
+// W' = fp32(w-hat + s B A) (rank sum in fp64) into the workspace, then
+// quantized into the output buffers in `out_format`. Workspace: merged fp32
+// [N*K] | B^T in fp64 [r*N] | quantize workspace.
+size_t merge_ws_bytes(int64_t N, int64_t K, int r);
+hipError_t launch_merge(const LinearArgs &w, const float *A, const float *B, int out_format, uint8_t *codes,
+                        int8_t *absmax_q, float *dq_scale, float *dq_mean, float *absmax, void *ws,
+                        hipStream_t s);
+
 // Skinny-M forward (M <= 32): fp32 split partials of Y and of X A^T at the
 // start of the workspace, then the bf16 output.
 size_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K, int r);

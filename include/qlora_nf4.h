@@ -210,6 +210,32 @@ int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qlora_nf4_w
                      void *dX, float *dA, float *dB, void *ws, size_t ws_bytes,
                      void *stream);
 
+/* Workspace bytes needed by qlora_nf4_merge (0 if the sizes are invalid). */
+size_t qlora_nf4_merge_workspace_bytes(int64_t rows, int64_t cols, int32_t r);
+
+/*
+ * Merge a LoRA adapter into the quantized base and quantize the result again
+ * (QLoRA vs ChatGPT page, capability on adapter composition: adapters are
+ * merged into the base weights to give a standalone model):
+ *     W'[n][k] = fp32(w-hat[n][k] + fp64(scale * sum_j B[n][j] A[j][k]))
+ * with w-hat the fp32 dequantized W (any qlora_format), the rank sum in fp64
+ * over j ascending (each fp32 product is exact in fp64), one fp64 multiply by
+ * scale, one fp64 add and one rounding to fp32; then W' is quantized into
+ * `out` exactly as qlora_nf4_quantize does, in out->format. Results are
+ * bit-identical to that definition.
+ *   W      the base, rows = N, cols = K (any shape the weight allows)
+ *   A      fp32 [r, K], B fp32 [N, r] (device); r = 0 with A = B = NULL
+ *          requantizes w-hat (for instance into another format); 0 <= r <= 256
+ *   out    same rows/cols as W, any format, buffers allocated by the caller;
+ *          it may be W itself (W is read completely before out is written)
+ *   ws     device workspace of at least qlora_nf4_merge_workspace_bytes()
+ * A weighted ensemble of adapters is one call with the adapters concatenated
+ * along r and each weight folded into its columns of B.
+ */
+int qlora_nf4_merge(const qlora_nf4_weight *W, const float *A, const float *B, int32_t r,
+                    float scale, const qlora_nf4_weight *out, void *ws, size_t ws_bytes,
+                    void *stream);
+
 /*
  * Opt-in kernel timing for benchmarks. While enabled, each call records a
  * pair of HIP events on its stream around its dominant kernel:

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(qb.EXPORTED_SYMBOLS) == names
@@ -77,6 +77,25 @@ def test_formats_reject_bad_values():
     # with DQ the fp32 constants are not needed, the DQ buffers are
     w = qb._Weight(64, 64, FAKE, FAKE, 0, FAKE, 0, 2)
     assert lib.qlora_nf4_dequantize(ref(w), FAKE, 0, None) == -1
+
+
+def test_merge_rejects_bad_arguments():
+    ref = ctypes.byref
+    w = _weight(64, 64)
+    assert qb.qlora_nf4_merge_workspace_bytes(64, 64, 300) == 0
+    assert qb.qlora_nf4_merge_workspace_bytes(0, 64, 8) == 0
+    need = qb.qlora_nf4_merge_workspace_bytes(64, 64, 8)
+    assert need >= 64 * 64 * 4 + 64 * 8 * 8
+    assert lib.qlora_nf4_merge(None, FAKE, FAKE, 8, 1.0, ref(w), FAKE, need, None) == -1
+    assert lib.qlora_nf4_merge(ref(w), FAKE, FAKE, 8, 1.0, ref(_weight(64, 128)), FAKE, need, None) == -2
+    assert lib.qlora_nf4_merge(ref(w), None, FAKE, 8, 1.0, ref(w), FAKE, need, None) == -1
+    assert lib.qlora_nf4_merge(ref(w), FAKE, FAKE, 0, 1.0, ref(w), FAKE, need, None) == -2
+    assert lib.qlora_nf4_merge(ref(w), FAKE, FAKE, 300, 1.0, ref(w), FAKE, need, None) == -2
+    assert lib.qlora_nf4_merge(ref(w), FAKE + 4, FAKE, 8, 1.0, ref(w), FAKE, need, None) == -6
+    assert lib.qlora_nf4_merge(ref(w), FAKE, FAKE, 8, 1.0, ref(w), FAKE, need - 1, None) == -4
+    assert "workspace needs" in qb.qlora_last_error()
+    bad = qb._Weight(64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 5)
+    assert lib.qlora_nf4_merge(ref(w), FAKE, FAKE, 8, 1.0, ref(bad), FAKE, need, None) == -7
 
 
 def test_sizes_reject_bad_shapes():
