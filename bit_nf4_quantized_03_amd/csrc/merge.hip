@@ -65,38 +65,63 @@ __global__ __launch_bounds__(kMgThreads) void k_merge(MergeParams p) {
 #pragma unroll
   for (int i = 0; i < kMgRows; ++i) acc[i] = 0.0;
   const float *ap = p.A + k;
-  for (int j = 0; j < p.r; ++j) {
-    const double a = static_cast<double>(ap[static_cast<int64_t>(j) * p.K]);
-    // the workgroup's 32 B values of this j: uniform, 256-byte aligned
-    const d8 *bt = reinterpret_cast<const d8 *>(p.Bt + static_cast<int64_t>(j) * p.Np + n0);
-    d8 bv[kMgRows / 8];
+  // Four rank steps per batch, with no branch inside, so that the four A
+  // loads go out together. A step past r reads row r - 1 and multiplies by
+  // a = 0, which leaves acc exactly unchanged (acc is never -0).
+  for (int j0 = 0; j0 < p.r; j0 += 4) {
+    float a4[4];
 #pragma unroll
-    for (int q = 0; q < kMgRows / 8; ++q) bv[q] = bt[q];
+    for (int u = 0; u < 4; ++u) a4[u] = ap[static_cast<int64_t>(min(j0 + u, p.r - 1)) * p.K];
 #pragma unroll
-    for (int i = 0; i < kMgRows; ++i) acc[i] = __fma_rn(bv[i / 8][i % 8], a, acc[i]);
+    for (int u = 0; u < 4; ++u) {
+      const int j = min(j0 + u, p.r - 1);
+      const double a = j0 + u < p.r ? static_cast<double>(a4[u]) : 0.0;
+      // the workgroup's 32 B values of this step: uniform, 256-byte aligned
+      const d8 *bt = reinterpret_cast<const d8 *>(p.Bt + static_cast<int64_t>(j) * p.Np + n0);
+      d8 bv[kMgRows / 8];
+#pragma unroll
+      for (int q = 0; q < kMgRows / 8; ++q) bv[q] = bt[q];
+#pragma unroll
+      for (int i = 0; i < kMgRows; ++i) acc[i] = __fma_rn(bv[i / 8][i % 8], a, acc[i]);
+    }
   }
 
   const double s = static_cast<double>(p.scale);
   const float mu = kDq ? p.dq_mean[0] : 0.0f;
   __syncthreads();   // lv ready
+  // w-hat and the store, eight rows at a time: every load of the eight rows
+  // (code byte, block constant) is issued before the first is used; rows
+  // past N are clamped for the loads and not stored.
+  constexpr int kChunk = 8;
 #pragma unroll
-  for (int i = 0; i < kMgRows; ++i) {
-    const int64_t n = n0 + i;
-    if (n >= p.N || !k_ok) continue;
-    const int64_t e = n * p.K + k;
-    const uint32_t byte = p.codes[e >> 1];
-    const uint32_t code = (e & 1) ? (byte & 0xFu) : (byte >> 4);
-    const int64_t b = e / kBlock;
-    float c;
-    if constexpr (kDq) {
-      const float kd = __fdiv_rn(p.dq_scale[b / kDqBlock], 127.0f);
-      c = __fadd_rn(__fmul_rn(static_cast<float>(p.absmax_q[b]), kd), mu);
-    } else {
-      c = p.absmax[b];
+  for (int i0 = 0; i0 < kMgRows; i0 += kChunk) {
+    int64_t e[kChunk];
+    uint32_t byte[kChunk];
+    float cv[kChunk];
+    float ds[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int64_t n = min(n0 + i0 + u, p.N - 1);
+      e[u] = n * p.K + k;
+      const int64_t blk = e[u] / kBlock;
+      byte[u] = p.codes[e[u] >> 1];
+      if constexpr (kDq) {
+        cv[u] = static_cast<float>(p.absmax_q[blk]);
+        ds[u] = p.dq_scale[blk / kDqBlock];
+      } else {
+        cv[u] = p.absmax[blk];
+        ds[u] = 0.0f;
+      }
     }
-    const float w = __fmul_rn(lv[code], c);
-    const double u = __dadd_rn(static_cast<double>(w), __dmul_rn(s, acc[i]));
-    p.out[e] = static_cast<float>(u);   // round to nearest even
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const uint32_t code = (e[u] & 1) ? (byte[u] & 0xFu) : (byte[u] >> 4);
+      float c = cv[u];
+      if constexpr (kDq) c = __fadd_rn(__fmul_rn(cv[u], __fdiv_rn(ds[u], 127.0f)), mu);
+      const float w = __fmul_rn(lv[code], c);
+      const double v = __dadd_rn(static_cast<double>(w), __dmul_rn(s, acc[i0 + u]));
+      if (n0 + i0 + u < p.N && k_ok) p.out[e[u]] = static_cast<float>(v);   // round to nearest even
+    }
   }
 }
 
