@@ -173,12 +173,18 @@ __device__ __forceinline__ float code_lane(const uint4 &raw, int64_t e, int64_t 
   }
   // Rare: exact division, element by element, so that a wave pays only for
   // the elements some lane needs (ratios of bf16 values hit a dyadic
-  // threshold such as FP4's 1/8 exactly now and then).
+  // threshold such as FP4's 1/8 exactly now and then). One test first, so
+  // that a wave with no such element skips the per-element tests.
+  bool any = false;
 #pragma unroll
-  for (int i = 0; i < kEpl; ++i) {
-    if (near[i]) {
-      const float y = (a == 0.0f) ? 0.0f : __fdiv_rn(x[i], a);
-      c[i] = code_from_y(y, tab);
+  for (int i = 0; i < kEpl; ++i) any |= near[i];
+  if (any) {
+#pragma unroll
+    for (int i = 0; i < kEpl; ++i) {
+      if (near[i]) {
+        const float y = (a == 0.0f) ? 0.0f : __fdiv_rn(x[i], a);
+        c[i] = code_from_y(y, tab);
+      }
     }
   }
   if (kGuard) {
