@@ -17,6 +17,7 @@ Modules
   linear  QLoRA linear forward and backward in fp64.
   merge   merging an adapter into the dequantized base (fp64 rank sum,
           one rounding to fp32) and requantizing it.
+  adamw   one AdamW step of the adapter parameters in fp32, op by op.
 
 Sources (the pages the method is taken from):
   * Guanaco topic page (chipfoundryservices.com), "Technical Innovations":
@@ -37,4 +38,4 @@ Sources (the pages the method is taken from):
 Every function whose result is pinned only by its own self-consistency says
 "parity unpinned" in its docstring; at present none does.
 """
-from . import nf4, linear, merge  # noqa: F401
+from . import nf4, linear, merge, adamw  # noqa: F401
