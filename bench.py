@@ -540,6 +540,32 @@ def main():
         del wsm, qbase, qout
         torch.cuda.empty_cache()
 
+    # ---------- AdamW on the adapter parameters of a 7B model (32 layers x
+    # q, k, v, o, gate, up, down at r = 64: 159.9 M parameters), state in
+    # device memory, then paged from pinned host memory
+    opt = None
+    if not args.no_formats:
+        n_opt = 32 * (4 * r * (4096 + 4096) + 3 * r * (4096 + 11008))
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(77)
+        Po = torch.randn(n_opt, generator=gen, device=dev) * 0.02
+        Go = torch.randn(n_opt, generator=gen, device=dev) * 1e-3
+        Mo, Vo = torch.zeros_like(Po), torch.zeros_like(Po)
+        d_ms = ev_time(lambda: qb.qlora_adamw_step(Po, Go, Mo, Vo, 1, 1e-4, weight_decay=0.01), 5)
+        Mh = torch.zeros(n_opt, dtype=torch.float32, pin_memory=True)
+        Vh = torch.zeros(n_opt, dtype=torch.float32, pin_memory=True)
+        wso = torch.empty(qb.qlora_adamw_workspace_bytes(n_opt, True), dtype=torch.uint8, device=dev)
+        h_ms = ev_time(lambda: qb.qlora_adamw_step(Po, Go, Mh, Vh, 1, 1e-4, weight_decay=0.01, ws=wso), 3)
+        hbm = 28.0 * n_opt
+        opt = {"params": n_opt, "device_state_us": d_ms * 1e3, "device_state_gbs": hbm / (d_ms * 1e-3) / 1e9,
+               "device_state_frac_of_hbm_peak": hbm / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+               "paged_state_ms": h_ms, "paged_state_pcie_gbs": 16.0 * n_opt / (h_ms * 1e-3) / 1e9}
+        log(f"adamw {n_opt / 1e6:.1f} M params: device state {d_ms * 1e3:.0f} us "
+            f"({opt['device_state_gbs']:.0f} GB/s HBM); paged state {h_ms:.1f} ms "
+            f"({opt['paged_state_pcie_gbs']:.1f} GB/s over PCIe, both ways)")
+        del Po, Go, Mo, Vo, Mh, Vh, wso
+        torch.cuda.empty_cache()
+
     mlp = {}
     if not args.no_large:
         for name, (Nm, Km) in (("up65b", (22016, 8192)), ("down65b", (8192, 22016))):
@@ -685,6 +711,7 @@ def main():
         "decode": decode,
         "formats": formats,
         "merge": merge_row,
+        "adamw": opt,
         "mlp65b": mlp,
         "dequant_solo": dq_solo,
         "whole_model_roundtrip": wm,

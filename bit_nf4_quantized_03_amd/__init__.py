@@ -23,6 +23,7 @@ __all__ = [
     "qlora_weight_storage_bytes", "qlora_format_levels", "format_has_dq",
     "QLORA_FMT_NF4_DQ", "QLORA_FMT_NF4", "QLORA_FMT_FP4_DQ", "QLORA_FMT_FP4",
     "qlora_nf4_merge_workspace_bytes", "qlora_nf4_merge",
+    "qlora_adamw_workspace_bytes", "qlora_adamw_step",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora_nf4.so")
@@ -37,6 +38,7 @@ EXPORTED_SYMBOLS = (
     "qlora_profile_enable", "qlora_profile_read", "qlora_profile_reset",
     "qlora_weight_storage_bytes", "qlora_format_levels",
     "qlora_nf4_merge_workspace_bytes", "qlora_nf4_merge",
+    "qlora_adamw_workspace_bytes", "qlora_adamw_step",
 )
 
 
@@ -53,6 +55,11 @@ class _Weight(ctypes.Structure):
         ("dq_scale", ctypes.c_void_p), ("dq_mean", ctypes.c_void_p),
         ("absmax", ctypes.c_void_p), ("format", ctypes.c_int32),
     ]
+
+
+class _AdamwHparams(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_float) for name in
+                ("lr", "beta1", "beta2", "eps", "weight_decay", "bias_correction1", "bias_correction2")]
 
 
 def _load():
@@ -80,6 +87,9 @@ def _load():
         "qlora_linear_bwd": (ctypes.c_int, [vp, vp, i64, wp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
         "qlora_nf4_merge_workspace_bytes": (sz, [i64, i64, i32]),
         "qlora_nf4_merge": (ctypes.c_int, [wp, vp, vp, i32, f32, wp, vp, sz, vp]),
+        "qlora_adamw_workspace_bytes": (sz, [i64, ctypes.c_int]),
+        "qlora_adamw_step": (ctypes.c_int, [vp, vp, vp, vp, i64, ctypes.POINTER(_AdamwHparams), ctypes.c_int,
+                                            vp, sz, vp]),
         "qlora_last_error": (ctypes.c_char_p, []),
         "qlora_profile_enable": (ctypes.c_int, [ctypes.c_int]),
         "qlora_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
@@ -305,6 +315,40 @@ def qlora_nf4_merge(W: NF4Weight, A=None, B=None, scale: float = 0.0, out: Optio
            lib.qlora_nf4_merge(ctypes.byref(sw), _ptr(A), _ptr(B), r, float(scale), ctypes.byref(so), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream_ptr(W.device)))
     return out
+
+
+def qlora_adamw_workspace_bytes(n: int, state_on_host: bool) -> int:
+    return int(lib.qlora_adamw_workspace_bytes(n, 1 if state_on_host else 0))
+
+
+def qlora_adamw_step(param, grad, m, v, step: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                     eps: float = 1e-8, weight_decay: float = 0.0, ws=None) -> None:
+    """One AdamW step in place on fp32 ``param`` and its state ``m``, ``v``.
+    param and grad are CUDA tensors; m and v are CUDA tensors, or pinned CPU
+    tensors (the state paged from host memory). ``step`` is t >= 1; the bias
+    corrections are fp32(1 - beta^t) with beta rounded to fp32 first."""
+    torch = _torch()
+    _need_cuda("param", param, torch.float32)
+    _need_cuda("grad", grad, torch.float32)
+    n = param.numel()
+    on_host = not m.is_cuda
+    for name, t in (("m", m), ("v", v)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+            raise ValueError(f"{name} must be a contiguous float32 tensor of {n} elements")
+        if t.is_cuda == on_host or (on_host and not t.is_pinned()):
+            raise ValueError("m and v must both be CUDA tensors or both pinned CPU tensors")
+    if grad.numel() != n or step < 1:
+        raise ValueError("grad must match param and step must be >= 1")
+    f32 = lambda x: float(ctypes.c_float(x).value)  # noqa: E731
+    hp = _AdamwHparams(lr, beta1, beta2, eps, weight_decay,
+                       f32(1.0 - f32(beta1) ** step), f32(1.0 - f32(beta2) ** step))
+    need = qlora_adamw_workspace_bytes(n, on_host)
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=param.device)
+    _check("qlora_adamw_step",
+           lib.qlora_adamw_step(_ptr(param), _ptr(grad), _ptr(m), _ptr(v), n, ctypes.byref(hp),
+                                1 if on_host else 0, _ptr(ws) if need else None,
+                                ws.numel() * ws.element_size() if need else 0, _stream_ptr(param.device)))
 
 
 def _linear_ws(M, N, K, r, device, ws):

@@ -1,0 +1,20 @@
+// Private interface of the AdamW step (adamw.hip), used by the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+#include <cstddef>
+
+namespace qnf4 {
+
+struct AdamwHparams {
+  float lr, beta1, beta2, eps, weight_decay, bias_correction1, bias_correction2;
+};
+
+// Workspace: with the state on the host, two device staging arrays (m, v) of
+// up to 4 Mi elements each; none otherwise.
+size_t adamw_ws_bytes(int64_t n, bool state_on_host);
+hipError_t launch_adamw(float *param, const float *grad, float *m, float *v, int64_t n, const AdamwHparams &hp,
+                        bool state_on_host, void *ws, hipStream_t s);
+
+}  // namespace qnf4

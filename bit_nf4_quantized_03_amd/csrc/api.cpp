@@ -7,6 +7,7 @@
 #include <string>
 
 #include "../../include/qlora_nf4.h"
+#include "adamw.h"
 #include "internal.h"
 
 namespace {
@@ -253,6 +254,34 @@ int qlora_nf4_merge(const qlora_nf4_weight *W, const float *A, const float *B, i
   hipError_t e = qnf4::launch_merge(make_args(0, W, r, scale), A, B, out->format, out->codes, out->absmax_q,
                                     out->dq_scale, out->dq_mean, out->absmax, ws,
                                     static_cast<hipStream_t>(stream));
+  return hip_status(e, fn);
+}
+
+size_t qlora_adamw_workspace_bytes(int64_t n, int state_on_host) {
+  if (n <= 0 || n > kMaxElems) return 0;
+  return qnf4::adamw_ws_bytes(n, state_on_host != 0);
+}
+
+int qlora_adamw_step(float *param, const float *grad, float *m, float *v, int64_t n,
+                     const qlora_adamw_hparams *hp, int state_on_host, void *ws, size_t ws_bytes,
+                     void *stream) {
+  const char *fn = "qlora_adamw_step";
+  if (!param || !grad || !m || !v || !hp) return fail(QLORA_ERR_NULL, "%s: a pointer is NULL", fn);
+  if (n <= 0 || n > kMaxElems) return fail(QLORA_ERR_SHAPE, "%s: invalid n = %lld", fn, static_cast<long long>(n));
+  if (!aligned16(param) || !aligned16(grad) || !aligned16(m) || !aligned16(v))
+    return fail(QLORA_ERR_ALIGN, "%s: param, grad, m and v must be 16-byte aligned", fn);
+  if (!(hp->bias_correction1 > 0.0f && hp->bias_correction1 <= 1.0f) ||
+      !(hp->bias_correction2 > 0.0f && hp->bias_correction2 <= 1.0f))
+    return fail(QLORA_ERR_SHAPE, "%s: bias corrections must lie in (0, 1]", fn);
+  if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) || !(hp->eps >= 0.0f))
+    return fail(QLORA_ERR_SHAPE, "%s: need 0 <= beta < 1 and eps >= 0", fn);
+  const size_t need = qnf4::adamw_ws_bytes(n, state_on_host != 0);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(QLORA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws ? ws_bytes : size_t(0));
+  if (need > 0 && !aligned16(ws)) return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  const qnf4::AdamwHparams h{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->bias_correction1,
+                             hp->bias_correction2};
+  hipError_t e = qnf4::launch_adamw(param, grad, m, v, n, h, state_on_host != 0, ws, static_cast<hipStream_t>(stream));
   return hip_status(e, fn);
 }
 

@@ -236,6 +236,43 @@ int qlora_nf4_merge(const qlora_nf4_weight *W, const float *A, const float *B, i
                     float scale, const qlora_nf4_weight *out, void *ws, size_t ws_bytes,
                     void *stream);
 
+/* AdamW hyperparameters; the bias corrections are 1 - beta1^t and
+ * 1 - beta2^t for the step count t >= 1, computed by the caller. */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  float bias_correction1, bias_correction2;
+} qlora_adamw_hparams;
+
+/* Workspace bytes of qlora_adamw_step: 0 with the state in device memory,
+ * two staging arrays of up to 4 Mi floats each with the state on the host
+ * (0 also if n is invalid). */
+size_t qlora_adamw_workspace_bytes(int64_t n, int state_on_host);
+
+/*
+ * One AdamW step of n adapter parameters (Guanaco topic page, "Technical
+ * Innovations: Paged Optimizers", and QLoRA vs ChatGPT page, capability on
+ * paged optimizers: the optimizer state, momentum and variance, is paged
+ * between GPU and host memory). Per element, all fp32, each operation
+ * rounded to nearest even, no fused multiply-add (c1 = 1 - beta1 and
+ * c2 = 1 - beta2 in fp32):
+ *     m' = b1 m + c1 g,  v' = b2 v + c2 (g g)
+ *     p' = p - lr ((m' / bc1) / (sqrt(v' / bc2) + eps) + wd p)
+ * Results are bit-identical to that definition wherever the state lives.
+ *   param, grad   fp32 [n] (device); param and the state are updated in place
+ *   m, v          fp32 [n]: device memory (state_on_host = 0) or pinned host
+ *                 memory from hipHostMalloc (state_on_host = 1), which the
+ *                 call pages through the workspace in chunks, copies ordered
+ *                 on `stream`; the host arrays may be read again only after
+ *                 the stream has reached this call's end
+ *   ws            device workspace of qlora_adamw_workspace_bytes() bytes
+ *                 (may be NULL when that is 0)
+ * Errors: NULL pointers, n <= 0, misaligned pointers, bias corrections
+ * outside (0, 1], beta outside [0, 1), eps < 0, a short workspace.
+ */
+int qlora_adamw_step(float *param, const float *grad, float *m, float *v, int64_t n,
+                     const qlora_adamw_hparams *hp, int state_on_host, void *ws, size_t ws_bytes,
+                     void *stream);
+
 /*
  * Opt-in kernel timing for benchmarks. While enabled, each call records a
  * pair of HIP events on its stream around its dominant kernel:

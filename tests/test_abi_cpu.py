@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(qb.EXPORTED_SYMBOLS) == names
@@ -96,6 +96,24 @@ def test_merge_rejects_bad_arguments():
     assert "workspace needs" in qb.qlora_last_error()
     bad = qb._Weight(64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 5)
     assert lib.qlora_nf4_merge(ref(w), FAKE, FAKE, 8, 1.0, ref(bad), FAKE, need, None) == -7
+
+
+def test_adamw_rejects_bad_arguments():
+    ref = ctypes.byref
+    hp = qb._AdamwHparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 0.1, 0.001)
+    assert qb.qlora_adamw_workspace_bytes(1000, False) == 0
+    assert qb.qlora_adamw_workspace_bytes(1001, True) == 2 * 1024 * 4
+    assert qb.qlora_adamw_workspace_bytes(0, True) == 0
+    step = lib.qlora_adamw_step
+    assert step(None, FAKE, FAKE, FAKE, 64, ref(hp), 0, None, 0, None) == -1
+    assert step(FAKE, FAKE, FAKE, FAKE, 0, ref(hp), 0, None, 0, None) == -2
+    assert step(FAKE, FAKE + 4, FAKE, FAKE, 64, ref(hp), 0, None, 0, None) == -6
+    assert step(FAKE, FAKE, FAKE, FAKE, 64, ref(hp), 1, None, 0, None) == -4
+    bad = qb._AdamwHparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 0.0, 0.001)
+    assert step(FAKE, FAKE, FAKE, FAKE, 64, ref(bad), 0, None, 0, None) == -2
+    assert "bias corrections" in qb.qlora_last_error()
+    bad = qb._AdamwHparams(1e-3, 1.0, 0.999, 1e-8, 0.0, 0.1, 0.001)
+    assert step(FAKE, FAKE, FAKE, FAKE, 64, ref(bad), 0, None, 0, None) == -2
 
 
 def test_sizes_reject_bad_shapes():
