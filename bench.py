@@ -566,6 +566,42 @@ def main():
         del Po, Go, Mo, Vo, Mh, Vh, wso
         torch.cuda.empty_cache()
 
+    # ---------- the seven QLoRA projections of one Llama-7B decoder layer
+    # (q, k, v, o: 4096 x 4096; gate, up: 11008 x 4096; down: 4096 x 11008),
+    # forward and backward at 4096 tokens, r = 64, one after another on the
+    # stream (attention and the activations are not part of the library)
+    layer_row = None
+    if not args.no_formats:
+        shapes = [("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
+                  ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008)]
+        Ml = 4096
+        projs = []
+        for i, (nm, Nl, Kl) in enumerate(shapes):
+            ql = qb.qlora_nf4_quantize(dev_normal((Nl, Kl), 0.02, 900 + i))
+            projs.append((ql, dev_normal((Ml, Kl), 1.0, 950 + i), dev_normal((r, Kl), 0.01, 970 + i).float(),
+                          dev_normal((Nl, r), 0.01, 990 + i).float(), dev_normal((Ml, Nl), 1.0, 1010 + i),
+                          torch.empty((Ml, Nl), dtype=torch.bfloat16, device=dev),
+                          torch.empty((Ml, Kl), dtype=torch.bfloat16, device=dev),
+                          torch.empty((r, Kl), dtype=torch.float32, device=dev),
+                          torch.empty((Nl, r), dtype=torch.float32, device=dev),
+                          torch.empty(qb.qlora_linear_workspace_bytes(Ml, Nl, Kl, r), dtype=torch.uint8, device=dev)))
+
+        def layer_step():
+            for (ql, Xl, Al, Bl, dYl, Yl, dXl, dAl, dBl, wsl) in projs:
+                qb.qlora_linear_fwd(Xl, ql, Al, Bl, s, ws=wsl, out=Yl)
+            for (ql, Xl, Al, Bl, dYl, Yl, dXl, dAl, dBl, wsl) in reversed(projs):
+                qb.qlora_linear_bwd(dYl, Xl, ql, Al, Bl, s, ws=wsl, outs=(dXl, dAl, dBl))
+        l_ms = ev_time(layer_step, 5)
+        l_flops = sum(2.0 * Ml * Nl * Kl * 2 + 2.0 * Ml * r * (Kl + Nl) + 4.0 * Ml * r * (Nl + Kl)
+                      for _, Nl, Kl in shapes)
+        layer_row = {"tokens": Ml, "r": r, "ms": l_ms, "tflops": l_flops / (l_ms * 1e-3) / 1e12,
+                 "frac_of_bf16_peak": l_flops / (l_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                 "weight_bytes_nf4": sum(qb.qlora_nf4_storage_bytes(Nl, Kl) for _, Nl, Kl in shapes)}
+        log(f"layer7b projections (7 x fwd + bwd, 4096 tokens): {l_ms:.2f} ms, "
+            f"{layer_row['tflops']:.0f} TFLOP/s")
+        del projs
+        torch.cuda.empty_cache()
+
     mlp = {}
     if not args.no_large:
         for name, (Nm, Km) in (("up65b", (22016, 8192)), ("down65b", (8192, 22016))):
@@ -712,6 +748,7 @@ def main():
         "formats": formats,
         "merge": merge_row,
         "adamw": opt,
+        "layer7b_projections": layer_row,
         "mlp65b": mlp,
         "dequant_solo": dq_solo,
         "whole_model_roundtrip": wm,
