@@ -20,6 +20,14 @@ The JSON line also carries
   decode        the skinny-M forward (GEMV) at the 7B MLP shapes in GB/s,
                 with rotation over > 512 MB of distinct weights;
   mlp65b        forward and backward at the 65B MLP shapes (M = 2048);
+  formats       per weight format (NF4 / FP4, with / without double
+                quantization): quantize, dequantize, forward, backward at the
+                step's shape and the decode GEMV at the 7B gate shape;
+  merge         adapter merge + requantize at the step's shape;
+  adamw         one AdamW step over the 7B model's adapter parameters, state
+                in HBM and paged from pinned host memory;
+  layer7b_projections
+                the seven QLoRA projections of a 7B decoder layer, fwd + bwd;
   dequant_solo  dequantize alone at 65B shapes, bf16 and fp32 out;
   whole_model_roundtrip
                 quantize + dequantize of every tensor of a 65B-shaped
@@ -28,7 +36,7 @@ The JSON line also carries
                 same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-decode] [--no-large] [--wm-layers L] [--no-graph]
+                       [--no-decode] [--no-large] [--no-formats] [--wm-layers L] [--no-graph]
 """
 from __future__ import annotations
 
