@@ -58,8 +58,8 @@ class _Weight(ctypes.Structure):
 
 
 class _AdamwHparams(ctypes.Structure):
-    _fields_ = [(name, ctypes.c_float) for name in
-                ("lr", "beta1", "beta2", "eps", "weight_decay", "bias_correction1", "bias_correction2")]
+    _fields_ = [(name, ctypes.c_float) for name in ("lr", "beta1", "beta2", "eps", "weight_decay")] + \
+        [("step", ctypes.c_int64)]
 
 
 def _load():
@@ -194,7 +194,11 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
-def _need_cuda(name, t, dtype=None):
+def _need_cuda(name, t, dtype=None, shape=None, device=None):
+    """Check that ``t`` is a contiguous CUDA (HIP) tensor of ``dtype``, exactly
+    ``shape`` and on ``device`` (each check only when given). The C ABI takes
+    bare pointers, so these checks are what keeps a short or misplaced tensor
+    from being read or written out of bounds on the GPU."""
     torch = _torch()
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
@@ -202,6 +206,32 @@ def _need_cuda(name, t, dtype=None):
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _need_ws(ws, device):
+    """A caller-supplied workspace: a contiguous CUDA tensor on ``device``
+    (its size is checked by the library)."""
+    _need_cuda("ws", ws, device=device)
+
+
+def _adapter(W, A, B, device):
+    """Rank of the adapter (A [r, K], B [N, r], fp32) or 0 without one."""
+    torch = _torch()
+    if A is None and B is None:
+        return 0
+    if A is None or B is None:
+        raise ValueError("A and B must both be given or both be None")
+    _need_cuda("A", A, torch.float32, device=device)
+    if A.dim() != 2 or A.shape[0] < 1:
+        raise ValueError(f"A must be [r, {W.cols}] with r >= 1")
+    r = A.shape[0]
+    _need_cuda("A", A, shape=(r, W.cols))
+    _need_cuda("B", B, torch.float32, (W.rows, r), device)
+    return r
 
 
 @dataclasses.dataclass
@@ -283,6 +313,8 @@ def qlora_nf4_dequantize(q: NF4Weight, dtype=None, out=None):
         raise TypeError(f"dtype must be float32 or bfloat16, got {dtype}")
     if out is None:
         out = torch.empty((q.rows, q.cols), dtype=dtype, device=q.device)
+    else:
+        _need_cuda("out", out, dtype, (q.rows, q.cols), q.device)
     st = q.c_struct()
     _check("qlora_nf4_dequantize",
            lib.qlora_nf4_dequantize(ctypes.byref(st), _ptr(out), dt, _stream_ptr(q.device)))
@@ -298,18 +330,14 @@ def qlora_nf4_merge(W: NF4Weight, A=None, B=None, scale: float = 0.0, out: Optio
     """Merge s * B A into the quantized base W and quantize the result again
     into ``out`` (a new weight in format ``fmt``, default W's format)."""
     torch = _torch()
-    r = 0
-    if A is not None or B is not None:
-        _need_cuda("A", A, torch.float32)
-        _need_cuda("B", B, torch.float32)
-        r = A.shape[0]
-        if A.shape != (r, W.cols) or B.shape != (W.rows, r):
-            raise ValueError(f"A must be [r, {W.cols}] and B [{W.rows}, r]")
+    r = _adapter(W, A, B, W.device)
     if out is None:
         out = NF4Weight.empty(W.rows, W.cols, W.device, W.fmt if fmt is None else fmt)
     need = qlora_nf4_merge_workspace_bytes(W.rows, W.cols, r)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=W.device)
+    else:
+        _need_ws(ws, W.device)
     sw, so = W.c_struct(), out.c_struct()
     _check("qlora_nf4_merge",
            lib.qlora_nf4_merge(ctypes.byref(sw), _ptr(A), _ptr(B), r, float(scale), ctypes.byref(so), _ptr(ws),
@@ -325,11 +353,11 @@ def qlora_adamw_step(param, grad, m, v, step: int, lr: float, beta1: float = 0.9
                      eps: float = 1e-8, weight_decay: float = 0.0, ws=None) -> None:
     """One AdamW step in place on fp32 ``param`` and its state ``m``, ``v``.
     param and grad are CUDA tensors; m and v are CUDA tensors, or pinned CPU
-    tensors (the state paged from host memory). ``step`` is t >= 1; the bias
-    corrections are fp32(1 - beta^t) with beta rounded to fp32 first."""
+    tensors (the state paged from host memory). ``step`` is t >= 1; the
+    library forms the bias corrections from it."""
     torch = _torch()
     _need_cuda("param", param, torch.float32)
-    _need_cuda("grad", grad, torch.float32)
+    _need_cuda("grad", grad, torch.float32, device=param.device)
     n = param.numel()
     on_host = not m.is_cuda
     for name, t in (("m", m), ("v", v)):
@@ -339,12 +367,14 @@ def qlora_adamw_step(param, grad, m, v, step: int, lr: float, beta1: float = 0.9
             raise ValueError("m and v must both be CUDA tensors or both pinned CPU tensors")
     if grad.numel() != n or step < 1:
         raise ValueError("grad must match param and step must be >= 1")
-    f32 = lambda x: float(ctypes.c_float(x).value)  # noqa: E731
-    hp = _AdamwHparams(lr, beta1, beta2, eps, weight_decay,
-                       f32(1.0 - f32(beta1) ** step), f32(1.0 - f32(beta2) ** step))
+    if not on_host and (m.device != param.device or v.device != param.device):
+        raise ValueError("m and v must be on param's device")
+    hp = _AdamwHparams(lr, beta1, beta2, eps, weight_decay, int(step))
     need = qlora_adamw_workspace_bytes(n, on_host)
     if need and ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=param.device)
+    elif need:
+        _need_ws(ws, param.device)
     _check("qlora_adamw_step",
            lib.qlora_adamw_step(_ptr(param), _ptr(grad), _ptr(m), _ptr(v), n, ctypes.byref(hp),
                                 1 if on_host else 0, _ptr(ws) if need else None,
@@ -356,21 +386,31 @@ def _linear_ws(M, N, K, r, device, ws):
     need = qlora_linear_workspace_bytes(M, N, K, r)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    else:
+        _need_ws(ws, device)
     return ws
+
+
+def _activation(name, X, W: NF4Weight):
+    """Rows M of a bf16 activation [M, W.cols] on W's device."""
+    torch = _torch()
+    _need_cuda(name, X, torch.bfloat16, device=W.device)
+    if X.dim() != 2 or X.shape[0] < 1:
+        raise ValueError(f"{name} must be 2-D [M, {W.cols}] with M >= 1")
+    _need_cuda(name, X, shape=(X.shape[0], W.cols))
+    return X.shape[0]
 
 
 def qlora_linear_fwd(X, W: NF4Weight, A=None, B=None, scale: float = 0.0, ws=None, out=None):
     """Y = X W^T + scale (X A^T) B^T; X bf16 [M, K], A fp32 [r, K], B fp32 [N, r]."""
     torch = _torch()
-    _need_cuda("X", X, torch.bfloat16)
-    M, K = X.shape
-    N = W.rows
-    r = 0 if A is None else A.shape[0]
-    if A is not None:
-        _need_cuda("A", A, torch.float32)
-        _need_cuda("B", B, torch.float32)
+    M = _activation("X", X, W)
+    K, N = W.cols, W.rows
+    r = _adapter(W, A, B, W.device)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    else:
+        _need_cuda("out", out, torch.bfloat16, (M, N), W.device)
     ws = _linear_ws(M, N, K, r, X.device, ws)
     st = W.c_struct()
     _check("qlora_linear_fwd",
@@ -384,17 +424,22 @@ def qlora_linear_bwd(dY, X, W: NF4Weight, A=None, B=None, scale: float = 0.0, ws
                      outs: Optional[Tuple] = None):
     """(dX, dA, dB) of the QLoRA linear layer; the base weight gets no gradient."""
     torch = _torch()
-    _need_cuda("dY", dY, torch.bfloat16)
-    _need_cuda("X", X, torch.bfloat16)
-    M, K = X.shape
-    N = W.rows
-    r = 0 if A is None else A.shape[0]
+    M = _activation("X", X, W)
+    K, N = W.cols, W.rows
+    _need_cuda("dY", dY, torch.bfloat16, (M, N), W.device)
+    r = _adapter(W, A, B, W.device)
     if outs is None:
         dX = torch.empty((M, K), dtype=torch.bfloat16, device=X.device)
         dA = torch.empty((r, K), dtype=torch.float32, device=X.device) if r else None
         dB = torch.empty((N, r), dtype=torch.float32, device=X.device) if r else None
     else:
         dX, dA, dB = outs
+        _need_cuda("dX", dX, torch.bfloat16, (M, K), W.device)
+        if r:
+            _need_cuda("dA", dA, torch.float32, (r, K), W.device)
+            _need_cuda("dB", dB, torch.float32, (N, r), W.device)
+        elif dA is not None or dB is not None:
+            raise ValueError("without an adapter dA and dB must be None")
     ws = _linear_ws(M, N, K, r, X.device, ws)
     st = W.c_struct()
     _check("qlora_linear_bwd",

@@ -8,8 +8,13 @@
 namespace qnf4 {
 
 struct AdamwHparams {
-  float lr, beta1, beta2, eps, weight_decay, bias_correction1, bias_correction2;
+  float lr, beta1, beta2, eps, weight_decay;
+  int64_t step;   // t >= 1
 };
+
+// fp32(1 - beta^t): beta is already an fp32 value; the power and the
+// difference are taken in fp64 and rounded once.
+float adamw_bias_correction(float beta, int64_t t);
 
 // Workspace: with the state on the host, two device staging arrays (m, v) of
 // up to 4 Mi elements each; none otherwise.

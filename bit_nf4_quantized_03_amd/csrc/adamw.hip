@@ -16,6 +16,8 @@
 // stream: copy m and v of a chunk in, run the step on the chunk, copy them
 // back. The stream orders the copies, so a chunk's staging is free again
 // before the next chunk's copies start.
+#include <cmath>
+
 #include "adamw.h"
 #include "internal.h"
 
@@ -96,6 +98,10 @@ void launch_step(float *p, const float *g, float *m, float *v, int64_t n, const 
 
 }  // namespace
 
+float adamw_bias_correction(float beta, int64_t t) {
+  return static_cast<float>(1.0 - std::pow(static_cast<double>(beta), static_cast<double>(t)));
+}
+
 // staging elements per state array, rounded up so that both arrays stay 16-byte aligned
 int64_t stage_elems(int64_t n) { return ceil_div(std::min(n, kPageElems), 64) * 64; }
 
@@ -114,8 +120,8 @@ hipError_t launch_adamw(float *param, const float *grad, float *m, float *v, int
   h.c2 = 1.0f - hp.beta2;
   h.eps = hp.eps;
   h.wd = hp.weight_decay;
-  h.bc1 = hp.bias_correction1;
-  h.bc2 = hp.bias_correction2;
+  h.bc1 = adamw_bias_correction(hp.beta1, hp.step);
+  h.bc2 = adamw_bias_correction(hp.beta2, hp.step);
   if (!state_on_host) {
     launch_step(param, grad, m, v, n, h, s);
     return hipGetLastError();

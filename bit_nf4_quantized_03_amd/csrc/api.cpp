@@ -37,6 +37,10 @@ int hip_status(hipError_t e, const char *where) {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+// The large-tile GEMMs address a 256-row operand tile with 32-bit byte
+// offsets from its first row: 255 rows of a row-major bf16 operand with
+// row length K (forward) or N (input gradient) must stay below 2^32 bytes.
+constexpr int64_t kMaxLinearDim = int64_t(1) << 23;
 
 bool valid_format(int format) { return format >= 0 && format < qnf4::kFormats; }
 
@@ -71,6 +75,10 @@ int check_linear_common(const char *fn, int64_t M, const qlora_nf4_weight *W, co
     return fail(QLORA_ERR_SHAPE,
                 "%s: N (%lld) and K (%lld) must be multiples of 64", fn,
                 static_cast<long long>(W->rows), static_cast<long long>(W->cols));
+  if (W->cols > kMaxLinearDim || W->rows > kMaxLinearDim)
+    return fail(QLORA_ERR_SHAPE, "%s: N (%lld) and K (%lld) must not exceed %lld", fn,
+                static_cast<long long>(W->rows), static_cast<long long>(W->cols),
+                static_cast<long long>(kMaxLinearDim));
   if (r < 0 || r > 256) return fail(QLORA_ERR_SHAPE, "%s: r = %d out of [0, 256]", fn, r);
   if (r > 0 && (!A || !B)) return fail(QLORA_ERR_NULL, "%s: r > 0 needs A and B", fn);
   if (r == 0 && (A || B)) return fail(QLORA_ERR_SHAPE, "%s: r = 0 needs A = B = NULL", fn);
@@ -180,6 +188,7 @@ int qlora_nf4_dequantize(const qlora_nf4_weight *q, void *out, int out_dtype, vo
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > 256) return 0;
   if (N % QLORA_NF4_BLOCK || K % QLORA_NF4_BLOCK) return 0;
+  if (N > kMaxLinearDim || K > kMaxLinearDim) return 0;
   if (N > kMaxElems / K || M > kMaxElems / K || M > kMaxElems / N) return 0;
   return qnf4::linear_ws_bytes(M, N, K, r);
 }
@@ -270,17 +279,14 @@ int qlora_adamw_step(float *param, const float *grad, float *m, float *v, int64_
   if (n <= 0 || n > kMaxElems) return fail(QLORA_ERR_SHAPE, "%s: invalid n = %lld", fn, static_cast<long long>(n));
   if (!aligned16(param) || !aligned16(grad) || !aligned16(m) || !aligned16(v))
     return fail(QLORA_ERR_ALIGN, "%s: param, grad, m and v must be 16-byte aligned", fn);
-  if (!(hp->bias_correction1 > 0.0f && hp->bias_correction1 <= 1.0f) ||
-      !(hp->bias_correction2 > 0.0f && hp->bias_correction2 <= 1.0f))
-    return fail(QLORA_ERR_SHAPE, "%s: bias corrections must lie in (0, 1]", fn);
+  if (hp->step < 1) return fail(QLORA_ERR_SHAPE, "%s: step must be >= 1", fn);
   if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) || !(hp->eps >= 0.0f))
     return fail(QLORA_ERR_SHAPE, "%s: need 0 <= beta < 1 and eps >= 0", fn);
   const size_t need = qnf4::adamw_ws_bytes(n, state_on_host != 0);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(QLORA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, ws ? ws_bytes : size_t(0));
   if (need > 0 && !aligned16(ws)) return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
-  const qnf4::AdamwHparams h{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->bias_correction1,
-                             hp->bias_correction2};
+  const qnf4::AdamwHparams h{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->step};
   hipError_t e = qnf4::launch_adamw(param, grad, m, v, n, h, state_on_host != 0, ws, static_cast<hipStream_t>(stream));
   return hip_status(e, fn);
 }

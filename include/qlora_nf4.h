@@ -180,7 +180,8 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
  * block on the fly.
  *   X      bf16 [M, K] (device)
  *   W      weight with rows = N, cols = K; N and K must be multiples
- *          of 64
+ *          of 64 and at most 2^23 (8388608): the large-tile kernels address
+ *          a 256-row operand tile with 32-bit byte offsets
  *   A      fp32 [r, K], B fp32 [N, r] (device); r = 0 with A = B = NULL
  *          means no adapter; 0 <= r <= 256
  *   scale  the LoRA scale s (alpha / r in the usual convention)
@@ -236,11 +237,13 @@ int qlora_nf4_merge(const qlora_nf4_weight *W, const float *A, const float *B, i
                     float scale, const qlora_nf4_weight *out, void *ws, size_t ws_bytes,
                     void *stream);
 
-/* AdamW hyperparameters; the bias corrections are 1 - beta1^t and
- * 1 - beta2^t for the step count t >= 1, computed by the caller. */
+/* AdamW hyperparameters and the step count t >= 1 of this update (the first
+ * update is t = 1). The library forms the bias corrections
+ * bc1 = fp32(1 - beta1^t) and bc2 = fp32(1 - beta2^t) from the fp32 betas,
+ * the power and the difference in fp64, rounded once. */
 typedef struct {
   float lr, beta1, beta2, eps, weight_decay;
-  float bias_correction1, bias_correction2;
+  int64_t step;
 } qlora_adamw_hparams;
 
 /* Workspace bytes of qlora_adamw_step: 0 with the state in device memory,
@@ -257,6 +260,7 @@ size_t qlora_adamw_workspace_bytes(int64_t n, int state_on_host);
  * c2 = 1 - beta2 in fp32):
  *     m' = b1 m + c1 g,  v' = b2 v + c2 (g g)
  *     p' = p - lr ((m' / bc1) / (sqrt(v' / bc2) + eps) + wd p)
+ * with bc1, bc2 the bias corrections of hp->step (see qlora_adamw_hparams).
  * Results are bit-identical to that definition wherever the state lives.
  *   param, grad   fp32 [n] (device); param and the state are updated in place
  *   m, v          fp32 [n]: device memory (state_on_host = 0) or pinned host
@@ -266,8 +270,8 @@ size_t qlora_adamw_workspace_bytes(int64_t n, int state_on_host);
  *                 the stream has reached this call's end
  *   ws            device workspace of qlora_adamw_workspace_bytes() bytes
  *                 (may be NULL when that is 0)
- * Errors: NULL pointers, n <= 0, misaligned pointers, bias corrections
- * outside (0, 1], beta outside [0, 1), eps < 0, a short workspace.
+ * Errors: NULL pointers, n <= 0, misaligned pointers, step < 1, beta
+ * outside [0, 1), eps < 0, a short workspace.
  */
 int qlora_adamw_step(float *param, const float *grad, float *m, float *v, int64_t n,
                      const qlora_adamw_hparams *hp, int state_on_host, void *ws, size_t ws_bytes,

@@ -43,3 +43,27 @@ def rel_fro(got, ref) -> float:
 def announce(msg: str):
     """Name the case before a GPU step, flushed, so a crash log shows it."""
     print(f"[gpu case] {msg}", flush=True)
+
+
+def max_tile_rel(got, ref, tile=(256, 256)) -> float:
+    """Largest relative Frobenius error over the tiles of a 2-D result (tiles
+    of `tile` rows x columns, clipped at the edges). A wrong tile, column
+    strip or tile edge that holds a tiny share of the whole tensor's energy
+    still fails this bound. A tile whose reference is zero counts as 0 if the
+    result is zero there too, else as infinite."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.ndim == 1:
+        got, ref = got[None, :], ref[None, :]
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    tr, tc = tile
+    worst = 0.0
+    for r0 in range(0, ref.shape[0], tr):
+        for c0 in range(0, ref.shape[1], tc):
+            g = got[r0:r0 + tr, c0:c0 + tc]
+            f = ref[r0:r0 + tr, c0:c0 + tc]
+            den = np.linalg.norm(f)
+            num = np.linalg.norm(g - f)
+            e = (0.0 if num == 0.0 else float("inf")) if den == 0.0 else float(num / den)
+            worst = max(worst, e)
+    return worst

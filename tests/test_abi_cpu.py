@@ -100,7 +100,7 @@ def test_merge_rejects_bad_arguments():
 
 def test_adamw_rejects_bad_arguments():
     ref = ctypes.byref
-    hp = qb._AdamwHparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 0.1, 0.001)
+    hp = qb._AdamwHparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
     assert qb.qlora_adamw_workspace_bytes(1000, False) == 0
     assert qb.qlora_adamw_workspace_bytes(1001, True) == 2 * 1024 * 4
     assert qb.qlora_adamw_workspace_bytes(0, True) == 0
@@ -109,10 +109,10 @@ def test_adamw_rejects_bad_arguments():
     assert step(FAKE, FAKE, FAKE, FAKE, 0, ref(hp), 0, None, 0, None) == -2
     assert step(FAKE, FAKE + 4, FAKE, FAKE, 64, ref(hp), 0, None, 0, None) == -6
     assert step(FAKE, FAKE, FAKE, FAKE, 64, ref(hp), 1, None, 0, None) == -4
-    bad = qb._AdamwHparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 0.0, 0.001)
+    bad = qb._AdamwHparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 0)
     assert step(FAKE, FAKE, FAKE, FAKE, 64, ref(bad), 0, None, 0, None) == -2
-    assert "bias corrections" in qb.qlora_last_error()
-    bad = qb._AdamwHparams(1e-3, 1.0, 0.999, 1e-8, 0.0, 0.1, 0.001)
+    assert "step must be >= 1" in qb.qlora_last_error()
+    bad = qb._AdamwHparams(1e-3, 1.0, 0.999, 1e-8, 0.0, 1)
     assert step(FAKE, FAKE, FAKE, FAKE, 64, ref(bad), 0, None, 0, None) == -2
 
 
@@ -125,6 +125,10 @@ def test_sizes_reject_bad_shapes():
     assert qb.qlora_linear_workspace_bytes(16, 256, 256, 300) == 0   # r out of range
     assert qb.qlora_linear_workspace_bytes(16, 256, 256, 8) > 0
     assert qb.qlora_linear_workspace_bytes(1, 11008, 4096, 64) > 0
+    # N and K above 2^23 would overflow the 32-bit tile offsets
+    assert qb.qlora_linear_workspace_bytes(16, 64, (1 << 23) + 64, 8) == 0
+    assert qb.qlora_linear_workspace_bytes(16, (1 << 23) + 64, 64, 8) == 0
+    assert qb.qlora_linear_workspace_bytes(16, 64, 1 << 23, 8) > 0
 
 
 def test_quantize_workspace_covers_partials():
@@ -185,3 +189,36 @@ def test_linear_rejects_bad_arguments():
     assert b(FAKE, FAKE, 16, ref(w), None, None, 0, 2.0, FAKE, FAKE, None, FAKE, big, None) == -2
     assert b(None, FAKE, 16, ref(w), FAKE, FAKE, 8, 2.0, FAKE, FAKE, FAKE, FAKE, big, None) == -1
     assert "dY, X and dX" in qb.qlora_last_error()
+
+
+@pytest.mark.parametrize("rows,cols", [(64, (1 << 23) + 64), ((1 << 23) + 64, 64)])
+def test_linear_rejects_dims_past_32bit_tile_offsets(rows, cols):
+    """K (forward operand rows) or N (input-gradient operand rows) above 2^23:
+    255 rows of the operand tile would pass 2^32 bytes of offset. Both calls
+    must fail on the host with QLORA_ERR_SHAPE and launch nothing (the
+    pointers are fake)."""
+    ref = ctypes.byref
+    w = _weight(rows, cols)
+    big = 1 << 40
+    assert lib.qlora_linear_fwd(FAKE, 16, ref(w), FAKE, FAKE, 8, 2.0, FAKE, FAKE, big, None) == -2
+    assert "must not exceed 8388608" in qb.qlora_last_error()
+    assert lib.qlora_linear_bwd(FAKE, FAKE, 16, ref(w), FAKE, FAKE, 8, 2.0, FAKE, FAKE, FAKE, FAKE, big,
+                                None) == -2
+
+
+def test_binding_rejects_host_tensors_before_any_call():
+    """The binding checks device, dtype and shape before calling the library:
+    host (CPU) tensors are refused with TypeError, a dangling adapter factor
+    with ValueError."""
+    torch = pytest.importorskip("torch")
+    W = qb.NF4Weight(64, 64, torch.zeros(2048, dtype=torch.uint8), torch.zeros(64, dtype=torch.int8),
+                     torch.zeros(1), torch.zeros(1))
+    X = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        qb.qlora_linear_fwd(X, W)
+    with pytest.raises(TypeError):
+        qb.qlora_linear_bwd(X, X, W)
+    with pytest.raises(TypeError):
+        qb.qlora_nf4_quantize(torch.zeros((64, 64)))
+    with pytest.raises(TypeError):
+        qb.qlora_adamw_step(torch.zeros(8), torch.zeros(8), torch.zeros(8), torch.zeros(8), 1, 1e-3)

@@ -125,7 +125,8 @@ def linear_case(qb, fmt, M, N, K, r, seed):
 @pytest.mark.parametrize("r", [0, 72])
 def test_linear_fwd_bwd(qb, fmt, M, K, r):
     """Decode path (M <= 32; K = 2240: several K splits, absmax bytes not
-    dword aligned) and the large-tile path (M > 32), forward and backward."""
+    dword aligned) and the large-tile path (M > 32) forward, and the backward
+    at every M (small M runs the large-tile kernels on partial tiles)."""
     N = 320
     wl, q, What = linear_case(qb, fmt, M, N, K, r, seed=fmt * 1000 + M * 10 + r)
     X = gu.dev_bf16(wl.X)
@@ -134,19 +135,22 @@ def test_linear_fwd_bwd(qb, fmt, M, K, r):
     B = gu.dev_f32(wl.B) if r else None
     gu.announce(f"fwd fmt={fmt} M={M} K={K} r={r}")
     Y = gu.host_bf16_f32(qb.qlora_linear_fwd(X, q, A, B, wl.s))
-    e = gu.rel_fro(Y, linear.forward(X32, What, wl.A, wl.B, wl.s))
+    Yr = linear.forward(X32, What, wl.A, wl.B, wl.s)
+    e = gu.rel_fro(Y, Yr)
     assert e <= TOL and e <= REG, f"fmt {fmt} M={M} r={r}: fwd {e}"
-    if M > 32:
-        dY, dY32 = gu.dev_bf16(wl.dY), synth.bf16_to_f32(wl.dY)
-        gu.announce(f"bwd fmt={fmt} M={M} K={K} r={r}")
-        dX, dA, dB = qb.qlora_linear_bwd(dY, X, q, A, B, wl.s)
-        rX, rA, rB = linear.backward(dY32, X32, What, wl.A, wl.B, wl.s)
-        errs = {"dX": gu.rel_fro(gu.host_bf16_f32(dX), rX)}
-        if r:
-            errs["dA"] = gu.rel_fro(gu.host(dA), rA)
-            errs["dB"] = gu.rel_fro(gu.host(dB), rB)
-        for k, v in errs.items():
-            assert v <= TOL and v <= REG, f"fmt {fmt} M={M} r={r}: {k} {v}"
+    assert gu.max_tile_rel(Y, Yr) <= TOL, f"fmt {fmt} M={M} r={r}: fwd worst tile"
+    dY, dY32 = gu.dev_bf16(wl.dY), synth.bf16_to_f32(wl.dY)
+    gu.announce(f"bwd fmt={fmt} M={M} K={K} r={r}")
+    dX, dA, dB = qb.qlora_linear_bwd(dY, X, q, A, B, wl.s)
+    rX, rA, rB = linear.backward(dY32, X32, What, wl.A, wl.B, wl.s)
+    pairs = {"dX": (gu.host_bf16_f32(dX), rX)}
+    if r:
+        pairs["dA"] = (gu.host(dA), rA)
+        pairs["dB"] = (gu.host(dB), rB)
+    for k, (got, ref) in pairs.items():
+        v = gu.rel_fro(got, ref)
+        assert v <= TOL and v <= REG, f"fmt {fmt} M={M} r={r}: {k} {v}"
+        assert gu.max_tile_rel(got, ref) <= TOL, f"fmt {fmt} M={M} r={r}: {k} worst tile"
 
 
 @pytest.mark.parametrize("fmt", list(FORMATS))
@@ -180,5 +184,7 @@ def test_decode_shapes_full(qb, fmt, name):
     What = nf4.dequantize(oracle_quant(w32, fmt), codebook(fmt))
     gu.announce(f"fwd {name} fmt={fmt}")
     Y = gu.host_bf16_f32(qb.qlora_linear_fwd(gu.dev_bf16(wl.X), q, gu.dev_f32(wl.A), gu.dev_f32(wl.B), wl.s))
-    e = gu.rel_fro(Y, linear.forward(synth.bf16_to_f32(wl.X), What, wl.A, wl.B, wl.s))
+    Yr = linear.forward(synth.bf16_to_f32(wl.X), What, wl.A, wl.B, wl.s)
+    e = gu.rel_fro(Y, Yr)
     assert e <= REG, f"{name} fmt {fmt}: {e}"
+    assert gu.max_tile_rel(Y, Yr) <= TOL, f"{name} fmt {fmt}: worst tile"

@@ -3,7 +3,9 @@
 Bar (relative Frobenius error against the oracle evaluated on the exact
 inputs: bf16 X and dY, the oracle's fp32 dequantized weight, fp32 A and B):
 2e-2 for Y, dX, dA and dB. A tighter regression bound (5e-3) is asserted too,
-since bf16 operand rounding gives about 1e-3. With X = I and no adapter the
+since bf16 operand rounding gives about 1e-3. The same 2e-2 bar holds on every
+256 x 256 tile of each result (gpu_util.max_tile_rel), so a wrong tile, strip
+or tile edge cannot hide in the whole tensor's norm. With X = I and no adapter the
 output must be bf16(W-hat^T) bit for bit (one nonzero product per output);
 the same holds for dX with dY = I.
 """
@@ -62,6 +64,8 @@ def _fwd(qb, c, label):
     e = gu.rel_fro(Yg, Yr)
     assert e <= TOL, f"{label}: fwd rel err {e}"
     assert e <= REG, f"{label}: fwd rel err {e} above regression bound"
+    et = gu.max_tile_rel(Yg, Yr)
+    assert et <= TOL, f"{label}: fwd worst tile rel err {et}"
     return e
 
 
@@ -70,13 +74,17 @@ def _bwd(qb, c, label):
     gu.announce(f"bwd {label} M={wl.M} N={wl.N} K={wl.K} r={wl.r}")
     dX, dA, dB = qb.qlora_linear_bwd(c.dY, c.X, c.q, c.A, c.B, wl.s)
     rX, rA, rB = linear.backward(c.dY32, c.X32, c.What, wl.A, wl.B, wl.s)
-    errs = {"dX": gu.rel_fro(gu.host_bf16_f32(dX), rX)}
+    pairs = {"dX": (gu.host_bf16_f32(dX), rX)}
     if wl.r > 0:
-        errs["dA"] = gu.rel_fro(gu.host(dA), rA)
-        errs["dB"] = gu.rel_fro(gu.host(dB), rB)
-    for k, e in errs.items():
+        pairs["dA"] = (gu.host(dA), rA)
+        pairs["dB"] = (gu.host(dB), rB)
+    errs = {}
+    for k, (got, ref) in pairs.items():
+        e = errs[k] = gu.rel_fro(got, ref)
         assert e <= TOL, f"{label}: {k} rel err {e}"
         assert e <= REG, f"{label}: {k} rel err {e} above regression bound"
+        et = gu.max_tile_rel(got, ref)
+        assert et <= TOL, f"{label}: {k} worst tile rel err {et}"
     return errs
 
 
@@ -183,6 +191,7 @@ def test_mlp65b_sampled(qb, cb, name):
     Yr = linear.forward(X32[rows], What, wl.A, wl.B, wl.s)
     e = gu.rel_fro(Y[rows], Yr)
     assert e <= REG, f"{name}: fwd {e}"
+    assert gu.max_tile_rel(Y[rows], Yr) <= TOL, f"{name}: fwd worst tile"
     gu.announce(f"bwd {name}")
     dX, dA, dB = qb.qlora_linear_bwd(dY, X, q, A, B, wl.s)
     dH = wl.s * (dY32.astype(np.float64) @ wl.B.astype(np.float64))
@@ -193,6 +202,7 @@ def test_mlp65b_sampled(qb, cb, name):
                         ("dB", gu.host(dB), rB)):
         e = gu.rel_fro(got, ref)
         assert e <= REG, f"{name}: {k} {e}"
+        assert gu.max_tile_rel(got, ref) <= TOL, f"{name}: {k} worst tile"
 
 
 @pytest.mark.parametrize("M", [16, 300])
@@ -241,3 +251,33 @@ def test_graph_replays_match_eager(qb, cb, M):
         torch.cuda.synchronize()
         for name, a, b in zip(("codes", "absmax_q", "dq_scale", "dq_mean", "Wd", "Y", "dX", "dA", "dB"), outs, eager):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager result"
+
+
+def test_binding_rejects_mismatched_tensors(qb, cb):
+    """Wrong shapes, dtypes or a missing factor are refused by the binding
+    with an exception before anything is launched: the C ABI takes bare
+    pointers and could not tell a short tensor from a long one."""
+    import torch
+    wl = synth.make_linear_workload("guard", M=8, N=128, K=192, r=8, alpha=16.0, seed=5)
+    c = Case(qb, wl, cb)
+    bad_X = torch.zeros((8, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        qb.qlora_linear_fwd(bad_X, c.q, c.A, c.B, wl.s)
+    with pytest.raises(ValueError):
+        qb.qlora_linear_fwd(c.X, c.q, c.A[:, :64].contiguous(), c.B, wl.s)
+    with pytest.raises(ValueError):
+        qb.qlora_linear_fwd(c.X, c.q, c.A, None, wl.s)
+    with pytest.raises(TypeError):
+        qb.qlora_linear_fwd(c.X, c.q, c.A.double(), c.B, wl.s)
+    with pytest.raises(ValueError):
+        qb.qlora_linear_fwd(c.X, c.q, c.A, c.B, wl.s, out=torch.empty((8, 64), dtype=torch.bfloat16,
+                                                                      device="cuda"))
+    with pytest.raises(ValueError):
+        qb.qlora_linear_bwd(c.dY[:, :64].contiguous(), c.X, c.q, c.A, c.B, wl.s)
+    with pytest.raises(ValueError):
+        qb.qlora_linear_bwd(c.dY, c.X, c.q, c.A, c.B, wl.s,
+                            outs=(torch.empty((8, 192), dtype=torch.bfloat16, device="cuda"),
+                                  torch.empty((8, 100), device="cuda"), torch.empty((128, 8), device="cuda")))
+    with pytest.raises(ValueError):
+        qb.qlora_nf4_dequantize(c.q, torch.float32, out=torch.empty((64, 192), device="cuda"))
+    torch.cuda.synchronize()

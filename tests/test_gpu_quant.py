@@ -141,3 +141,35 @@ def test_up65b_shape_sampled(qb, cb):
     for r in rows:
         c, _ = nf4.nf4_codes(w32[r], cb)
         assert np.array_equal(codes[r], nf4.pack_codes(c)), f"row {r}"
+
+
+@pytest.mark.parametrize("rows,cols", [(4096, 5120), (11008, 4096), (8192, 8192)])
+def test_dq_mean_single_chunk_tree(qb, cb, rows, cols):
+    """Tensors of 1025 to 8192 DQ blocks (nd = 1280, 2752, 4096), whose mean
+    is completed in one chunk of the fp64 tree with register runs of 8 and
+    16 partials: codes, DQ codes, DQ scales, the mean and both dequantized
+    outputs compared in full. 11008 x 4096 is the 7B MLP weight, 8192 x 8192
+    the 65B attention projection of the whole-model stack."""
+    rng = np.random.default_rng(rows + cols)
+    bits = synth.normal_bf16(rng, (rows, cols), 0.02)
+    _check_quant(qb, gu.dev_bf16(bits), synth.bf16_to_f32(bits), (rows, cols), cb, f"{rows}x{cols}")
+
+
+def test_dq_mean_single_chunk_run32(qb, cb):
+    """8192 x 11008 (nd = 5504, register runs of 32 partials in the single
+    chunk): the mean, DQ codes and DQ scales in full, the NF4 codes on
+    sampled rows."""
+    rows, cols = 8192, 11008
+    rng = np.random.default_rng(5504)
+    bits = synth.normal_bf16(rng, (rows, cols), 0.02)
+    w32 = synth.bf16_to_f32(bits)
+    gu.announce(f"quantize {rows}x{cols}")
+    q = qb.qlora_nf4_quantize(gu.dev_bf16(bits))
+    qd, scale, mu = nf4.double_quantize(nf4.block_absmax(w32))
+    assert np.array_equal(gu.host(q.absmax_q), qd)
+    assert np.array_equal(gu.host(q.dq_scale).view(np.uint32), scale.view(np.uint32))
+    assert gu.host(q.dq_mean).view(np.uint32)[0] == np.float32(mu).view(np.uint32)
+    codes = gu.host(q.codes).reshape(rows, cols // 2)
+    for r in rng.choice(rows, 32, replace=False):
+        c, _ = nf4.nf4_codes(w32[r], cb)
+        assert np.array_equal(codes[r], nf4.pack_codes(c)), f"row {r}"
