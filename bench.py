@@ -239,7 +239,7 @@ def main():
     W, X, A, B, dY = d_bf16(wl.W), d_bf16(wl.X), d_f32(wl.A), d_f32(wl.B), d_bf16(wl.dY)
     q = qb.NF4Weight.empty(N, K, dev)
     ws_q = torch.empty(qb.qlora_nf4_quantize_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
-    ws_l = torch.empty(qb.qlora_linear_workspace_bytes(M, N, K, r), dtype=torch.uint8, device=dev)
+    ws_l = qb.linear_workspace(M, N, K, r, dev)
     Wdq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
@@ -431,7 +431,7 @@ def main():
             Bd = [d_f32(w2.B) for _ in range(Rd)]
             Xd = d_bf16(w2.X)
             Yd = torch.empty((Mx, Nx), dtype=torch.bfloat16, device=dev)
-            wsd = torch.empty(qb.qlora_linear_workspace_bytes(Mx, Nx, Kx, r), dtype=torch.uint8, device=dev)
+            wsd = qb.linear_workspace(Mx, Nx, Kx, r, dev)
             R_saved, R = R, Rd
             # one untimed call first: a kernel's first launch also loads its code
             qb.qlora_linear_fwd(Xd, qd[0], Ad[0], Bd[0], w2.s, ws=wsd, out=Yd)
@@ -494,7 +494,7 @@ def main():
         Wg = d_bf16(wg.W)
         Xg = d_bf16(wg.X)
         Yg = torch.empty((wg.M, wg.N), dtype=torch.bfloat16, device=dev)
-        wsg = torch.empty(qb.qlora_linear_workspace_bytes(wg.M, wg.N, wg.K, r), dtype=torch.uint8, device=dev)
+        wsg = qb.linear_workspace(wg.M, wg.N, wg.K, r, dev)
         for fmt, fname in ((qb.QLORA_FMT_NF4_DQ, "nf4_dq"), (qb.QLORA_FMT_NF4, "nf4"),
                            (qb.QLORA_FMT_FP4_DQ, "fp4_dq"), (qb.QLORA_FMT_FP4, "fp4")):
             qf = qb.NF4Weight.empty(N, K, dev, fmt)
@@ -592,7 +592,7 @@ def main():
                           torch.empty((Ml, Kl), dtype=torch.bfloat16, device=dev),
                           torch.empty((r, Kl), dtype=torch.float32, device=dev),
                           torch.empty((Nl, r), dtype=torch.float32, device=dev),
-                          torch.empty(qb.qlora_linear_workspace_bytes(Ml, Nl, Kl, r), dtype=torch.uint8, device=dev)))
+                          qb.linear_workspace(Ml, Nl, Kl, r, dev)))
 
         def layer_step():
             for (ql, Xl, Al, Bl, dYl, Yl, dXl, dAl, dBl, wsl) in projs:
@@ -622,7 +622,7 @@ def main():
             dYm = dev_normal((Mm, Nm), 1.0, seed + 2000)
             Am = dev_normal((r, Km), 0.01, seed + 3000).float()
             Bm = dev_normal((Nm, r), 0.01, seed + 4000).float()
-            wsm = torch.empty(qb.qlora_linear_workspace_bytes(Mm, Nm, Km, r), dtype=torch.uint8, device=dev)
+            wsm = qb.linear_workspace(Mm, Nm, Km, r, dev)
             Ym = torch.empty((Mm, Nm), dtype=torch.bfloat16, device=dev)
             dXm = torch.empty((Mm, Km), dtype=torch.bfloat16, device=dev)
             dAm = torch.empty((r, Km), dtype=torch.float32, device=dev)

@@ -23,7 +23,7 @@ __all__ = [
     "qlora_weight_storage_bytes", "qlora_format_levels", "format_has_dq",
     "QLORA_FMT_NF4_DQ", "QLORA_FMT_NF4", "QLORA_FMT_FP4_DQ", "QLORA_FMT_FP4",
     "qlora_nf4_merge_workspace_bytes", "qlora_nf4_merge",
-    "qlora_adamw_workspace_bytes", "qlora_adamw_step",
+    "qlora_adamw_workspace_bytes", "qlora_adamw_step", "linear_workspace", "LINEAR_SYNC_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora_nf4.so")
@@ -381,13 +381,26 @@ def qlora_adamw_step(param, grad, m, v, step: int, lr: float, beta1: float = 0.9
                                 ws.numel() * ws.element_size() if need else 0, _stream_ptr(param.device)))
 
 
-def _linear_ws(M, N, K, r, device, ws):
+# Bytes of synchronization words at the start of every linear workspace: they
+# must be zero before the workspace's first use (the library leaves them zero).
+LINEAR_SYNC_BYTES = 256 * 1024
+
+
+def linear_workspace(M: int, N: int, K: int, r: int, device):
+    """A workspace for qlora_linear_fwd / qlora_linear_bwd at these sizes,
+    allocated zero-filled (its leading synchronization words must start at
+    zero; every call leaves them zero again)."""
     torch = _torch()
     need = qlora_linear_workspace_bytes(M, N, K, r)
+    if need == 0:
+        raise ValueError(f"invalid linear sizes M={M} N={N} K={K} r={r}")
+    return torch.zeros(need, dtype=torch.uint8, device=device)
+
+
+def _linear_ws(M, N, K, r, device, ws):
     if ws is None:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-    else:
-        _need_ws(ws, device)
+        return linear_workspace(M, N, K, r, device)
+    _need_ws(ws, device)
     return ws
 
 

@@ -1,31 +1,56 @@
-// Skinny-M QLoRA forward (decode):
+// Skinny-M QLoRA forward (decode, M <= 32 rows of X):
 //   Y = X W^T + s (X A^T) B^T
-// with the NF4 + DQ weight streamed from HBM once and decoded on the fly
-// (QLoRA vs ChatGPT page, capability "training pipeline": block-wise
-// dequantization of the 4-bit base in the forward pass; capability "LoRA on
-// the quantized base": a frozen base plus a full-precision adapter).
+// in ONE launch per call, with the 4-bit weight streamed from HBM once and
+// decoded on the fly (QLoRA vs ChatGPT page, capability "training pipeline":
+// block-wise dequantization of the 4-bit base in the forward pass; capability
+// "LoRA on the quantized base": a frozen base plus a full-precision adapter).
 //
-// One pass handles up to 16 rows of X (more rows run as further passes).
-// Two launches per pass:
-//   k_gemv         grid = (column strips of 128) x (K splits of 1024). A wave
-//                  owns 16 output columns. The workgroup first loads its X
-//                  chunk, absmax bytes and DQ constants and stages X and a
-//                  byte table in LDS; then each lane streams the code words of
-//                  its split, two to six super-blocks ahead of their use (the
-//                  stream starts after X is staged, so X is not queued behind
-//                  it). Per 64-element block, a lane maps its code bytes to
-//                  bf16 level pairs (table lookups = MFMA B operands), runs
-//                  v_mfma_f32_16x16x32_bf16 into a temporary and adds
-//                  c_b * temporary to its accumulator: the block scale is
-//                  applied once per block and output, not once per weight.
-//                  The workgroups then form the split partials of H = X A^T.
-//   k_gemv_finish  per output: the fixed-order sum of the split partials plus
-//                  the adapter term bf16(s H) bf16(B)^T (MFMA), rounded to bf16.
-// For M <= 4 (M <= 8) one MFMA spans 4 (2) blocks in block-diagonal row
-// groups (see k_gemv). Within a block the reduction order is free: each lane
-// group takes contiguous code bytes and reads X in the same order. Levels
-// enter the MFMA as bf16 and c_b is applied in fp32, so Y differs from
-// bf16(X bf16(W-hat)^T) at the bf16 operand level.
+// Grid = U adapter workgroups, then S x C weight workgroups.
+//
+// Weight workgroups. Strip s owns 16 T consecutive weight rows (outputs n);
+// its C workgroups split the reduction into chunks whose slice of X fits in
+// LDS (C = 1 whenever all of X fits). The 8 waves of a workgroup take T row
+// tiles of 16 x KS = 8 / T reduction slices. Each lane issues the code loads
+// of its whole slice at once (16 bytes per quad-piece: 128 elements of its
+// row = two 64-blocks; lane group g = lane / 16 holds bytes 16 g .. 16 g + 15,
+// i.e. half g % 2 of block g / 2), then decodes byte by byte through a table
+// of bf16 level pairs in LDS into the B operand of v_mfma_f32_16x16x32_bf16.
+// The A operand is X in block-diagonal form: MFMA rows 0-7 carry X rows
+// 8 mt .. 8 mt + 7 against the lanes of block 0 (lane groups 0, 1), rows 8-15
+// the same X rows against block 1 (lane groups 2, 3), zero elsewhere. An
+// output lane therefore holds only its own block's contribution and scales it
+// by that block's constant c_b after the four MFMAs of the quad-piece: the
+// scale costs one FMA per output and block, not one multiply per weight. The
+// two block halves are added across lanes once at the end, the slices in a
+// fixed order through LDS.
+//
+// Split reduction (C > 1): a workgroup writes its fp32 partial and bumps its
+// strip's arrival counter; the last of the C to arrive sums the C partials in
+// chunk order, resets the counter and finishes the strip.
+//
+// Adapter workgroups. Unit u = (16 adapter columns, a range of the
+// reduction) forms that piece of H = X A^T with the fp32 rows of A rounded to
+// bf16 as MFMA operands, writes it, and marks it published in one flag word
+// per strip. A strip's finisher waits for its U flags (bounded), resets them,
+// sums the H pieces in a fixed order, and adds bf16(s H) bf16(B)^T on the
+// MFMA to its outputs before rounding Y to bf16.
+//
+// Cross-workgroup data (partials, H pieces, counters, flags) is written with
+// write-through stores (agent-scope relaxed atomic stores, sc1), made
+// complete with a wait on every outstanding memory access before the
+// counter or flag that announces it, and read with agent-scope atomic loads
+// (sc1): no L2 write-back or invalidate is issued, since those walk a whole
+// XCD's L2. Counters and flags live at the start of the workspace and are
+// zero between calls: every word a call raises is cleared again by the call
+// (the counter by its strip's last arrival, a flag by its strip's finisher).
+// Waits are bounded; a wait that runs out sets an error word and the call
+// finishes (its output is then wrong). Adapter workgroups come first in the
+// grid and never wait, so a waiting finisher never holds a slot an adapter
+// workgroup still needs.
+//
+// Numerics: the base enters the MFMA as bf16(level) and c_b is applied in
+// fp32 to each block's partial product; A, B and s H enter as bf16; all
+// accumulation is fp32 in a fixed order, so results are deterministic.
 #include <algorithm>
 
 #include "gemm_core.h"
@@ -35,445 +60,592 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGvRows = 16;                  // rows of X per pass
 constexpr int kGvWaves = 8;
-constexpr int kGvThreads = 64 * kGvWaves;    // 512; two workgroups per CU
-constexpr int kGvCols = 16 * kGvWaves;       // output columns per workgroup
-constexpr int kGvMaxBlocks = 16;             // most 64-element blocks per split
-constexpr int kGvChunk = kGvMaxBlocks * kBlock;
-constexpr int kGvXStride = kGvChunk + 8;     // bf16; +16 bytes keeps b128 reads conflict-free
-constexpr int kLutCopies = 32;               // one table copy per LDS bank: conflict-free lookups
-constexpr int kFinWaves = 8;                 // finish kernel: 128 columns per workgroup
-constexpr int kFinThreads = 64 * kFinWaves;
-constexpr int kFinCols = 16 * kFinWaves;
+constexpr int kGvThreads = 64 * kGvWaves;
+constexpr int kLutCopies = 16;                  // table copies: lanes 16 apart share one
+constexpr int kLutBytes = 256 * kLutCopies * 4;  // 16 KB
+constexpr int kScaleMax = 4096;                  // block constants of a workgroup's region, fp32 in LDS
+constexpr int kScaleBytes = kScaleMax * 4;       // 16 KB
+constexpr int kXOffset = kLutBytes + kScaleBytes;  // X slice after the table and the constants
+constexpr int kZeroBytes = 8 * 512;              // zero row: the largest A-operand read offset of a slice
+constexpr int kXPad = 8;                         // bf16 per X row in LDS: b128 reads of 8 rows on distinct banks
+constexpr int kXLdsMax = 40 * 1024;              // X slice in LDS: two workgroups per CU (72 KB each)
+constexpr int kMaxNq = 16;                       // quad-pieces per wave slice
+constexpr int kHBlocks = 16;                     // reduction blocks (1024 elements) per adapter step
+constexpr int kMaxUnits = 64;                    // adapter units: a unit's range grows past that
+constexpr int kSpinLimit = 1 << 16;              // polls of about 1 us: a wait gives up after about 65 ms
+constexpr int kStripTarget = 512;                // weight workgroups: two per CU
+constexpr int kGvLdsMax = kXOffset + kXLdsMax + kZeroBytes + 1024;   // dynamic LDS bound of every plan
 
 struct GemvParams {
-  const __bf16 *X;        // [M][K]
-  const uint8_t *codes;   // [N][K/2]
-  const int8_t *absmax_q; // [N*K/64] (with DQ)
-  const float *dq_scale;  // [nd]
-  const float *dq_mean;   // [1]
-  const float *absmax;    // [N*K/64] fp32 block constants (without DQ)
-  const float *A;         // [r][K] fp32, or null when r == 0
-  const float *B;         // [N][r] fp32, or null when r == 0
-  float *part;            // [splits][M][N] fp32
-  float *hpart;           // [splits][M][r] fp32
-  __bf16 *Y;              // [M][N]
-  int64_t M, N, K;        // M <= 16
-  int r, splits;
-  int split_blocks;       // 64-element blocks per split (the last split may have fewer)
+  const __bf16 *X;         // [M][K]
+  const uint8_t *codes;    // [N][K/2]
+  const int8_t *absmax_q;  // [N*K/64] (with DQ)
+  const float *dq_scale;   // [nd]
+  const float *dq_mean;    // [1]
+  const float *absmax;     // [N*K/64] fp32 block constants (without DQ)
+  const float *A;          // [r][K] fp32 (r > 0)
+  const float *B;          // [N][r] fp32 (r > 0)
+  __bf16 *Y;               // [M][N]
+  float *part;             // [S][C][M][16 T] split partials (C > 1)
+  float *hpart;            // [HK][M][rp] pieces of H
+  uint32_t *flags;         // [S][U]
+  uint32_t *ctr;           // [S]
+  uint32_t *err;           // [1]
+  int64_t M, N, K;
+  int r, rp;
   float scale;
+  int T, S, C;             // row tiles per strip, strips, reduction chunks
+  int cq;                  // quad-pieces per chunk (the last may be shorter)
+  int U, HK, hb;           // adapter units: (rp / 16) x HK reduction ranges of hb blocks
+  int hstep;               // blocks per adapter step (16, or 8 when M > 16)
+  int xstride;             // bf16 per X row in LDS
+  int zoff;                // byte offset in LDS of a zero row of kZeroBytes
   Nf4Tables tab;
 };
 
-// Code words of one lane for one super-block (BD consecutive 64-blocks).
-template <int BD> struct CodeWords;
-template <> struct CodeWords<1> {
-  uint2 v;
-  __device__ uint32_t word(int q) const { return q == 0 ? v.x : v.y; }
-  __device__ void load(const uint8_t *p) { v = *reinterpret_cast<const uint2 *>(p); }
-};
-template <> struct CodeWords<2> {
-  uint4 v;
-  __device__ uint32_t word(int q) const { return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w; }
-  __device__ void load(const uint8_t *p) { v = *reinterpret_cast<const uint4 *>(p); }
-};
-template <> struct CodeWords<4> {
-  uint4 v0, v1;
-  __device__ uint32_t word(int q) const {
-    const uint4 &v = q < 4 ? v0 : v1;
-    const int e = q & 3;
-    return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
-  }
-  __device__ void load(const uint8_t *p) {
-    v0 = *reinterpret_cast<const uint4 *>(p);
-    v1 = *reinterpret_cast<const uint4 *>(p + 16);
-  }
-};
+__device__ __forceinline__ void st_wt(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_wt(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_wt(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_wt(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Every memory access this wave issued is complete (stores included).
+__device__ __forceinline__ void wait_all_memory() {
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" ::: "memory");
+}
 
-// One pass of at most 16 / BD rows of X. BD is the number of 64-blocks one
-// MFMA spans: the 16 MFMA rows are BD row groups of 16 / BD rows, and row
-// group b multiplies block b of the super-block while the other rows of the
-// A operand are zero. Lane group g (lane / 16) then always holds 8 BD
-// contiguous code bytes of one block (b = g BD / 4) and one block scale, and
-// its accumulator rows all belong to that block; the row groups are summed
-// across lanes once at the end. BD = 1, 2, 4 serve M <= 16, 8, 4: larger BD
-// reads 16 or 32 contiguous bytes per lane and fewer X fragments.
-// kAligned: K is a multiple of 256, so each lane's absmax bytes are whole dwords.
-// kDq: block scales decoded from int8 codes + DQ; else the stored fp32 constants.
-template <int BD, bool kAligned, bool kDq>
-__global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
-  constexpr int NB = kGvMaxBlocks;
-  constexpr int NS = NB / BD;                       // super-blocks per split
-  constexpr int G = 4 / BD;                         // lane groups per block
-  constexpr int RB = 16 / BD;                       // rows per row group
-  constexpr int NW = 2 * BD;                        // code words (= MFMAs) per lane per super-block
-  constexpr int P = BD == 1 ? 6 : BD == 2 ? 3 : 2;  // super-blocks in flight per lane
-  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * kLutCopies];   // 32 KB
-  __shared__ __attribute__((aligned(16))) __bf16 xs[kGvRows * kGvXStride];
-  __shared__ __attribute__((aligned(16))) float as_[2][kGvChunk];          // two rows of A
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int z = blockIdx.y;
-  const int64_t k0 = static_cast<int64_t>(z) * p.split_blocks * kBlock;
-  const int kc = static_cast<int>(min<int64_t>(p.split_blocks * kBlock, p.K - k0));   // a multiple of 64
-  const int nblk = kc / kBlock;
-  const int M = static_cast<int>(p.M);
-  const int gx = gridDim.x, jr0 = blockIdx.x;
-
-  const int64_t n_raw = static_cast<int64_t>(blockIdx.x) * kGvCols + w * 16 + (lane & 15);
-  const bool n_ok = n_raw < p.N;
-  const int64_t n = n_ok ? n_raw : p.N - 1;
-  const int g = lane >> 4;
-  const int bg = g / G, sub = g % G;               // block of this lane group, part of it
-  const int64_t kb = p.K / kBlock;                 // blocks per weight row (a multiple of 4 if kAligned)
-  const int64_t b0 = n * kb + k0 / kBlock;         // first block of this lane's split
-  const uint8_t *crow = p.codes + b0 * (kBlock / 2) + 8 * BD * sub;
-  // Super-block s covers blocks s BD .. s BD + BD - 1 of the split; blocks past
-  // the end of a short split are clamped to its last block (in bounds, scale
-  // zero), so the load sequence has no branches.
-  auto cptr = [&](int s) { return crow + (kBlock / 2) * min(s * BD + bg, nblk - 1); };
-
-  // ---- global loads, in the order they are waited for: one level, the X
-  // chunk (16-byte pieces in named registers; columns past the end of a short
-  // split are staged as zero, so blocks past the end contribute exactly
-  // nothing), absmax bytes, DQ scales, two rows of A.
-  constexpr int pieces = kGvChunk / 8;
-  static_assert(kGvRows * pieces == 4 * kGvThreads, "X chunk = 4 pieces per thread");
-  const int kpieces = kc / 8, xtotal = M * pieces;
-  uint4 x0, x1, x2, x3;
-#define QNF4_XLOAD(u, v)                                                                        \
-  {                                                                                            \
-    const int i = min(tid + (u) * kGvThreads, xtotal - 1);                                     \
-    const int xm = i / pieces, c = i - xm * pieces;                                            \
-    v = *reinterpret_cast<const uint4 *>(p.X + static_cast<int64_t>(xm) * p.K + k0 + 8 * min(c, kpieces - 1)); \
-  }
-  QNF4_XLOAD(0, x0) QNF4_XLOAD(1, x1) QNF4_XLOAD(2, x2) QNF4_XLOAD(3, x3)
-#undef QNF4_XLOAD
-  // absmax bytes (packed dwords, or one per entry) with DQ; without it the
-  // fp32 constant of this lane's block in each super-block
-  uint32_t am[kDq ? (kAligned ? NB / 4 : NB) : 1];
-  float af[kDq ? 1 : NS];
-  if constexpr (!kDq) {
+// sum_{i < count} src[e_j + i stride] for the E elements e_j = e0 + j estep
+// (those with e_j < elim), each added in index order i = 0, 1, ... The loads
+// of eight terms of all E elements go out together (clamped indices, the
+// extra terms dropped), so a sum costs ceil(count / 8) memory round trips
+// instead of one per term.
+template <int E>
+__device__ __forceinline__ void sum_wt(const float *src, int64_t stride, int count, int e0, int estep, int elim,
+                                       float (&out)[E]) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) af[s] = p.absmax[b0 + min(s * BD + bg, nblk - 1)];
-  } else if constexpr (kAligned) {
-    const uint32_t *ap = reinterpret_cast<const uint32_t *>(p.absmax_q + b0);
+  for (int j = 0; j < E; ++j) out[j] = 0.0f;
+  for (int i0 = 0; i0 < count; i0 += 8) {
+    float t[E][8];
 #pragma unroll
-    for (int i = 0; i < NB / 4; ++i) am[i] = ap[min(i, nblk / 4 - 1)];
-  } else {
+    for (int j = 0; j < E; ++j) {
+      const int e = min(e0 + j * estep, elim - 1);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) am[j] = static_cast<uint8_t>(p.absmax_q[b0 + min(j, nblk - 1)]);
-  }
-  const int64_t d0 = b0 / kDqBlock;                // a split spans at most two DQ blocks
-  const float s0 = kDq ? p.dq_scale[d0] : 0.0f;
-  const float s1 = kDq ? p.dq_scale[(b0 + nblk - 1) / kDqBlock] : 0.0f;
-  const float mu = kDq ? p.dq_mean[0] : 0.0f;
-  // thread t holds A[jr, k0 + 2t .. +1] of rows jr0 and jr0 + gx (last: only
-  // the H partials at the end use them)
-  const int ka = min(2 * tid, kc - 2);
-  auto aload = [&](int jr) {
-    return *reinterpret_cast<const float2 *>(p.A + static_cast<int64_t>(min(jr, p.r - 1)) * p.K + k0 + ka);
-  };
-  float2 a0 = make_float2(0.f, 0.f), a1 = a0;
-  if (jr0 < p.r) {
-    a0 = aload(jr0);
-    a1 = aload(jr0 + gx);
-  }
-
-  // ---- LDS: byte table (entry (b, copy) = (level[b >> 4], level[b & 15]);
-  // thread t writes b = t / 32 + 16 i for i < 16 into copy t % 32: the high
-  // nibble i is a constant and the low nibble t / 32 takes one value per half
-  // wave, so the levels come from kernel arguments without a vector load) and
-  // the X chunk (clamped pieces rewrite their own value)
-  {
-    const float lv_lo = p.tab.lv[2 * w], lv_hi = p.tab.lv[2 * w + 1];
-    const float lv_low = lane < 32 ? lv_lo : lv_hi;   // level[t / 32]
-#pragma unroll
-    for (int i = 0; i < 16; ++i) lut[tid + kGvThreads * i] = pack_bf16x2(p.tab.lv[i], lv_low);
-  }
-#define QNF4_XSTORE(u, v)                                                                       \
-  {                                                                                            \
-    const int i = min(tid + (u) * kGvThreads, xtotal - 1);                                     \
-    const int xm = i / pieces, c = i - xm * pieces;                                            \
-    *reinterpret_cast<uint4 *>(xs + xm * kGvXStride + 8 * c) = c < kpieces ? v : make_uint4(0, 0, 0, 0); \
-  }
-  QNF4_XSTORE(0, x0) QNF4_XSTORE(1, x1) QNF4_XSTORE(2, x2) QNF4_XSTORE(3, x3)
-#undef QNF4_XSTORE
-  __syncthreads();
-
-  // The code stream starts only now: loads issued before the barrier would
-  // queue ahead of, or beside, every workgroup's X chunk and delay it.
-  CodeWords<BD> cw[NS];
-#pragma unroll
-  for (int s = 0; s < P; ++s) cw[s].load(cptr(s));
-  // block scale of this lane's block in each super-block (0 past the end);
-  // formed after the barrier, so that nothing before it waits for the
-  // code words issued behind the DQ scales
-  const float kd0 = __fdiv_rn(s0, 127.0f);
-  const float kd1 = __fdiv_rn(s1, 127.0f);
-  float cs[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int j = s * BD + bg;
-    if constexpr (!kDq) {
-      cs[s] = j < nblk ? af[s] : 0.0f;
-    } else {
-      const float kd = (b0 + j) / kDqBlock == d0 ? kd0 : kd1;
-      int q;
-      if constexpr (kAligned) {
-        uint32_t word = am[0];
-#pragma unroll
-        for (int i = 1; i < NB / 4; ++i) word = (j >> 2) == i ? am[i] : word;
-        q = static_cast<int8_t>(word >> (8 * (j & 3)));
-      } else {
-        uint32_t byte = am[0];
-#pragma unroll
-        for (int i = 1; i < NB; ++i) byte = j == i ? am[i] : byte;
-        q = static_cast<int8_t>(byte);
-      }
-      cs[s] = j < nblk ? __fadd_rn(__fmul_rn(static_cast<float>(q), kd), mu) : 0.0f;
-    }
-  }
-  // ---- decode + MFMA, one super-block at a time, P super-blocks of code
-  // words in flight. The A operand of lane (row rho, group g) is X row
-  // rho % RB when its row group rho / RB is this lane group's block, else 0.
-  const int rho = lane & 15;
-  const bool xact = rho / RB == bg && rho % RB < M;
-  const __bf16 *xrow = xs + (rho % RB) * kGvXStride + kBlock * bg + 16 * BD * sub;
-  const uint32_t *lt = lut + (lane & (kLutCopies - 1));
-  bf16x8 xv[NW];
-#pragma unroll
-  for (int q = 0; q < NW; ++q) xv[q] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  const f32x4 zero = acc;
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    asm volatile("" ::: "memory");   // keep the prefetch distance: no load moves across
-    if (s + P < NS) cw[s + P].load(cptr(s + P));
-    if (s * BD >= nblk) continue;    // uniform: the rest of a short split
-    if (xact) {
-#pragma unroll
-      for (int q = 0; q < NW; ++q) xv[q] = *reinterpret_cast<const bf16x8 *>(xrow + kBlock * BD * s + 8 * q);
-    }
-    f32x4 t = zero;
-#pragma unroll
-    for (int q = 0; q < NW; ++q) {
-      const uint32_t wq = cw[s].word(q);
-      const uint4 wv = make_uint4(lt[(wq & 0xFFu) * kLutCopies], lt[((wq >> 8) & 0xFFu) * kLutCopies],
-                                  lt[((wq >> 16) & 0xFFu) * kLutCopies], lt[(wq >> 24) * kLutCopies]);
-      t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[q], __builtin_bit_cast(bf16x8, wv), t, 0, 0, 0);
+      for (int u = 0; u < 8; ++u) t[j][u] = ld_wt(src + e + static_cast<int64_t>(min(i0 + u, count - 1)) * stride);
     }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(cs[s], t[v], acc[v]);
-  }
-  // Accumulator register v holds MFMA row 4 g + v: row group bg, X row
-  // (4 g + v) % RB. Sum the row groups (lanes 16 and 32 apart), fixed order.
-  if constexpr (BD == 4) {
+    for (int j = 0; j < E; ++j)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] += __shfl_xor(acc[v], 16, 64);
-  }
-  if constexpr (BD >= 2) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] += __shfl_xor(acc[v], 32, 64);
-  }
-  if (n_ok && g < G) {
-    float *out = p.part + static_cast<int64_t>(z) * p.M * p.N + n;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = (4 * g + v) % RB;
-      if (row < M) out[static_cast<int64_t>(row) * p.N] = acc[v];
-    }
-  }
-
-  // ---- split partials of H = X A^T for the adapter rows jr0 + i gx: thread
-  // (row hm, slice sl) forms a 32-long dot product over the chunk, the 32
-  // slices of a row (consecutive lanes) are summed by an xor butterfly. The
-  // first two rows of A were loaded at the start; they are staged only now,
-  // so that nothing before the main loop waits for them.
-  const int hm = tid >> 5, sl = tid & 31;
-  const bool kin = 2 * tid < kc;
-  for (int jp = jr0; jp < p.r; jp += 2 * gx) {
-    const float2 b0v = jp == jr0 ? a0 : aload(jp), b1v = jp == jr0 ? a1 : aload(jp + gx);
-    __syncthreads();   // every wave is past the main loop / the previous pair
-    *reinterpret_cast<float2 *>(&as_[0][2 * tid]) = kin ? b0v : make_float2(0.f, 0.f);
-    *reinterpret_cast<float2 *>(&as_[1][2 * tid]) = kin && jp + gx < p.r ? b1v : make_float2(0.f, 0.f);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int jr = jp + i * gx;
-      if (jr >= p.r) break;
-      const uint4 *xp = reinterpret_cast<const uint4 *>(xs + hm * kGvXStride + 32 * sl);
-      const float4 *ap = reinterpret_cast<const float4 *>(&as_[i][32 * sl]);
-      float acc4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint4 xq = xp[u];
-        const float4 av0 = ap[2 * u], av1 = ap[2 * u + 1];
-        acc4[0] = __builtin_fmaf(av0.x, __uint_as_float(xq.x << 16), acc4[0]);
-        acc4[1] = __builtin_fmaf(av0.y, __uint_as_float(xq.x & 0xFFFF0000u), acc4[1]);
-        acc4[2] = __builtin_fmaf(av0.z, __uint_as_float(xq.y << 16), acc4[2]);
-        acc4[3] = __builtin_fmaf(av0.w, __uint_as_float(xq.y & 0xFFFF0000u), acc4[3]);
-        acc4[0] = __builtin_fmaf(av1.x, __uint_as_float(xq.z << 16), acc4[0]);
-        acc4[1] = __builtin_fmaf(av1.y, __uint_as_float(xq.z & 0xFFFF0000u), acc4[1]);
-        acc4[2] = __builtin_fmaf(av1.z, __uint_as_float(xq.w << 16), acc4[2]);
-        acc4[3] = __builtin_fmaf(av1.w, __uint_as_float(xq.w & 0xFFFF0000u), acc4[3]);
-      }
-      float hsum = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) hsum += __shfl_xor(hsum, o, 64);
-      if (sl == 0 && hm < M) p.hpart[(static_cast<int64_t>(z) * p.M + hm) * p.r + jr] = hsum;
-    }
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u < count) out[j] += t[j][u];
   }
 }
 
-// Y = bf16(sum_z part[z] + bf16(s H) bf16(B)^T), H = sum_z hpart[z].
-// Split partials are summed in index order, in groups of four whose loads are
-// all issued before the first add (clamped indices, zero weight past the end).
-__global__ __launch_bounds__(kFinThreads) void k_gemv_finish(GemvParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 hs[kGvRows * (256 + 8)];
+// X[0:M][k0 : k0 + len) (len a multiple of 64) staged into LDS rows of
+// `stride` bf16, zero from len up to `width` (a multiple of 8): at most XP
+// 16-byte pieces per thread. load() issues the reads (stripes with no piece
+// are skipped as a whole, the rest read a clamped, valid address), store()
+// writes LDS; in between the caller may issue loads that must not be waited
+// for before X (loads complete in issue order).
+template <int XP>
+struct XStage {
+  uint4 v[XP];
+  int pieces, total, len8;
+  __device__ __forceinline__ void load(const __bf16 *X, int64_t K, int M, int64_t k0, int len, int width) {
+    pieces = width / 8;
+    total = M * pieces;
+    len8 = len / 8;
+#pragma unroll
+    for (int u = 0; u < XP; ++u) {
+      if (u * kGvThreads >= total) break;   // uniform
+      const int i = min(static_cast<int>(threadIdx.x) + u * kGvThreads, total - 1);
+      const int m = i / pieces, c = min(i - m * pieces, len8 - 1);
+      v[u] = *reinterpret_cast<const uint4 *>(X + static_cast<int64_t>(m) * K + k0 + 8 * c);
+    }
+  }
+  __device__ __forceinline__ void store(int stride, __bf16 *xs) const {
+#pragma unroll
+    for (int u = 0; u < XP; ++u) {
+      if (u * kGvThreads >= total) break;   // uniform
+      const int i = threadIdx.x + u * kGvThreads;
+      if (i >= total) continue;
+      const int m = i / pieces, c = i - m * pieces;
+      *reinterpret_cast<uint4 *>(xs + m * stride + 8 * c) = c < len8 ? v[u] : make_uint4(0, 0, 0, 0);
+    }
+  }
+};
+// pieces per thread: the weight strips' slice (<= kXLdsMax bytes) and the
+// adapter units' range (M x 64 hstep, at most 32 x 512 or 16 x 1024)
+constexpr int kXPieces = (kXLdsMax / 16 + kGvThreads - 1) / kGvThreads;
+constexpr int kHPieces = 16 * kHBlocks * kBlock / 8 / kGvThreads;
+constexpr int kScalePieces = kScaleMax / kGvThreads;
+
+// Block constants c_b of a workgroup's region (`rows` weight rows from n0 x
+// nblk blocks from blk0) for LDS, element e = row * nblk + block: with DQ
+// c_b = fp32(fp32(q_b k_d) + mean), k_d = fp32(scale_d / 127); without it the
+// stored fp32 constant. Consecutive threads take consecutive elements, so the
+// int8 codes (and the constants) arrive in a few coalesced loads instead of
+// one gather per block and lane. load() issues the reads, store() computes
+// and writes LDS.
+template <bool kDq>
+struct ScaleStage {
+  int q[kScalePieces];
+  float f[kScalePieces];
+  int total;
+  __device__ __forceinline__ void load(const GemvParams &p, int64_t n0, int rows, int64_t kb, int64_t blk0,
+                                       int nblk) {
+    total = rows * nblk;
+#pragma unroll
+    for (int u = 0; u < kScalePieces; ++u) {
+      if (u * kGvThreads >= total) break;   // uniform
+      const int e = min(static_cast<int>(threadIdx.x) + u * kGvThreads, total - 1);
+      const int r = e / nblk, b = e - r * nblk;
+      const int64_t gb = min(n0 + r, p.N - 1) * kb + blk0 + b;
+      if constexpr (kDq) {
+        q[u] = p.absmax_q[gb];
+        f[u] = p.dq_scale[gb / kDqBlock];
+      } else {
+        f[u] = p.absmax[gb];
+      }
+    }
+  }
+  __device__ __forceinline__ void store(float mu, float *cs) const {
+#pragma unroll
+    for (int u = 0; u < kScalePieces; ++u) {
+      if (u * kGvThreads >= total) break;   // uniform
+      const int e = threadIdx.x + u * kGvThreads;
+      if (e >= total) continue;
+      cs[e] = kDq ? __fadd_rn(__fmul_rn(static_cast<float>(q[u]), __fdiv_rn(f[u], 127.0f)), mu) : f[u];
+    }
+  }
+};
+
+// ---------------------------------------------------------------- adapter units
+// Unit u: adapter columns 16 jg .. 16 jg + 15 over the reduction blocks
+// [hk hb, (hk + 1) hb), taken kHBlocks (1024 elements) at a time: X of the
+// range staged in LDS, 32-element steps round robin over the waves, A read as
+// fp32 and rounded to bf16.
+template <int MT16>
+__device__ void adapter_unit(const GemvParams &p, char *smem) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int u = blockIdx.x, jg = u / p.HK, hk = u % p.HK;
+  const int M = static_cast<int>(p.M);
+  const int64_t kb = p.K / kBlock;
+  const int64_t ublk0 = static_cast<int64_t>(hk) * p.hb;
+  const int64_t ublk1 = min<int64_t>(kb, ublk0 + p.hb);
+  __bf16 *xs = reinterpret_cast<__bf16 *>(smem + kXOffset);
+  f32x4 *red = reinterpret_cast<f32x4 *>(smem);   // [8 waves][MT16][64 lanes]
+  constexpr int kSteps = kHBlocks * kBlock / 32 / kGvWaves;   // 32-element steps per wave and range
+  const int j = 16 * jg + (lane & 15), g = lane >> 4;
+  const bool jok = j < p.r;
+  const float *arow = p.A + static_cast<int64_t>(min(j, p.r - 1)) * p.K + 8 * g;
+
+  f32x4 acc[MT16];
+#pragma unroll
+  for (int mt = 0; mt < MT16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t blk0 = ublk0; blk0 < ublk1; blk0 += p.hstep) {
+    const int nblk = static_cast<int>(min<int64_t>(p.hstep, ublk1 - blk0));
+    const int64_t k0 = blk0 * kBlock;
+    const int len = nblk * kBlock, nsteps = len / 32;
+    XStage<kHPieces> xst;
+    xst.load(p.X, p.K, M, k0, len, len);
+    float4 av[kSteps][2];
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+      const int st = min(w + kGvWaves * i, nsteps - 1);
+      av[i][0] = *reinterpret_cast<const float4 *>(arow + k0 + 32 * st);
+      av[i][1] = *reinterpret_cast<const float4 *>(arow + k0 + 32 * st + 4);
+    }
+    __syncthreads();   // the previous range's X is no longer read
+    xst.store(p.xstride, xs);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+      const int st = w + kGvWaves * i;
+      if (st >= nsteps) break;   // uniform
+      const float4 a0 = av[i][0], a1 = av[i][1];
+      const uint4 bw = jok ? make_uint4(pack_bf16x2(a0.x, a0.y), pack_bf16x2(a0.z, a0.w), pack_bf16x2(a1.x, a1.y),
+                                        pack_bf16x2(a1.z, a1.w))
+                           : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int mt = 0; mt < MT16; ++mt) {
+        const int m = 16 * mt + (lane & 15);
+        bf16x8 xv = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        if (m < M) xv = *reinterpret_cast<const bf16x8 *>(xs + m * p.xstride + 32 * st + 8 * g);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8, bw), acc[mt], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT16; ++mt) red[(w * MT16 + mt) * 64 + lane] = acc[mt];
+  __syncthreads();
+  if (w < MT16) {   // wave mt sums the eight waves' tiles of m-tile mt, in wave order
+    const int mt = w;
+    f32x4 v = red[mt * 64 + lane];
+    for (int ww = 1; ww < kGvWaves; ++ww) v += red[(ww * MT16 + mt) * 64 + lane];
+    // lane holds rows 16 mt + 4 (lane / 16) + e of column j
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 16 * mt + 4 * g + e;
+      if (m < M) st_wt(p.hpart + (static_cast<int64_t>(hk) * M + m) * p.rp + j, v[e]);
+    }
+  }
+  wait_all_memory();
+  __syncthreads();
+  // published: one flag per strip
+  for (int s = tid; s < p.S; s += kGvThreads) st_wt(p.flags + static_cast<int64_t>(s) * p.U + u, 1u);
+}
+
+// ------------------------------------------------------------- weight strips
+
+template <int MT, int NQ, bool kDq>
+__global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int MT16 = (MT + 1) / 2;
+  if (static_cast<int>(blockIdx.x) < p.U) {
+    adapter_unit<MT16>(p, smem);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int M = static_cast<int>(p.M);
-  const int r = p.r, splits = p.splits;
-  const int rp = (r + 31) / 32 * 32;
-  const int hstride = rp + 8;
-  const int64_t n_raw = static_cast<int64_t>(blockIdx.x) * kFinCols + w * 16 + (lane & 15);
+  const int T = p.T, KS = kGvWaves / T, RN = 16 * T;
+  const int b = blockIdx.x - p.U;
+  const int s = b / p.C, c = b - s * p.C;
+  const int t = w % T, ks = w / T;
+  const int64_t kb = p.K / kBlock;                        // blocks per weight row
+  const int64_t blk0 = static_cast<int64_t>(c) * 2 * p.cq;  // first block of the chunk
+  const int nblk = static_cast<int>(min<int64_t>(2 * p.cq, kb - blk0));
+  const int nqp = (nblk + 1) / 2;                         // quad-pieces of the chunk
+  const int q0 = ks * nqp / KS, nq = (ks + 1) * nqp / KS - q0;
+  const int ln = lane & 15, g = lane >> 4, half = g >> 1;
+  const int64_t n_raw = static_cast<int64_t>(s) * RN + 16 * t + ln;
   const int64_t n = n_raw < p.N ? n_raw : p.N - 1;
-  const int g = lane >> 4;
-  const int64_t plane = p.M * p.N;
+  const int64_t rowblk = n * kb;
+  uint32_t *lut = reinterpret_cast<uint32_t *>(smem);
+  float *cs = reinterpret_cast<float *>(smem + kLutBytes);   // [RN][nblk] block constants
+  __bf16 *xs = reinterpret_cast<__bf16 *>(smem + kXOffset);
 
-  // Every load that does not depend on another goes out first: B for the
-  // first 64 adapter columns, the first four Y partials, then the H partials.
-  // Columns of B past r are clamped to column r - 1: they meet zeros in bf16(s H).
-  const float *brow = p.B + n * r;
-  auto bload = [&](int j0, float *b) {
+  // ---- prologue: the X slice and the block constants are read, staged in
+  // LDS and published before any code word is requested. They are small and
+  // mostly L2 hits, and issued behind the whole grid's code stream they
+  // would wait for it. Then every code word of the slice is requested at
+  // once, and quad-piece jq waits for its own code words only, so the decode
+  // runs while the rest of the slice streams in. Quad-pieces past the slice
+  // and a second block past the end of the chunk read a clamped, valid block
+  // and are scaled by 0.
+  XStage<kXPieces> xst;
+  xst.load(p.X, p.K, M, blk0 * kBlock, nblk * kBlock, nqp * 128);
+  ScaleStage<kDq> sst;
+  sst.load(p, static_cast<int64_t>(s) * RN, RN, kb, blk0, nblk);
+  const float mu = kDq ? p.dq_mean[0] : 0.0f;
+
+  // ---- the level-pair table, the X slice and the block constants into
+  // LDS. Entry (byte e, copy c) at e * 16 + c holds (level[e >> 4],
+  // level[e & 15]); thread tid writes entries e = tid / 16 + 32 i (copy
+  // tid % 16): high nibble 2 i + tid / 256 (wave-uniform), low nibble
+  // (tid / 16) % 16. The levels are kernel-argument constants picked by
+  // selects: no vector load, which would have to wait behind the code words.
+  {
+    const int lo_i = (tid >> 4) & 15;
+    float lo = p.tab.lv[0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) b[i] = brow[min(j0 + 8 * g + i, r - 1)];
-  };
-  float bA[8], bB[8];
-  if (r > 0) {
-    bload(0, bA);
-    bload(32, bB);
+    for (int i = 1; i < 16; ++i) lo = lo_i == i ? p.tab.lv[i] : lo;
+    const bool odd = (tid >> 8) != 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lut[tid + kGvThreads * i] = pack_bf16x2(odd ? p.tab.lv[2 * i + 1] : p.tab.lv[2 * i], lo);
   }
-  float y0[4][4];
+  xst.store(p.xstride, xs);
+  sst.store(mu, cs);
+  // the zero row the A operand reads where it is zero (inactive lanes)
+  reinterpret_cast<uint2 *>(smem + p.zoff)[tid] = make_uint2(0u, 0u);
+  __syncthreads();
+  auto blk_of = [&](int jq) { return min(2 * (q0 + min(jq, max(nq - 1, 0))) + half, nblk - 1); };
+  uint4 cw[NQ];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t zz = min(u, splits - 1);
+  for (int jq = 0; jq < NQ; ++jq)
+    cw[jq] = *reinterpret_cast<const uint4 *>(p.codes + (rowblk + blk0 + blk_of(jq)) * (kBlock / 2) + 16 * (g & 1));
+
+  // ---- decode + MFMA, quad-piece by quad-piece
+  const float *crow = cs + (16 * t + ln) * nblk;   // this lane's weight row in the region
+  const uint32_t *lt = lut + (lane & (kLutCopies - 1));
+  // A operand: lane (row rho = lane % 16, group g) is X row 8 mt + rho % 8
+  // when rho / 8 == g / 2 (its block), zero otherwise: those lanes read the
+  // zero row, so that every read is one LDS load at an immediate offset
+  const int rho = lane & 15;
+  const bool blk_lane = (rho >> 3) == half;
+  const __bf16 *xzero = reinterpret_cast<const __bf16 *>(smem + p.zoff);
+  const __bf16 *xb[MT];
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      y0[u][v] = p.part[zz * plane + static_cast<int64_t>(min(4 * g + v, M - 1)) * p.N + n];
+  for (int mt = 0; mt < MT; ++mt)
+    xb[mt] = blk_lane && 8 * mt + (lane & 7) < M ? xs + (8 * mt + (lane & 7)) * p.xstride + 32 * g + 128 * q0 : xzero;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma clang loop unroll(full)
+  for (int jq = 0; jq < NQ; ++jq) {
+    if (jq >= nq) continue;   // uniform
+    const int bi = 2 * (q0 + jq) + half;
+    const float cb = bi < nblk ? crow[bi] : 0.0f;
+    f32x4 tq[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) tq[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint4 cv = cw[jq];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t wq = q == 0 ? cv.x : q == 1 ? cv.y : q == 2 ? cv.z : cv.w;
+      const uint4 bv = make_uint4(lt[(wq & 0xFFu) * kLutCopies], lt[((wq >> 8) & 0xFFu) * kLutCopies],
+                                  lt[((wq >> 16) & 0xFFu) * kLutCopies], lt[(wq >> 24) * kLutCopies]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xb[mt] + 128 * jq + 8 * q);
+        tq[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8, bv), tq[mt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(cb, tq[mt][e], acc[mt][e]);
+  }
+  // the two blocks' rows: lanes l and l + 32 hold the same outputs
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[mt][e] += __shfl_xor(acc[mt][e], 32, 64);
+  __syncthreads();   // every wave is done with the table and X
+
+  // ---- slices summed in order through LDS: red[ks][m][RN], then bsum[m][RN]
+  float *red = reinterpret_cast<float *>(smem);
+  float *bsum = red + KS * M * RN;
+  if (lane < 32) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 8 * mt + 4 * g + e;
+        if (m < M) red[(ks * M + m) * RN + 16 * t + ln] = acc[mt][e];
+      }
+  }
+  __syncthreads();
+  for (int i = tid; i < M * RN; i += kGvThreads) {
+    float v = red[i];
+    for (int k2 = 1; k2 < KS; ++k2) v += red[k2 * M * RN + i];
+    bsum[i] = v;
   }
 
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (r > 0) {
-    // bf16(s H) into LDS, two entries per thread per pass, their split
-    // partials loaded together (clamped entries are computed and dropped)
-    const int ne = M * rp;
-    for (int e0 = tid; e0 < ne; e0 += 2 * kFinThreads) {
-      int ie[2], je[2], jc[2];
+  // ---- B rows of the adapter's up projection for the output waves (slice 0),
+  // loaded now so that they travel during the waits below (first 64 columns)
+  float bpre[16];
+  const bool out_wave = ks == 0;
+  if (p.r > 0 && out_wave) {
+    const float *brow = p.B + n * p.r;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int e = min(e0 + t * kFinThreads, ne - 1);
-        ie[t] = e / rp;
-        je[t] = e - ie[t] * rp;
-        jc[t] = min(je[t], r - 1);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bpre[8 * h + i] = brow[min(32 * h + 8 * g + i, p.r - 1)];
+  }
+
+  // ---- split reduction: the last of the strip's C workgroups finishes it
+  if (p.C > 1) {
+    float *mine = p.part + (static_cast<int64_t>(s) * p.C + c) * M * RN;
+    for (int i = tid; i < M * RN; i += kGvThreads) st_wt(mine + i, bsum[i]);
+    wait_all_memory();
+    __shared__ uint32_t arrived;
+    __syncthreads();
+    if (tid == 0) arrived = __hip_atomic_fetch_add(p.ctr + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrived != static_cast<uint32_t>(p.C - 1)) return;
+    if (tid == 0) st_wt(p.ctr + s, 0u);
+    const float *all = p.part + static_cast<int64_t>(s) * p.C * M * RN;
+    for (int i = tid; i < M * RN; i += 4 * kGvThreads) {
+      float v[4];
+      sum_wt<4>(all, static_cast<int64_t>(M) * RN, p.C, i, kGvThreads, M * RN, v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (i + j * kGvThreads < M * RN) bsum[i + j * kGvThreads] = v[j];
+    }
+  }
+
+  // ---- adapter: wait for the U pieces of H, sum them, bf16(s H) into LDS
+  __bf16 *hs = xs;   // [MT16 * 16][rp + 8]
+  const int hstride = p.rp + 8;
+  if (p.r > 0) {
+    if (w == 0) {
+      uint32_t *fl = p.flags + static_cast<int64_t>(s) * p.U;
+      for (int spins = 0;; ++spins) {
+        bool mine = true;
+        for (int u0 = 0; u0 < p.U; u0 += 64)
+          if (u0 + lane < p.U) mine = mine && ld_wt(fl + u0 + lane) != 0u;
+        if (__all(mine)) break;
+        if (spins >= kSpinLimit) {
+          if (lane == 0) atomicOr(p.err, 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
       }
-      float v[2] = {0.0f, 0.0f};
-      for (int z0 = 0; z0 < splits; z0 += 4) {
-        float gq[2][4];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            gq[t][u] = p.hpart[(static_cast<int64_t>(min(z0 + u, splits - 1)) * p.M + ie[t]) * r + jc[t]];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) v[t] += z0 + u < splits ? gq[t][u] : 0.0f;
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        if (e0 + t * kFinThreads < ne)
-          hs[ie[t] * hstride + je[t]] = static_cast<__bf16>(je[t] < r ? p.scale * v[t] : 0.0f);
+      for (int u0 = 0; u0 < p.U; u0 += 64)
+        if (u0 + lane < p.U) st_wt(fl + u0 + lane, 0u);
     }
     __syncthreads();
-    const __bf16 *hrow = hs + (lane & 15) * hstride + 8 * g;   // rows >= M feed unstored outputs
-    auto mma = [&](int j0, const float *b) {
-      const uint4 bv = make_uint4(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]), pack_bf16x2(b[4], b[5]),
-                                  pack_bf16x2(b[6], b[7]));
-      const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(hrow + j0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
-    };
-    mma(0, bA);
-    if (rp > 32) mma(32, bB);
-    for (int j0 = 64; j0 < rp; j0 += 32) {
-      float b[8];
-      bload(j0, b);
-      mma(j0, b);
+    const int nh = M * p.rp;   // H[m][j], m < M
+    for (int i = tid; i < 16 * MT16 * p.rp; i += 2 * kGvThreads) {
+      float v[2];
+      sum_wt<2>(p.hpart, static_cast<int64_t>(nh), p.HK, i, kGvThreads, nh, v);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = i + j * kGvThreads;
+        if (e >= 16 * MT16 * p.rp) continue;
+        const int m = e / p.rp, jj = e - m * p.rp;
+        hs[m * hstride + jj] = static_cast<__bf16>(e < nh && jj < p.r ? p.scale * v[j] : 0.0f);
+      }
     }
   }
+  __syncthreads();
 
-  float y[4];
+  // ---- outputs: waves of slice 0 take their row tile; adapter on the MFMA
+  if (!out_wave) return;
+  f32x4 ad[MT16];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    y[v] = 0.0f;
+  for (int mt = 0; mt < MT16; ++mt) ad[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // 32 adapter columns j0 .. j0 + 31: B row values bv (this lane's 8 of them)
+  auto adapter_mma = [&](int j0, const float *bv) {
+    uint32_t wv[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) y[v] += u < splits ? y0[u][v] : 0.0f;
-  }
-  for (int z0 = 4; z0 < splits; z0 += 4) {
-    float gq[4][4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t zz = min(z0 + u, splits - 1);
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        gq[u][v] = p.part[zz * plane + static_cast<int64_t>(min(4 * g + v, M - 1)) * p.N + n];
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + 8 * g + 2 * i;
+      wv[i] = pack_bf16x2(j < p.r ? bv[2 * i] : 0.0f, j + 1 < p.r ? bv[2 * i + 1] : 0.0f);
     }
+    const uint4 bw = make_uint4(wv[0], wv[1], wv[2], wv[3]);
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
+    for (int mt = 0; mt < MT16; ++mt) {
+      const bf16x8 hv = *reinterpret_cast<const bf16x8 *>(hs + (16 * mt + ln) * hstride + j0 + 8 * g);
+      ad[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, __builtin_bit_cast(bf16x8, bw), ad[mt], 0, 0, 0);
+    }
+  };
+  if (p.r > 0) {
+    adapter_mma(0, bpre);
+    if (p.rp > 32) adapter_mma(32, bpre + 8);
+    const float *brow = p.B + n * p.r;
+    for (int j0 = 64; j0 < p.rp; j0 += 32) {
+      float bvf[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) y[v] += z0 + u < splits ? gq[u][v] : 0.0f;
+      for (int i = 0; i < 8; ++i) bvf[i] = brow[min(j0 + 8 * g + i, p.r - 1)];
+      adapter_mma(j0, bvf);
+    }
   }
   if (n_raw >= p.N) return;
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
-    if (4 * g + v < M) p.Y[static_cast<int64_t>(4 * g + v) * p.N + n] = static_cast<__bf16>(y[v] + acc[v]);
+  for (int mt = 0; mt < MT16; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 16 * mt + 4 * g + e;
+      if (m < M) p.Y[static_cast<int64_t>(m) * p.N + n] = static_cast<__bf16>(bsum[m * RN + 16 * t + ln] + ad[mt][e]);
+    }
 }
 
-// Splits of K: kGvMaxBlocks blocks each (the last one may be shorter).
-struct GemvSplit {
-  int splits, blocks;
+// ------------------------------------------------------------------ planning
+
+struct GemvPlan {
+  int T, S, C, cq, KS, nq_max;
+  int U, HK, hb, hstep, rp;
+  int xstride, zoff;
+  size_t lds;
 };
-GemvSplit gemv_split(int64_t N, int64_t K) {
-  (void)N;
-  return {static_cast<int>(ceil_div(K / kBlock, kGvMaxBlocks)), kGvMaxBlocks};
-}
 
-template <int BD>
-void launch_stream(bool aligned, bool dq, dim3 grid, hipStream_t s, const GemvParams &p) {
-  if (dq) {
-    if (aligned) hipLaunchKernelGGL((k_gemv<BD, true, true>), grid, dim3(kGvThreads), 0, s, p);
-    else hipLaunchKernelGGL((k_gemv<BD, false, true>), grid, dim3(kGvThreads), 0, s, p);
-  } else {
-    if (aligned) hipLaunchKernelGGL((k_gemv<BD, true, false>), grid, dim3(kGvThreads), 0, s, p);
-    else hipLaunchKernelGGL((k_gemv<BD, false, false>), grid, dim3(kGvThreads), 0, s, p);
+GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int r) {
+  GemvPlan pl{};
+  const int64_t kb = K / kBlock;
+  const int64_t qk = (kb + 1) / 2;                 // quad-pieces per row
+  const int Mi = static_cast<int>(M);
+  // largest chunk (quad-pieces) whose X slice fits
+  const int64_t cq_x = std::max<int64_t>(1, (kXLdsMax / (2 * Mi) - kXPad) / 128);
+  pl.cq = static_cast<int>(std::min<int64_t>(qk, cq_x));
+  pl.C = static_cast<int>(ceil_div(qk, pl.cq));
+  pl.cq = static_cast<int>(ceil_div(qk, pl.C));   // even out the chunks
+  const int64_t tiles16 = N / 16;
+  pl.T = 1;
+  while (pl.T < 8 && ceil_div(tiles16, pl.T) * pl.C > kStripTarget) pl.T *= 2;
+  pl.KS = kGvWaves / pl.T;
+  // the slices of a chunk must fit the unrolled code loads, and a
+  // workgroup's block constants the LDS array
+  while (ceil_div(pl.cq, pl.KS) > kMaxNq || 16 * pl.T * 2 * pl.cq > kScaleMax) {
+    pl.C *= 2;
+    pl.cq = static_cast<int>(ceil_div(qk, pl.C));
+    pl.C = static_cast<int>(ceil_div(qk, pl.cq));
   }
+  pl.S = static_cast<int>(ceil_div(tiles16, pl.T));
+  const int nq = static_cast<int>(ceil_div(pl.cq, pl.KS));
+  pl.nq_max = nq <= 4 ? 4 : nq <= 8 ? 8 : nq <= 12 ? 12 : 16;
+  pl.rp = r > 0 ? static_cast<int>(ceil_div(r, 32) * 32) : 0;
+  if (r > 0) {
+    const int jgroups = pl.rp / 16;
+    const int hk_max = std::max(1, kMaxUnits / jgroups);
+    pl.hb = static_cast<int>(kHBlocks * ceil_div(ceil_div(kb, kHBlocks), hk_max));
+    pl.HK = static_cast<int>(ceil_div(kb, pl.hb));
+    pl.U = jgroups * pl.HK;
+  }
+  pl.hstep = M <= 16 ? kHBlocks : kHBlocks / 2;   // adapter step: X of M x 64 hstep in LDS
+  const int xw = std::max<int>(pl.cq * 128, pl.hstep * kBlock);
+  pl.xstride = xw + kXPad;
+  const int mt16 = static_cast<int>(ceil_div(M, 16));
+  const size_t xbytes = static_cast<size_t>(M) * pl.xstride * 2;
+  const size_t hbytes = static_cast<size_t>(16 * mt16) * (pl.rp + 8) * 2;
+  pl.zoff = static_cast<int>(align_up(kXOffset + std::max(xbytes, hbytes), 16));
+  pl.lds = pl.zoff + kZeroBytes;
+  return pl;   // pl.lds <= kGvLdsMax: X slice <= kXLdsMax, adapter X <= 32 x 520 x 2, H <= 32 x 264 x 2
 }
 
-size_t part_bytes(int64_t N, int64_t K) {
-  return align_up(static_cast<size_t>(gemv_split(N, K).splits * kGvRows * N) * sizeof(float), 256);
+// Dynamic LDS above 64 KB must be allowed per kernel, once.
+template <int MT, int NQ, bool kDq>
+void launch_one(unsigned grid, size_t lds, hipStream_t s, const GemvParams &p) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv<MT, NQ, kDq>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kGvLdsMax);
+  (void)attr;
+  hipLaunchKernelGGL((k_gemv<MT, NQ, kDq>), dim3(grid), dim3(kGvThreads), lds, s, p);
+}
+
+template <int MT, int NQ>
+void launch_mt_nq(bool dq, unsigned grid, size_t lds, hipStream_t s, const GemvParams &p) {
+  if (dq) launch_one<MT, NQ, true>(grid, lds, s, p);
+  else launch_one<MT, NQ, false>(grid, lds, s, p);
+}
+
+template <int MT>
+void launch_mt(int nq, bool dq, unsigned grid, size_t lds, hipStream_t s, const GemvParams &p) {
+  if (nq <= 4) launch_mt_nq<MT, 4>(dq, grid, lds, s, p);
+  else if (nq <= 8) launch_mt_nq<MT, 8>(dq, grid, lds, s, p);
+  else if (nq <= 12) launch_mt_nq<MT, 12>(dq, grid, lds, s, p);
+  else launch_mt_nq<MT, 16>(dq, grid, lds, s, p);
+}
+
+size_t part_bytes(const GemvPlan &pl, int64_t M) {
+  return pl.C > 1 ? align_up(static_cast<size_t>(pl.S) * pl.C * M * 16 * pl.T * sizeof(float), 256) : 0;
 }
 
 }  // namespace
 
+bool gemv_sync_fits(int64_t M, int64_t N, int64_t K, int r) {
+  const GemvPlan pl = gemv_plan(M, N, K, r);
+  return static_cast<size_t>(pl.S) * (pl.U + 1) * sizeof(uint32_t) + 256 <= kLinearSyncBytes;
+}
+
 size_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
-  (void)M;
-  return part_bytes(N, K) + align_up(static_cast<size_t>(gemv_split(N, K).splits * kGvRows * r) * sizeof(float), 256);
+  const GemvPlan pl = gemv_plan(M, N, K, r);
+  return kLinearSyncBytes + part_bytes(pl, M) +
+         align_up(static_cast<size_t>(pl.HK) * M * pl.rp * sizeof(float), 256);
 }
 
 hipError_t launch_gemv(const LinearArgs &a, const void *X, const float *A, const float *B, void *Y, void *ws,
                        hipStream_t s) {
+  const GemvPlan pl = gemv_plan(a.M, a.N, a.K, a.r);
   GemvParams p{};
+  p.X = static_cast<const __bf16 *>(X);
   p.codes = a.codes;
   p.absmax_q = a.absmax_q;
   p.dq_scale = a.dq_scale;
@@ -481,31 +653,39 @@ hipError_t launch_gemv(const LinearArgs &a, const void *X, const float *A, const
   p.absmax = a.absmax;
   p.A = A;
   p.B = B;
+  p.Y = static_cast<__bf16 *>(Y);
+  p.M = a.M;
   p.N = a.N;
   p.K = a.K;
   p.r = a.r;
+  p.rp = pl.rp;
   p.scale = a.scale;
+  p.T = pl.T;
+  p.S = pl.S;
+  p.C = pl.C;
+  p.cq = pl.cq;
+  p.U = pl.U;
+  p.HK = pl.HK;
+  p.hb = pl.hb;
+  p.hstep = pl.hstep;
+  p.xstride = pl.xstride;
+  p.zoff = pl.zoff;
   p.tab = format_tables(a.format);
-  const GemvSplit sp = gemv_split(a.N, a.K);
-  p.splits = sp.splits;
-  p.split_blocks = sp.blocks;
-  p.part = static_cast<float *>(ws);
-  p.hpart = reinterpret_cast<float *>(static_cast<char *>(ws) + part_bytes(a.N, a.K));
-  const dim3 grid(static_cast<unsigned>(ceil_div(a.N, kGvCols)), static_cast<unsigned>(p.splits));
-  // passes of up to 16 rows, in order on the stream (they share the workspace)
-  const bool aligned = a.K % 256 == 0, dq = fmt_dq(a.format);
-  for (int64_t row0 = 0; row0 < a.M; row0 += kGvRows) {
-    p.M = std::min<int64_t>(kGvRows, a.M - row0);
-    p.X = static_cast<const __bf16 *>(X) + row0 * a.K;
-    p.Y = static_cast<__bf16 *>(Y) + row0 * a.N;
-    prof_begin(kProfFwdGemm, s);
-    if (p.M <= 4) launch_stream<4>(aligned, dq, grid, s, p);
-    else if (p.M <= 8) launch_stream<2>(aligned, dq, grid, s, p);
-    else launch_stream<1>(aligned, dq, grid, s, p);
-    prof_end(kProfFwdGemm, s);
-    hipLaunchKernelGGL(k_gemv_finish, dim3(static_cast<unsigned>(ceil_div(a.N, kFinCols))), dim3(kFinThreads), 0,
-                       s, p);
-  }
+  // sync words: [0] error, [64 ..) strip counters [S], then flags [S][U]
+  char *base = static_cast<char *>(ws);
+  p.err = reinterpret_cast<uint32_t *>(base);
+  p.ctr = p.err + 64;
+  p.flags = p.ctr + pl.S;
+  p.part = reinterpret_cast<float *>(base + kLinearSyncBytes);
+  p.hpart = reinterpret_cast<float *>(base + kLinearSyncBytes + part_bytes(pl, a.M));
+  const unsigned grid = static_cast<unsigned>(pl.U + pl.S * pl.C);
+  const int mt = static_cast<int>(ceil_div(a.M, 8));
+  const bool dq = fmt_dq(a.format);
+  prof_begin(kProfFwdGemm, s);
+  if (mt == 1) launch_mt<1>(pl.nq_max, dq, grid, pl.lds, s, p);
+  else if (mt == 2) launch_mt<2>(pl.nq_max, dq, grid, pl.lds, s, p);
+  else launch_mt<4>(pl.nq_max, dq, grid, pl.lds, s, p);
+  prof_end(kProfFwdGemm, s);
   return hipGetLastError();
 }
 

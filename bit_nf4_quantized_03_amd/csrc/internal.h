@@ -6,6 +6,8 @@
 #include <cstdint>
 #include <cstddef>
 
+#include "../../include/qlora_nf4.h"
+
 namespace qnf4 {
 
 constexpr int kBlock = 64;     // weight elements per absmax constant
@@ -79,6 +81,12 @@ struct LinearArgs {
   const float *absmax;      // without DQ: the fp32 block constants
 };
 
+// A linear workspace starts with kLinearSyncBytes of synchronization words
+// (counters and flags of the single-launch skinny-M forward). They must be zero
+// before the workspace is first used; every call leaves them zero. The other
+// kernels' scratch follows them.
+constexpr size_t kLinearSyncBytes = QLORA_LINEAR_SYNC_BYTES;
+
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int r);
 hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const float *B,
                       void *Y, void *ws, hipStream_t s);
@@ -95,8 +103,11 @@ hipError_t launch_merge(const LinearArgs &w, const float *A, const float *B, int
                         int8_t *absmax_q, float *dq_scale, float *dq_mean, float *absmax, void *ws,
                         hipStream_t s);
 
-// Skinny-M forward (M <= 32): fp32 split partials of Y and of X A^T at the
-// start of the workspace, then the bf16 output.
+// Skinny-M forward (M <= 32) in one launch: sync words, then the split
+// partials of Y and the pieces of X A^T. gemv_sync_fits is false when the
+// shape needs more sync words than the workspace header holds (then the
+// large-tile path runs instead).
+bool gemv_sync_fits(int64_t M, int64_t N, int64_t K, int r);
 size_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K, int r);
 hipError_t launch_gemv(const LinearArgs &a, const void *X, const float *A, const float *B, void *Y,
                        void *ws, hipStream_t s);

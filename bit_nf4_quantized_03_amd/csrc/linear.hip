@@ -20,7 +20,8 @@
 //                     transposed (reduction over out_features)
 //   k_grad            split-M partials of dA = dHb^T X and dB = dY^T Hs
 //   k_grad_finish     fixed-order sums of those partials
-// Small M (decode, M <= 32) runs the weight-streaming kernels of gemv.hip instead.
+// Small M (decode, M <= 32) runs the single-launch weight-streaming kernel of
+// gemv.hip instead.
 #include <algorithm>
 
 #include "gemm_big.h"
@@ -573,7 +574,7 @@ struct Plan {
 Plan make_plan(int64_t M, int64_t N, int64_t K, int r) {
   Plan pl;
   pl.rp = static_cast<int>(ceil_div(r, kBK) * kBK);
-  pl.small = M <= kSmallM;
+  pl.small = M <= kSmallM && gemv_sync_fits(M, N, K, r);
   const int ksteps = static_cast<int>(K / kBK), nsteps = static_cast<int>(N / kBK);
   const int64_t skinny_tiles = grid_blocks(M, kDownRows) * grid_blocks(pl.rp, 64);
   pl.down = choose_split(skinny_tiles, ksteps, 64, kDownGroups);
@@ -597,7 +598,8 @@ struct Buffers {
 };
 
 Buffers carve(void *ws, const Plan &pl, int64_t M, int64_t N, int64_t K, size_t *bytes) {
-  Carve c{static_cast<char *>(ws)};
+  // the sync words at the start of the workspace belong to the skinny-M path
+  Carve c{static_cast<char *>(ws), kLinearSyncBytes};
   Buffers b{};
   const int64_t nb = ceil_div(N * K, kBlock);
   const int rp = pl.rp;

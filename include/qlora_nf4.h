@@ -169,7 +169,15 @@ int qlora_nf4_quantize(const void *W, int w_dtype, int64_t rows, int64_t cols,
 int qlora_nf4_dequantize(const qlora_nf4_weight *q, void *out, int out_dtype, void *stream);
 
 /* Workspace bytes needed by qlora_linear_fwd and qlora_linear_bwd for these
- * sizes (the larger of the two; 0 if the sizes are invalid). */
+ * sizes (the larger of the two; 0 if the sizes are invalid).
+ * The first QLORA_LINEAR_SYNC_BYTES of a linear workspace are
+ * synchronization words (arrival counters and publication flags of the
+ * single-launch skinny-M forward). They must be zero when the workspace is
+ * first passed to the library (allocate it zero-filled, or clear it once);
+ * every call returns them to zero by the time it completes, so a workspace
+ * can be reused for any sizes and for both calls without clearing it again.
+ * One workspace must not be used by two calls that run concurrently. */
+#define QLORA_LINEAR_SYNC_BYTES (256 * 1024)
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
 
 /*
@@ -190,6 +198,9 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
  * adapter activations enter them rounded to bf16. For M > 32 the base enters
  * as bf16(w_i); for M <= 32 (the decode path) it enters as bf16(level) and
  * the fp32 block scale c_b multiplies each block's partial product. M >= 1.
+ * The decode path is one kernel launch; its workgroups exchange partial sums
+ * through the workspace and wait for one another with bounded spins (see
+ * QLORA_LINEAR_SYNC_BYTES for the workspace's leading words).
  */
 int qlora_linear_fwd(const void *X, int64_t M, const qlora_nf4_weight *W,
                      const float *A, const float *B, int32_t r, float scale,

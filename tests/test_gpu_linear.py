@@ -220,7 +220,7 @@ def test_graph_replays_match_eager(qb, cb, M):
     A, B = gu.dev_f32(wl.A), gu.dev_f32(wl.B)
     q = qb.NF4Weight.empty(wl.N, wl.K, dev)
     ws_q = torch.empty(qb.qlora_nf4_quantize_workspace_bytes(wl.N, wl.K), dtype=torch.uint8, device=dev)
-    ws_l = torch.empty(qb.qlora_linear_workspace_bytes(M, wl.N, wl.K, wl.r), dtype=torch.uint8, device=dev)
+    ws_l = qb.linear_workspace(M, wl.N, wl.K, wl.r, dev)
     Wd = torch.empty((wl.N, wl.K), dtype=torch.bfloat16, device=dev)
     Y = torch.empty((M, wl.N), dtype=torch.bfloat16, device=dev)
     dX = torch.empty((M, wl.K), dtype=torch.bfloat16, device=dev)
@@ -281,3 +281,36 @@ def test_binding_rejects_mismatched_tensors(qb, cb):
     with pytest.raises(ValueError):
         qb.qlora_nf4_dequantize(c.q, torch.float32, out=torch.empty((64, 192), device="cuda"))
     torch.cuda.synchronize()
+
+
+def test_decode_sync_words_return_to_zero_and_results_repeat(qb):
+    """The single-launch decode forward exchanges partials between workgroups
+    through the workspace's leading synchronization words. After every call
+    they are all zero again (no wait timed out, every counter and flag was
+    cleared), one workspace serves several shapes in turn (split and unsplit
+    reductions, adapter ranks 0 to 256), and repeated calls give bit-identical
+    outputs."""
+    import torch
+    dev = torch.device("cuda:0")
+    shapes = [(1, 11008, 4096, 64), (16, 4096, 11008, 64), (4, 320, 2240, 72), (32, 320, 448, 256),
+              (7, 1024, 576, 0), (1, 64, 64, 8)]
+    need = max(qb.qlora_linear_workspace_bytes(*s) for s in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    for rep in range(2):
+        for (M, N, K, r) in shapes:
+            gu.announce(f"decode sync M={M} N={N} K={K} r={r} rep={rep}")
+            W = (torch.randn((N, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            q = qb.qlora_nf4_quantize(W)
+            X = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+            A = torch.randn((r, K), generator=gen, device=dev) * 0.01 if r else None
+            B = torch.randn((N, r), generator=gen, device=dev) * 0.01 if r else None
+            outs = [qb.qlora_linear_fwd(X, q, A, B, 0.25, ws=ws) for _ in range(3)]
+            torch.cuda.synchronize()
+            assert torch.count_nonzero(ws[:qb.LINEAR_SYNC_BYTES]).item() == 0, \
+                f"sync words not cleared after M={M} N={N} K={K} r={r}"
+            for o in outs[1:]:
+                assert torch.equal(o, outs[0]), f"M={M} N={N} K={K} r={r}: repeated calls differ"
+            fresh = qb.qlora_linear_fwd(X, q, A, B, 0.25)
+            assert torch.equal(fresh, outs[0]), f"M={M} N={N} K={K} r={r}: shared workspace differs"
