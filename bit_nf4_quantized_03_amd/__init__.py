@@ -24,6 +24,7 @@ __all__ = [
     "QLORA_FMT_NF4_DQ", "QLORA_FMT_NF4", "QLORA_FMT_FP4_DQ", "QLORA_FMT_FP4",
     "qlora_nf4_merge_workspace_bytes", "qlora_nf4_merge",
     "qlora_adamw_workspace_bytes", "qlora_adamw_step", "linear_workspace", "LINEAR_SYNC_BYTES",
+    "qlora_linear_fwd_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora_nf4.so")
@@ -38,7 +39,7 @@ EXPORTED_SYMBOLS = (
     "qlora_profile_enable", "qlora_profile_read", "qlora_profile_reset",
     "qlora_weight_storage_bytes", "qlora_format_levels",
     "qlora_nf4_merge_workspace_bytes", "qlora_nf4_merge",
-    "qlora_adamw_workspace_bytes", "qlora_adamw_step",
+    "qlora_adamw_workspace_bytes", "qlora_adamw_step", "qlora_linear_fwd_noalloc",
 )
 
 
@@ -85,6 +86,7 @@ def _load():
         "qlora_linear_workspace_bytes": (sz, [i64, i64, i64, i32]),
         "qlora_linear_fwd": (ctypes.c_int, [vp, i64, wp, vp, vp, i32, f32, vp, vp, sz, vp]),
         "qlora_linear_bwd": (ctypes.c_int, [vp, vp, i64, wp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
+        "qlora_linear_fwd_noalloc": (ctypes.c_int, [vp, i64, wp, vp, vp, i32, f32, vp, vp]),
         "qlora_nf4_merge_workspace_bytes": (sz, [i64, i64, i32]),
         "qlora_nf4_merge": (ctypes.c_int, [wp, vp, vp, i32, f32, wp, vp, sz, vp]),
         "qlora_adamw_workspace_bytes": (sz, [i64, ctypes.c_int]),
@@ -460,3 +462,19 @@ def qlora_linear_bwd(dY, X, W: NF4Weight, A=None, B=None, scale: float = 0.0, ws
                                 float(scale), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream_ptr(X.device)))
     return dX, dA, dB
+
+
+def qlora_linear_fwd_noalloc(X, W: NF4Weight, A=None, B=None, scale: float = 0.0, out=None):
+    """qlora_linear_fwd through the allocation-free entry point: no workspace,
+    and ``out`` (bf16 [M, N]) must be given, so nothing is allocated."""
+    torch = _torch()
+    M = _activation("X", X, W)
+    r = _adapter(W, A, B, W.device)
+    if out is None:
+        raise ValueError("out must be given: the allocation-free call allocates nothing")
+    _need_cuda("out", out, torch.bfloat16, (M, W.rows), W.device)
+    st = W.c_struct()
+    _check("qlora_linear_fwd_noalloc",
+           lib.qlora_linear_fwd_noalloc(_ptr(X), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale),
+                                        _ptr(out), _stream_ptr(X.device)))
+    return out

@@ -24,7 +24,8 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libqlora_nf4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "codebook.cpp", "profile.cpp", "nf4_quant.hip", "linear.hip", "gemv.hip", "merge.hip", "adamw.hip"]
+SOURCES = ["api.cpp", "codebook.cpp", "profile.cpp", "nf4_quant.hip", "linear.hip", "gemv.hip", "merge.hip", "adamw.hip",
+           "noalloc.hip"]
 ARCH = os.environ.get("QLORA_OFFLOAD_ARCH", "gfx950")
 
 

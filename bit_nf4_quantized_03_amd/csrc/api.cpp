@@ -234,6 +234,25 @@ int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qlora_nf4_w
   return hip_status(e, fn);
 }
 
+int qlora_linear_fwd_noalloc(const void *X, int64_t M, const qlora_nf4_weight *W, const float *A,
+                             const float *B, int32_t r, float scale, void *Y, void *stream) {
+  const char *fn = "qlora_linear_fwd_noalloc";
+  if (!X || !Y) return fail(QLORA_ERR_NULL, "%s: X and Y must not be NULL", fn);
+  int st = check_linear_common(fn, M, W, A, B, r);
+  if (st != QLORA_OK) return st;
+  if (!aligned16(X) || !aligned16(Y))
+    return fail(QLORA_ERR_ALIGN, "%s: X and Y must be 16-byte aligned", fn);
+  const size_t need = qnf4::linear_fwd_ws_bytes(M, W->rows, W->cols, r);
+  if (need > qnf4::kNoAllocScratchBytes)
+    return fail(QLORA_ERR_WORKSPACE, "%s: these sizes need %zu bytes of scratch, more than the %zu the library holds",
+                fn, need, qnf4::kNoAllocScratchBytes);
+  void *scratch = nullptr;
+  hipError_t e = qnf4::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, fn);
+  e = qnf4::linear_fwd(make_args(M, W, r, scale), X, A, B, Y, scratch, static_cast<hipStream_t>(stream));
+  return hip_status(e, fn);
+}
+
 size_t qlora_nf4_merge_workspace_bytes(int64_t rows, int64_t cols, int32_t r) {
   if (rows <= 0 || cols <= 0 || rows > kMaxElems / cols || r < 0 || r > 256) return 0;
   return qnf4::merge_ws_bytes(rows, cols, r);

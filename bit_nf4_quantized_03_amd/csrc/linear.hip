@@ -693,6 +693,14 @@ size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
   return pl.small ? std::max(bytes, gemv_ws_bytes(M, N, K, r)) : bytes;
 }
 
+size_t linear_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
+  const Plan pl = make_plan(M, N, K, r);
+  if (pl.small) return gemv_ws_bytes(M, N, K, r);
+  size_t bytes = 0;
+  carve(nullptr, pl, M, N, K, &bytes);
+  return bytes;
+}
+
 hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const float *B, void *Y,
                       void *ws, hipStream_t s) {
   const Plan pl = make_plan(a.M, a.N, a.K, a.r);

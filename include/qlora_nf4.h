@@ -222,6 +222,23 @@ int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qlora_nf4_w
                      void *dX, float *dA, float *dB, void *ws, size_t ws_bytes,
                      void *stream);
 
+/*
+ * qlora_linear_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The same kernels and results as
+ * qlora_linear_fwd; the library uses a scratch array of 64 MiB in device
+ * memory that each GPU holds from library load until the process ends, and
+ * the call allocates nothing. Sizes whose forward needs more scratch than
+ * that fail with QLORA_ERR_WORKSPACE before anything is launched (every
+ * M <= 32 call of the 7B and 65B shapes fits, and M = 4096 at 4096 x 4096).
+ * Every call on one GPU uses that GPU's array: calls that overlap on one GPU
+ * (two streams, two threads) race and must not be issued; calls ordered on
+ * one stream are safe. Arguments and errors as qlora_linear_fwd.
+ */
+int qlora_linear_fwd_noalloc(const void *X, int64_t M, const qlora_nf4_weight *W,
+                             const float *A, const float *B, int32_t r, float scale,
+                             void *Y, void *stream);
+
 /* Workspace bytes needed by qlora_nf4_merge (0 if the sizes are invalid). */
 size_t qlora_nf4_merge_workspace_bytes(int64_t rows, int64_t cols, int32_t r);
 

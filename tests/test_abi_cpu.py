@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(qb.EXPORTED_SYMBOLS) == names
@@ -222,3 +222,18 @@ def test_binding_rejects_host_tensors_before_any_call():
         qb.qlora_nf4_quantize(torch.zeros((64, 64)))
     with pytest.raises(TypeError):
         qb.qlora_adamw_step(torch.zeros(8), torch.zeros(8), torch.zeros(8), torch.zeros(8), 1, 1e-3)
+
+
+def test_noalloc_rejects_before_launch():
+    """The allocation-free forward checks its arguments like qlora_linear_fwd
+    and refuses sizes whose forward needs more than its scratch array, all on
+    the host (the pointers are fake, so a launch would fault)."""
+    ref = ctypes.byref
+    f = lib.qlora_linear_fwd_noalloc
+    w = _weight(256, 256)
+    assert f(None, 16, ref(w), FAKE, FAKE, 8, 2.0, FAKE, None) == -1
+    assert f(FAKE, 0, ref(w), FAKE, FAKE, 8, 2.0, FAKE, None) == -2
+    assert f(FAKE, 16, ref(w), FAKE + 4, FAKE, 8, 2.0, FAKE, None) == -6
+    big = _weight(22016, 8192)
+    assert f(FAKE, 2048, ref(big), FAKE, FAKE, 64, 0.25, FAKE, None) == -4
+    assert "scratch" in qb.qlora_last_error()
