@@ -392,26 +392,42 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
   for (int jq = 0; jq < NQ; ++jq) {
     if (jq >= nq) continue;   // uniform
     const int bi = 2 * (q0 + jq) + half;
-    const float cb = bi < nblk ? crow[bi] : 0.0f;
-    f32x4 tq[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) tq[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // every LDS read of the quad-piece is issued before its first MFMA, so
+    // that the reads' latency is paid once per quad-piece, not once per MFMA
     const uint4 cv = cw[jq];
+    uint32_t pr[16];   // level pairs of the 16 code bytes
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t wq = q == 0 ? cv.x : q == 1 ? cv.y : q == 2 ? cv.z : cv.w;
-      const uint4 bv = make_uint4(lt[(wq & 0xFFu) * kLutCopies], lt[((wq >> 8) & 0xFFu) * kLutCopies],
-                                  lt[((wq >> 16) & 0xFFu) * kLutCopies], lt[(wq >> 24) * kLutCopies]);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) pr[4 * q + b] = lt[((wq >> (8 * b)) & 0xFFu) * kLutCopies];
+    }
+    bf16x8 xv[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[mt][q] = *reinterpret_cast<const bf16x8 *>(xb[mt] + 128 * jq + 8 * q);
+    const float cb = bi < nblk ? crow[bi] : 0.0f;
+    // two accumulator chains (MFMAs q = 0, 2 and q = 1, 3), added at the end
+    f32x4 ta[MT], tb[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      ta[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tb[mt] = ta[mt];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 bv = make_uint4(pr[4 * q], pr[4 * q + 1], pr[4 * q + 2], pr[4 * q + 3]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(xb[mt] + 128 * jq + 8 * q);
-        tq[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, __builtin_bit_cast(bf16x8, bv), tq[mt], 0, 0, 0);
+        f32x4 &t = (q & 1) ? tb[mt] : ta[mt];
+        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[mt][q], __builtin_bit_cast(bf16x8, bv), t, 0, 0, 0);
       }
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(cb, tq[mt][e], acc[mt][e]);
+      for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(cb, ta[mt][e] + tb[mt][e], acc[mt][e]);
   }
   // the two blocks' rows: lanes l and l + 32 hold the same outputs
 #pragma unroll
