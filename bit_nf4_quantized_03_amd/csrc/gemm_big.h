@@ -35,28 +35,41 @@ using CfgBig8 = TileCfg<256, 256, 2, 4>;   // eight waves: 128 x 64 per wave
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Dense bf16 operand rows [256][64] of src (row stride ld) via LDS DMA. The
-// tile is 32 blocks of 1 KB (8 rows each); wave w copies blocks w + W i
-// (W waves), and lane L of a block fetches the global chunk that the swizzle
-// places at byte 16 L of the block.
-template <int T>
+// Dense bf16 operand rows [ROWS][64] of src (row stride ld) via LDS DMA. The
+// tile is ROWS / 8 blocks of 1 KB (8 rows each); wave w of the W = T / 64
+// copying waves copies blocks w + W i, and lane L of a block fetches the
+// global chunk that the swizzle places at byte 16 L of the block.
+//
+// The swizzle of row 8 b + rb is rb ^ (b & 3). With W a multiple of 4 every
+// block of a wave has the same b & 3, so one chunk serves all of its blocks;
+// otherwise the chunk is recomputed per block.
+template <int T, int ROWS = kBigRows>
 struct DirectRowsT {
   static constexpr int kWaves = T / 64;
-  static constexpr int kPerWave = kBigRows / 8 / kWaves;   // 8 or 4
+  static constexpr int kPerWave = ROWS / 8 / kWaves;
+  static constexpr bool kOneChunk = kWaves % 4 == 0;
   const char *base;
   uint32_t off;     // block 0 of this wave; block i adds i * bstride
   uint32_t bstride; // bytes between the wave's blocks (8 W rows)
   uint32_t clamp;   // largest valid row offset (bytes), for a tile crossing the end
+  int prb;          // p ^ rb: the chunk of block b is prb ^ (b & 3)
   __device__ DirectRowsT(const void *src, int64_t ld, int64_t nrows, int64_t row0) {
     base = static_cast<const char *>(src) + row0 * ld * 2;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int rb = lane >> 3, p = lane & 7;
-    const int row = 8 * w + rb;              // the swizzle of row 8 (w + W i) + rb does not depend on i
+    const int row = 8 * w + rb;
     const int c = p ^ swz(row);
-    off = static_cast<uint32_t>((row * ld + 8 * c) * 2);
+    prb = p ^ rb;
+    const int64_t last = (nrows - 1 - row0) < ROWS - 1 ? (nrows - 1 - row0) : ROWS - 1;
     bstride = static_cast<uint32_t>(8 * kWaves * ld * 2);
-    const int64_t last = (nrows - 1 - row0) < 255 ? (nrows - 1 - row0) : 255;
-    clamp = static_cast<uint32_t>((last * ld + 8 * c) * 2);
+    if constexpr (kOneChunk) {
+      off = static_cast<uint32_t>((row * ld + 8 * c) * 2);
+      clamp = static_cast<uint32_t>((last * ld + 8 * c) * 2);
+    } else {
+      // row parts only; the chunk is added per block after the clamp
+      off = static_cast<uint32_t>(row * ld * 2);
+      clamp = static_cast<uint32_t>(last * ld * 2);
+    }
   }
   // Issue the copies of reduction step red0 into the LDS tile `lds`. They are
   // written as inline assembly so that the compiler does not treat every
@@ -74,7 +87,8 @@ struct DirectRowsT {
         static_cast<uint32_t>(w) * 1024u);
 #pragma unroll
     for (int i = i0; i < i0 + n; ++i) {
-      const uint32_t o = min(off + static_cast<uint32_t>(i) * bstride, clamp);
+      uint32_t o = min(off + static_cast<uint32_t>(i) * bstride, clamp);
+      if constexpr (!kOneChunk) o += 16u * static_cast<uint32_t>(prb ^ ((w + kWaves * i) & 3));
       const uint32_t dst = dst0 + static_cast<uint32_t>(i) * (1024u * kWaves);   // block w + W i
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                    :

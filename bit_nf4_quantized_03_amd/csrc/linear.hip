@@ -160,173 +160,221 @@ struct DownParams {
   int h_splits, h_steps, dh_splits, dh_steps;
 };
 
-// Skinny product tile of k_adapter_down: 128 rows of P (32 per wave) by the
-// 64 adapter columns j0 .. j0 + 63 of Q, over a range of the reduction.
-//
-// P is streamed straight from memory into the MFMA A operand (no LDS): the
-// reduction is processed in chunks of CS 64-deep steps, and within a chunk
-// lane (row i = lane % 32, half h = lane / 32) holds the contiguous run
-// k = h * 32 CS + 8 s .. + 7 for slices s = 0 .. 4 CS - 1. The Q operand is
-// rounded to bf16 and staged in LDS as [64][264] (rows padded by 16 bytes, so
-// that the 32 rows a fragment read touches start in different banks) and read
-// with the same permutation of k, so each MFMA pairs equal k.
+// One workgroup of k_adapter_down: kDownRows = 128 rows of P (X for H, dY
+// for G) by the 64 adapter columns j0 .. j0 + 63 of Q (A^T for H, B for G),
+// over a range of 64-deep reduction steps. Every global read is a copy
+// straight into LDS (no registers), issued kDownAhead steps ahead into a ring
+// of kDownAhead + 1 stages; a stage holds
+//   the P tile  [128][64] bf16, 128 contiguous bytes a row (16-byte copies),
+//               swizzled as the fragment reads expect, and
+//   the Q tile  fp32: rows of A as [64 j][64 k], or rows of B as
+//               [64 n][64 j] (16-byte copies when r is a multiple of 4, else
+//               one 4-byte copy a lane and 256 bytes a row of B, whose rows
+//               of r floats are then not 16-byte aligned).
+// All four waves copy both tiles, so each wave's count of copies in flight
+// covers the whole stage and one wait per step suffices. After a stage
+// landed, the waves round its Q tile to the bf16 operand [64 j][64 k]
+// (swizzled; columns j >= r zero) and each wave runs the MFMAs of its 32 rows.
 constexpr int kDownWaves = 4;
-constexpr int kDownRows = 32 * kDownWaves;
+constexpr int kDownRows = 128;
 constexpr int kDownThreads = 64 * kDownWaves;
-constexpr int kDownLd = 256 + 8;         // LDS row of the Q chunk (bf16)
-constexpr int kDownLds = 64 * kDownLd;   // bf16 per Q buffer
+constexpr int kDownPBytes = kDownRows * kBK * 2;   // 16 KB
+constexpr int kDownQBytes = 64 * kBK * 4;          // 16 KB
+constexpr int kDownStageBytes = kDownPBytes + kDownQBytes;
+constexpr int kDownQbBytes = 64 * kBK * 2;         // 8 KB
+constexpr int kDownAhead = 3;                      // 96 KB in flight per workgroup
+constexpr size_t kDownLds = static_cast<size_t>(kDownAhead + 1) * kDownStageBytes + kDownQbBytes;
 
-// fp32 source of the Q operand: rows j0 .. j0 + 63 of Q, rows >= r zero.
-struct QSrc {
-  const float *src;
-  int64_t ld;
-  int r;
-  int j0;
-};
+using DownRows = DirectRowsT<kDownThreads, kDownRows>;   // 4 blocks of 1 KB per wave and step
 
-// Q = A (row j of Q is row j of A [r][K]): 8-element runs of a row, two
-// 16-byte loads each, consecutive threads along the row.
-template <int CS>
-struct QFromRows {
-  static constexpr int kRuns = 64 * 8 * CS / kDownThreads;
-  float4 v[2 * kRuns];
-  __device__ __forceinline__ void load(const QSrc &q, int64_t kc) {
-#pragma unroll
-    for (int u = 0; u < kRuns; ++u) {
-      const int idx = threadIdx.x + u * kDownThreads, j = idx / (8 * CS), c = idx % (8 * CS);
-      const float *p = q.src + static_cast<int64_t>(min(q.j0 + j, q.r - 1)) * q.ld + kc + 8 * c;
-      v[2 * u] = *reinterpret_cast<const float4 *>(p);
-      v[2 * u + 1] = *reinterpret_cast<const float4 *>(p + 4);
-    }
-  }
-  __device__ __forceinline__ void stage(const QSrc &q, __bf16 *lds) const {
-#pragma unroll
-    for (int u = 0; u < kRuns; ++u) {
-      const int idx = threadIdx.x + u * kDownThreads, j = idx / (8 * CS), c = idx % (8 * CS);
-      const bool ok = q.j0 + j < q.r;
-      const float4 a = v[2 * u], b = v[2 * u + 1];
-      const uint4 w = make_uint4(ok ? pack_bf16x2(a.x, a.y) : 0u, ok ? pack_bf16x2(a.z, a.w) : 0u,
-                                 ok ? pack_bf16x2(b.x, b.y) : 0u, ok ? pack_bf16x2(b.z, b.w) : 0u);
-      *reinterpret_cast<uint4 *>(lds + j * kDownLd + 8 * c) = w;
-    }
-  }
-};
-
-// Q = B^T (row j of Q is column j of B [N][r]): lane j of a wave reads
-// B[n][j0 + j], so one load covers a row of B; wave w takes the pairs of
-// reduction indices n = kc + 2 (w + 4 i), + 1 and writes each pair as one
-// 4-byte LDS store.
-template <int CS>
-struct QFromCols {
-  static constexpr int kPairs = 64 * CS / 2 / kDownWaves;
-  float v[2 * kPairs];
-  __device__ __forceinline__ void load(const QSrc &q, int64_t kc) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const float *p = q.src + min(q.j0 + lane, q.r - 1);
-#pragma unroll
-    for (int i = 0; i < kPairs; ++i) {
-      const int64_t n = kc + 2 * (w + kDownWaves * i);
-      v[2 * i] = p[n * q.ld];
-      v[2 * i + 1] = p[(n + 1) * q.ld];
-    }
-  }
-  __device__ __forceinline__ void stage(const QSrc &q, __bf16 *lds) const {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const bool ok = q.j0 + lane < q.r;
-#pragma unroll
-    for (int i = 0; i < kPairs; ++i)
-      *reinterpret_cast<uint32_t *>(lds + lane * kDownLd + 2 * (w + kDownWaves * i)) =
-          ok ? pack_bf16x2(v[2 * i], v[2 * i + 1]) : 0u;
-  }
-};
-
-template <int CS, template <int> class QL>
-struct DownChunk {
-  static constexpr int kSlices = 4 * CS;   // 16-deep MFMA slices
-  uint4 x[kSlices];
-  QL<CS> q;
-  __device__ __forceinline__ const char *xptr(const char *xrow, int64_t kc, int h) const {
-    return xrow + (kc + h * 32 * CS) * 2;
-  }
-  __device__ __forceinline__ void load_x(const char *xrow, int64_t kc, int h) {
-    const char *px = xptr(xrow, kc, h);
-#pragma unroll
-    for (int s = 0; s < kSlices; ++s) x[s] = *reinterpret_cast<const uint4 *>(px + 16 * s);
-  }
-  // MFMAs of the staged chunk; with NEXT, slice s of the next chunk (at px)
-  // is loaded into x[s] as soon as slice s has been consumed.
-  template <bool NEXT>
-  __device__ __forceinline__ void mma(f32x16 (&acc)[2], const __bf16 *lds, int lane, const char *px) {
-    const __bf16 *lb = lds + (lane & 31) * kDownLd + (lane >> 5) * 32 * CS;
-#pragma unroll
-    for (int s = 0; s < kSlices; ++s) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, x[s]);
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(lb + jb * 32 * kDownLd + 8 * s);
-        acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[jb], 0, 0, 0);
-      }
-      if (NEXT) x[s] = *reinterpret_cast<const uint4 *>(px + 16 * s);
-    }
-  }
-};
-
-// `n` chunks of CS steps from reduction offset k0. The Q chunk alternates
-// between the two LDS buffers, one barrier per chunk; the P operand streams
-// through the registers slice by slice. On entry and on exit the LDS is free.
-template <int CS, template <int> class QL>
-__device__ __forceinline__ void down_chunks(f32x16 (&acc)[2], const char *xrow, const QSrc &qs, int64_t k0,
-                                            int n, __bf16 *lds) {
-  if (n <= 0) return;
-  const int lane = threadIdx.x & 63, h = lane >> 5;
-  constexpr int64_t kLen = 64 * CS;
-  DownChunk<CS, QL> c;
-  c.load_x(xrow, k0, h);
-  c.q.load(qs, k0);
-  for (int i = 0; i < n; ++i) {
-    __bf16 *buf = lds + (i & 1) * kDownLds;
-    c.q.stage(qs, buf);
-    __syncthreads();
-    const int64_t kn = k0 + (i + 1) * kLen;
-    if (i + 1 < n) {
-      c.q.load(qs, kn);
-      c.template mma<true>(acc, buf, lane, c.xptr(xrow, kn, h));
-    } else {
-      c.template mma<false>(acc, buf, lane, nullptr);
-    }
-  }
-  __syncthreads();
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char *)p)));
 }
 
-template <template <int> class QL, int CS>
-__device__ __forceinline__ void down_tile(const char *P, int64_t L, int64_t M, const QSrc &qs, int64_t m0,
-                                          int s0, int steps, float *part, int rp, __bf16 *lds) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // rows past M read row M - 1 (always valid) and are not stored
-  const int64_t row = min(m0 + 32 * w + (lane & 31), M - 1);
-  const char *xrow = P + row * L * 2;
+// This wave's index, known to the compiler as wave-uniform (scalar).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)); }
+
+__device__ __forceinline__ void copy16(uint32_t dst, uint32_t off, const void *src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(dst), "v"(off), "s"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void copy4(uint32_t dst, uint32_t off, const void *src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" : : "s"(dst), "v"(off), "s"(src) : "memory", "m0");
+}
+
+// A Q tile of 64 fp32 rows of 64 floats, row q of the tile at `row_ptr(q)`
+// plus column offset `col` (floats): 16 blocks of 1 KB (4 rows each); wave w
+// copies blocks w + 4 i, lane L of a block fetching row 4 b + L / 16,
+// floats 4 (L % 16) .. + 3, which land at byte 16 L of the block, so the
+// stage is row-major [64][64].
+//   H (QRowsA): row q = row j0 + q of A [r][K] (rows >= r read row r - 1),
+//               columns from the step's k0;
+//   G (QColsB): row q = row n0 + q of B [N][r], columns j0 .. j0 + 63
+//               (columns past r read the row's last aligned four; they are
+//               dropped by the rounding), or with r % 4 != 0 one 4-byte copy
+//               per row, lane j fetching column min(j0 + j, r - 1).
+struct QRowsA {
+  static constexpr int kCopies = 4;   // per wave and step
+  const float *A;
+  int64_t K;
+  int brow[kCopies];        // first (clamped) row of each block: wave-uniform
+  uint32_t off[kCopies];    // this lane's byte offset from that row
+  __device__ QRowsA(const float *A_, int64_t K_, int r, int j0) : A(A_), K(K_) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+      const int b = w + 4 * i;
+      const int r0 = min(j0 + 4 * b, r - 1), rl = min(j0 + 4 * b + lane / 16, r - 1);
+      brow[i] = __builtin_amdgcn_readfirstlane(r0);
+      off[i] = static_cast<uint32_t>(static_cast<int64_t>(rl - r0) * K * 4 + 16 * (lane % 16));
+    }
+  }
+  __device__ __forceinline__ int copies() const { return kCopies; }
+  __device__ __forceinline__ void issue(int64_t k0, float *stage) const {
+    const uint32_t dst0 = lds_addr(stage) + static_cast<uint32_t>(wave_id()) * 1024u;
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) copy16(dst0 + i * 4096u, off[i], A + static_cast<int64_t>(brow[i]) * K + k0);
+  }
+  // Stage [64 j][64 k] fp32 -> operand rows j: units (j, chunk c) of 8 floats.
+  __device__ __forceinline__ static void convert(const float *st, __bf16 *qb, int r, int j0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = threadIdx.x + kDownThreads * u, j = idx >> 3, c = idx & 7;
+      const float4 a = *reinterpret_cast<const float4 *>(st + j * 64 + 8 * c);
+      const float4 b = *reinterpret_cast<const float4 *>(st + j * 64 + 8 * c + 4);
+      const bool ok = j0 + j < r;
+      *reinterpret_cast<uint4 *>(qb + lds_off(j, c)) =
+          ok ? make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w))
+             : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+};
+
+struct QColsB {
+  const float *B;
+  int r;
+  bool wide;         // r % 4 == 0: 16-byte copies
+  uint32_t off;      // wide: row (lane / 16) and column; else column only
+  __device__ QColsB(const float *B_, int r_, int j0) : B(B_), r(r_), wide(r_ % 4 == 0) {
+    const int lane = threadIdx.x & 63;
+    if (wide)
+      off = static_cast<uint32_t>(((lane / 16) * r_ + min(j0 + 4 * (lane % 16), r_ - 4)) * 4);
+    else
+      off = static_cast<uint32_t>(4 * min(j0 + lane, r_ - 1));
+  }
+  __device__ __forceinline__ int copies() const { return wide ? 4 : 16; }
+  __device__ __forceinline__ void issue(int64_t n0, float *stage) const {
+    const int w = wave_id();
+    const uint32_t dst0 = lds_addr(stage);
+    if (wide) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = w + 4 * i;   // rows 4 b .. 4 b + 3
+        copy16(dst0 + b * 1024u, off, B + (n0 + 4 * b) * r);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int n = w + 4 * i;
+        copy4(dst0 + n * 256u, off, B + (n0 + n) * r);
+      }
+    }
+  }
+  // Stage [64 n][64 j] fp32 -> operand rows j: chunk c of row j holds
+  // n = 8 c .. 8 c + 7 of column j.
+  __device__ __forceinline__ static void convert(const float *st, __bf16 *qb, int r, int j0) {
+    const int j = threadIdx.x & 63;
+    const bool ok = j0 + j < r;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = (threadIdx.x >> 6) + 4 * u;
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = st[(8 * c + i) * 64 + j];
+      *reinterpret_cast<uint4 *>(qb + lds_off(j, c)) =
+          ok ? make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                          pack_bf16x2(v[6], v[7]))
+             : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+};
+
+// Wait until at most `k` copies of this wave are in flight; k is a multiple
+// of the copies per step (8 or 20) below kDownAhead steps' worth.
+__device__ __forceinline__ void wait_down_copies(int k) {
+  switch (k) {
+    case 8: DownRows::wait_copies<8>(); break;
+    case 16: DownRows::wait_copies<16>(); break;
+    case 20: DownRows::wait_copies<20>(); break;
+    case 40: DownRows::wait_copies<40>(); break;
+    default: DownRows::wait_copies<0>(); break;
+  }
+}
+
+template <class QL>
+__device__ __forceinline__ void down_tile(const void *P, int64_t L, int64_t M, const QL &ql, int r, int j0,
+                                          int64_t m0, int s0, int n, float *part, int rp, char *smem) {
+  static_assert(kDownAhead == 3, "wait_down_copies covers two steps in flight");
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  constexpr int kRing = kDownAhead + 1;
+  __bf16 *qb = reinterpret_cast<__bf16 *>(smem + kRing * kDownStageBytes);
+  auto ptile = [&](int st) { return reinterpret_cast<__bf16 *>(smem + st * kDownStageBytes); };
+  auto qtile = [&](int st) { return reinterpret_cast<float *>(smem + st * kDownStageBytes + kDownPBytes); };
+  const DownRows pr(P, L, M, m0);
+  const int64_t k0 = static_cast<int64_t>(s0) * kBK;
+  const int per_step = DownRows::kPerWave + ql.copies();
+  for (int i = 0; i < min(kDownAhead, n); ++i) {
+    pr.issue(k0 + i * kBK, ptile(i));
+    ql.issue(k0 + i * kBK, qtile(i));
+  }
+  // fragment offsets of this wave's 32 rows and of the Q operand rows
+  int fa[4], fb[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    fa[kk] = lds_off(32 * w + (lane & 31), 2 * kk + (lane >> 5));
+    fb[kk] = lds_off(lane & 31, 2 * kk + (lane >> 5));
+  }
   f32x16 acc[2];
 #pragma unroll
   for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[jb][v] = 0.0f;
-  const int64_t k0 = static_cast<int64_t>(s0) * kBK;
-  down_chunks<CS, QL>(acc, xrow, qs, k0, steps / CS, lds);
-  if (CS > 1) down_chunks<1, QL>(acc, xrow, qs, k0 + (steps / CS) * CS * kBK, steps % CS, lds);
+  for (int s = 0; s < n; ++s) {
+    wait_down_copies(min(kDownAhead - 1, n - 1 - s) * per_step);
+    __syncthreads();   // stage s landed; every wave is done with step s - 1
+    if (s + kDownAhead < n) {
+      const int st = (s + kDownAhead) % kRing;
+      pr.issue(k0 + (s + kDownAhead) * kBK, ptile(st));
+      ql.issue(k0 + (s + kDownAhead) * kBK, qtile(st));
+    }
+    QL::convert(qtile(s % kRing), qb, r, j0);
+    __syncthreads();
+    const __bf16 *pt = ptile(s % kRing);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(pt + fa[kk]);
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(qb + fb[kk] + jb * 32 * kLDK);
+        acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[jb], 0, 0, 0);
+      }
+    }
+  }
   const int h = lane >> 5;
 #pragma unroll
   for (int jb = 0; jb < 2; ++jb) {
-    const int64_t col = qs.j0 + jb * 32 + (lane & 31);
+    const int64_t col = j0 + jb * 32 + (lane & 31);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int64_t r = m0 + 32 * w + 8 * (v >> 2) + 4 * h + (v & 3);
-      if (r < M) part[r * rp + col] = acc[jb][v];
+      const int64_t row = m0 + 32 * w + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (row < M) part[row * rp + col] = acc[jb][v];
     }
   }
 }
 
-__global__ __launch_bounds__(kDownThreads, 2) void k_adapter_down(DownParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * kDownLds];
+__global__ __launch_bounds__(kDownThreads, 1) void k_adapter_down(DownParams p) {
+  extern __shared__ __attribute__((aligned(16))) char down_smem[];
   int g = blockIdx.x;
   const int per = p.jt * p.mt;
   const bool is_h = g < per * p.h_splits;
@@ -339,13 +387,13 @@ __global__ __launch_bounds__(kDownThreads, 2) void k_adapter_down(DownParams p) 
   const int total = static_cast<int>(L / kBK);
   const int s0 = z * steps_per, steps = min(steps_per, total - s0);
   if (is_h) {
-    const QSrc qs{p.A, p.K, p.r, j0};
-    down_tile<QFromRows, 4>(static_cast<const char *>(p.X), L, p.M, qs, m0, s0, steps,
-                         p.h_part + static_cast<int64_t>(z) * p.M * p.rp, p.rp, lds);
+    const QRowsA ql(p.A, p.K, p.r, j0);
+    down_tile(p.X, L, p.M, ql, p.r, j0, m0, s0, steps, p.h_part + static_cast<int64_t>(z) * p.M * p.rp, p.rp,
+              down_smem);
   } else {
-    const QSrc qs{p.B, p.r, p.r, j0};
-    down_tile<QFromCols, 2>(static_cast<const char *>(p.dY), L, p.M, qs, m0, s0, steps,
-                         p.dh_part + static_cast<int64_t>(z) * p.M * p.rp, p.rp, lds);
+    const QColsB ql(p.B, p.r, j0);
+    down_tile(p.dY, L, p.M, ql, p.r, j0, m0, s0, steps, p.dh_part + static_cast<int64_t>(z) * p.M * p.rp, p.rp,
+              down_smem);
   }
 }
 
@@ -567,7 +615,7 @@ struct Carve {
 
 struct Plan {
   int rp;
-  Split down, dh, ga, gb;
+  Split down, hb, dh, ga, gb;   // forward H; backward H and dY B; dA; dB
   bool small;
 };
 
@@ -577,8 +625,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int r) {
   pl.small = M <= kSmallM && gemv_sync_fits(M, N, K, r);
   const int ksteps = static_cast<int>(K / kBK), nsteps = static_cast<int>(N / kBK);
   const int64_t skinny_tiles = grid_blocks(M, kDownRows) * grid_blocks(pl.rp, 64);
+  // one down-projection workgroup per CU (its LDS ring takes most of a CU):
+  // the forward's H fills the GPU alone, the backward shares it with dY B
   pl.down = choose_split(skinny_tiles, ksteps, 64, kDownGroups);
-  pl.dh = choose_split(skinny_tiles, nsteps, 64, kDownGroups);
+  pl.hb = choose_split(skinny_tiles, ksteps, 64, kDownGroups / 2);
+  pl.dh = choose_split(skinny_tiles, nsteps, 64, kDownGroups / 2);
   const int msteps = static_cast<int>(ceil_div(M, kBK));
   pl.ga = choose_split(grid_blocks(pl.rp, 64) * grid_blocks(K, 256), msteps, 8);
   pl.gb = choose_split(grid_blocks(N, 256) * grid_blocks(pl.rp, 64), msteps, 8);
@@ -605,7 +656,7 @@ Buffers carve(void *ws, const Plan &pl, int64_t M, int64_t N, int64_t K, size_t 
   const int rp = pl.rp;
   b.cs = c.take<float>(nb);
   if (rp > 0) {
-    b.down_part = c.take<float>(static_cast<size_t>(pl.down.splits) * M * rp);
+    b.down_part = c.take<float>(static_cast<size_t>(std::max(pl.down.splits, pl.hb.splits)) * M * rp);
     b.Hs = c.take<__bf16>(static_cast<size_t>(M) * rp);
     b.Bb = c.take<__bf16>(static_cast<size_t>(N) * rp);
     b.dh_part = c.take<float>(static_cast<size_t>(pl.dh.splits) * M * rp);
@@ -643,12 +694,17 @@ hipError_t run_adapter_pre(const LinearArgs &a, const Plan &pl, const Buffers &b
     dp.rp = pl.rp;
     dp.jt = pl.rp / 64;
     dp.mt = static_cast<int>(ceil_div(a.M, kDownRows));
-    dp.h_splits = pl.down.splits;
-    dp.h_steps = pl.down.steps_per_split;
+    const Split &hs = backward ? pl.hb : pl.down;
+    dp.h_splits = hs.splits;
+    dp.h_steps = hs.steps_per_split;
     dp.dh_splits = backward ? pl.dh.splits : 0;
     dp.dh_steps = pl.dh.steps_per_split;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k_adapter_down),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       static_cast<int>(kDownLds));
+    if (attr != hipSuccess) return attr;
     const int64_t groups = static_cast<int64_t>(dp.jt) * dp.mt * (dp.h_splits + dp.dh_splits);
-    hipLaunchKernelGGL(k_adapter_down, dim3(groups), dim3(kDownThreads), 0, s, dp);
+    hipLaunchKernelGGL(k_adapter_down, dim3(groups), dim3(kDownThreads), kDownLds, s, dp);
   }
   FinishParams fp{};
   fp.h_part = b.down_part;
@@ -658,7 +714,7 @@ hipError_t run_adapter_pre(const LinearArgs &a, const Plan &pl, const Buffers &b
   fp.M = a.M;
   fp.r = a.r;
   fp.rp = pl.rp;
-  fp.h_splits = pl.down.splits;
+  fp.h_splits = backward ? pl.hb.splits : pl.down.splits;
   fp.dh_splits = pl.dh.splits;
   fp.scale = a.scale;
   fp.absmax_q = a.absmax_q;

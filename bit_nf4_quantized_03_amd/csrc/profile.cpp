@@ -28,7 +28,7 @@ void prof_begin(int kind, hipStream_t s) {
   if (!prof_enabled()) return;
   hipEvent_t e = nullptr;
   if (hipEventCreate(&e) != hipSuccess) return;
-  hipEventRecord(e, s);
+  (void)hipEventRecord(e, s);
   g_open[kind] = e;
 }
 
@@ -36,7 +36,7 @@ void prof_end(int kind, hipStream_t s) {
   if (!prof_enabled() || !g_open[kind]) return;
   hipEvent_t e = nullptr;
   if (hipEventCreate(&e) != hipSuccess) return;
-  hipEventRecord(e, s);
+  (void)hipEventRecord(e, s);
   std::lock_guard<std::mutex> lk(g_mu);
   g_done[kind].push_back({g_open[kind], e});
   g_open[kind] = nullptr;
@@ -62,9 +62,9 @@ void prof_reset() {
   std::lock_guard<std::mutex> lk(g_mu);
   for (auto &v : g_done) {
     for (const EventPair &p : v) {
-      hipEventSynchronize(p.stop);
-      hipEventDestroy(p.start);
-      hipEventDestroy(p.stop);
+      (void)hipEventSynchronize(p.stop);
+      (void)hipEventDestroy(p.start);
+      (void)hipEventDestroy(p.stop);
     }
     v.clear();
   }
