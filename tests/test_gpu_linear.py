@@ -314,3 +314,40 @@ def test_decode_sync_words_return_to_zero_and_results_repeat(qb):
                 assert torch.equal(o, outs[0]), f"M={M} N={N} K={K} r={r}: repeated calls differ"
             fresh = qb.qlora_linear_fwd(X, q, A, B, 0.25)
             assert torch.equal(fresh, outs[0]), f"M={M} N={N} K={K} r={r}: shared workspace differs"
+
+
+
+def test_large_m_counters_return_to_zero_and_results_repeat(qb):
+    """Large-M forward and backward (split partials of the adapter
+    down-projection, summed in a fixed split order): the workspace's leading
+    synchronization words stay zero, repeated calls give bit-identical
+    outputs and gradients, and a fresh workspace gives the same results.
+    Shapes: split and unsplit reductions, ragged M, r = 8, 9 (rows of B not
+    16-byte aligned), 72 (two column tiles) and 256."""
+    import torch
+    dev = torch.device("cuda:0")
+    shapes = [(4096, 4096, 4096, 64), (300, 320, 448, 72), (33, 320, 448, 9), (130, 320, 448, 256),
+              (2048, 1024, 8192, 8)]
+    need = max(qb.qlora_linear_workspace_bytes(*s) for s in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(12)
+    for (M, N, K, r) in shapes:
+        gu.announce(f"large-M counters M={M} N={N} K={K} r={r}")
+        W = (torch.randn((N, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        q = qb.qlora_nf4_quantize(W)
+        X = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+        dY = torch.randn((M, N), generator=gen, device=dev).to(torch.bfloat16)
+        A = torch.randn((r, K), generator=gen, device=dev) * 0.01
+        B = torch.randn((N, r), generator=gen, device=dev) * 0.01
+        fw = [qb.qlora_linear_fwd(X, q, A, B, 0.25, ws=ws) for _ in range(2)]
+        bw = [qb.qlora_linear_bwd(dY, X, q, A, B, 0.25, ws=ws) for _ in range(2)]
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(ws[:qb.LINEAR_SYNC_BYTES]).item() == 0, \
+            f"counters not cleared after M={M} N={N} K={K} r={r}"
+        assert torch.equal(fw[0], fw[1]), f"M={M} N={N} K={K} r={r}: repeated forwards differ"
+        for a, b in zip(bw[0], bw[1]):
+            assert torch.equal(a, b), f"M={M} N={N} K={K} r={r}: repeated backwards differ"
+        assert torch.equal(qb.qlora_linear_fwd(X, q, A, B, 0.25), fw[0])
+        for a, b in zip(qb.qlora_linear_bwd(dY, X, q, A, B, 0.25), bw[0]):
+            assert torch.equal(a, b), f"M={M} N={N} K={K} r={r}: fresh workspace differs"
