@@ -162,26 +162,29 @@ __device__ __forceinline__ float code_lane(const uint4 &raw, int64_t e, int64_t 
   // Outside the fast range the lookup runs on z = 0 (always a valid cell)
   // and the exact path below recomputes every code of the lane.
   const float r128 = (a == 0.0f || !fast_scale) ? 0.0f : __fmul_rn(__builtin_amdgcn_rcpf(a), 128.0f);
+  // d = tz - z, exact in sign (a difference of two floats is negative
+  // exactly when the first is smaller), so z > tz is d < 0; and |d| is the
+  // distance to the cell's threshold (infinite where the cell has none).
   int c[kEpl];
-  bool near[kEpl];
+  float d[kEpl];
+  float dmin = __builtin_huge_valf();
 #pragma unroll
   for (int i = 0; i < kEpl; ++i) {
     const float z = __fmul_rn(x[i], r128);
     const float2 en = lut[static_cast<int>(z) + 128];   // truncation: |z| < 129
-    c[i] = __float_as_int(en.y) + ((z > en.x) ? 1 : 0);
-    near[i] = !fast_scale || fabsf(__fsub_rn(z, en.x)) <= 0x1p-14f;
+    d[i] = __fsub_rn(en.x, z);
+    c[i] = __float_as_int(en.y) + (d[i] < 0.0f ? 1 : 0);
+    dmin = fminf(dmin, fabsf(d[i]));
   }
   // Rare: exact division, element by element, so that a wave pays only for
   // the elements some lane needs (ratios of bf16 values hit a dyadic
-  // threshold such as FP4's 1/8 exactly now and then). One test first, so
-  // that a wave with no such element skips the per-element tests.
-  bool any = false;
-#pragma unroll
-  for (int i = 0; i < kEpl; ++i) any |= near[i];
-  if (any) {
+  // threshold such as FP4's 1/8 exactly now and then). One test on the
+  // lane's nearest threshold first, so that a wave with no such element
+  // skips the per-element tests.
+  if (!fast_scale || dmin <= 0x1p-14f) {
 #pragma unroll
     for (int i = 0; i < kEpl; ++i) {
-      if (near[i]) {
+      if (!fast_scale || fabsf(d[i]) <= 0x1p-14f) {
         const float y = (a == 0.0f) ? 0.0f : __fdiv_rn(x[i], a);
         c[i] = code_from_y(y, tab);
       }
@@ -192,10 +195,15 @@ __device__ __forceinline__ float code_lane(const uint4 &raw, int64_t e, int64_t 
     for (int i = 0; i < kEpl; ++i)
       if (e + i >= n) c[i] = 0;  // padding nibble of an odd tail
   }
-  uint32_t word = 0;
+  // two codes per byte (first in the high nibble), bytes in element order
+  uint32_t byte[kEpl / 2];
 #pragma unroll
-  for (int j = 0; j < kEpl / 2; ++j)
-    word |= static_cast<uint32_t>((c[2 * j] << 4) | c[2 * j + 1]) << (8 * j);
+  for (int j = 0; j < kEpl / 2; ++j) byte[j] = (static_cast<uint32_t>(c[2 * j]) << 4) | static_cast<uint32_t>(c[2 * j + 1]);
+  uint32_t word;
+  if (kEpl == 8)
+    word = ((byte[3] << 8 | byte[2]) << 16) | (byte[1] << 8 | byte[0]);
+  else
+    word = byte[1] << 8 | byte[0];
   const int64_t byte0 = e / 2;
   if (!kGuard || e + kEpl <= n) {
     if (kBf16) *reinterpret_cast<uint32_t *>(codes + byte0) = word;
