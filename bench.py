@@ -177,6 +177,51 @@ def write_traffic(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_
     print(json.dumps({k: (v["bytes_per_launch"] if "bytes_per_launch" in v else v) for k, v in data.items()}))
 
 
+def decoder_layer_row(qb, dev, ev_time):
+    """A Llama-7B decoder layer (d 4096, MLP 11008, 32 heads, r = 64) on 4
+    sequences of 1024 tokens: the seven QLoRA projections on the library's
+    kernels through the autograd wrapper, RMSNorm, causal attention and the
+    SwiGLU gating as fp32 torch glue. Forward + backward time, plain and with
+    the layer's forward recomputed in the backward, and the peak of device
+    memory above the inputs for one layer and for a stack of four."""
+    import torch
+    import torch.utils.checkpoint as ckpt
+    from tests import decoder_layer as dl
+    spec = dl.LayerSpec(d=4096, f=11008, heads=32, r=64, alpha=16.0)
+    layer = dl.GpuLayer(qb, spec, dl.make_params(spec, seed=77), dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(78)
+    x = torch.randn((4, 1024, spec.d), generator=gen, device=dev)
+    dy = torch.randn((4, 1024, spec.d), generator=gen, device=dev)
+
+    def run(checkpoint, depth=1):
+        layer.zero_grad()
+        xi = x.detach().requires_grad_(True)
+        y = xi
+        for _ in range(depth):
+            y = ckpt.checkpoint(layer.forward, y, use_reentrant=False) if checkpoint else layer.forward(y)
+        y.backward(dy)
+
+    row = {"tokens": 4096, "sequences": 4, "d": spec.d, "f": spec.f, "heads": spec.heads, "r": spec.r,
+           "weight_bytes_nf4": sum(qb.qlora_weight_storage_bytes(*spec.shape(n), 0) for n in dl.NAMES)}
+    for name, ck in (("plain", False), ("checkpointed", True)):
+        run(ck)
+        row[f"ms_{name}"] = ev_time(lambda: run(ck), 3)
+        for depth in (1, 4):
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats()
+            base = torch.cuda.memory_allocated()
+            run(ck, depth)
+            torch.cuda.synchronize()
+            row[f"peak_mib_{name}_depth{depth}"] = (torch.cuda.max_memory_allocated() - base) / 2**20
+    log(f"decoder layer 7B (4 x 1024 tokens, fwd + bwd): {row['ms_plain']:.2f} ms plain, "
+        f"{row['ms_checkpointed']:.2f} ms checkpointed; peak above inputs, stack of 4: "
+        f"{row['peak_mib_plain_depth4']:.0f} MiB plain, {row['peak_mib_checkpointed_depth4']:.0f} MiB checkpointed")
+    del layer
+    torch.cuda.empty_cache()
+    return row
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -609,6 +654,9 @@ def main():
             f"{layer_row['tflops']:.0f} TFLOP/s")
         del projs
         torch.cuda.empty_cache()
+        dec_row = decoder_layer_row(qb, dev, ev_time)
+    else:
+        dec_row = None
 
     mlp = {}
     if not args.no_large:
@@ -757,6 +805,7 @@ def main():
         "merge": merge_row,
         "adamw": opt,
         "layer7b_projections": layer_row,
+        "decoder_layer7b": dec_row,
         "mlp65b": mlp,
         "dequant_solo": dq_solo,
         "whole_model_roundtrip": wm,
