@@ -468,6 +468,10 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict_
                                                       void *__restrict__ out, Nf4Tables tab) {
   __shared__ float lv[16];
   __shared__ float cs[kDqBlock];
+  // fp32 output: each wave's 512 results of a piece pass through its own 2 KB
+  // of LDS, so that every store instruction writes 1 KB contiguous (lane l
+  // at 16 l) instead of every other 16 bytes of 2 KB
+  __shared__ __attribute__((aligned(16))) float stage[kOutBf16 ? 1 : kThreads * 8];
   const int tid = threadIdx.x;
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const int64_t nbytes = (n + 1) / 2;
@@ -534,7 +538,21 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict_
         }
       } else {
         float *o = reinterpret_cast<float *>(out) + e;
-        if (e + 8 <= n) {
+        // the wave's 512 elements are contiguous: [w0, w0 + 512) with w0 = e - 8 lane
+        const int lane = tid & 63;
+        const int64_t w0 = e - 8 * lane;
+        if (w0 + 512 <= n) {
+          float *st = stage + (tid - lane) * 8;
+          *reinterpret_cast<float4 *>(st + 8 * lane) = make_float4(v[0], v[1], v[2], v[3]);
+          *reinterpret_cast<float4 *>(st + 8 * lane + 4) = make_float4(v[4], v[5], v[6], v[7]);
+          __builtin_amdgcn_wave_barrier();
+          const float4 lo = *reinterpret_cast<const float4 *>(st + 4 * lane);
+          const float4 hi = *reinterpret_cast<const float4 *>(st + 256 + 4 * lane);
+          __builtin_amdgcn_wave_barrier();
+          float *ow = reinterpret_cast<float *>(out) + w0;
+          *reinterpret_cast<float4 *>(ow + 4 * lane) = lo;
+          *reinterpret_cast<float4 *>(ow + 256 + 4 * lane) = hi;
+        } else if (e + 8 <= n) {
           *reinterpret_cast<float4 *>(o) = make_float4(v[0], v[1], v[2], v[3]);
           *reinterpret_cast<float4 *>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
         } else {
