@@ -106,7 +106,8 @@ def load_traffic(kernel: str):
 
 
 def _counter_per_dispatch(folder: str, counter: str):
-    """{kernel name: [counter value summed per dispatch]} from a rocprofv3 --pmc run."""
+    """{(kernel name, grid work-items): [counter value summed per dispatch]}
+    from a rocprofv3 --pmc run."""
     import csv
     import glob
     files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
@@ -119,20 +120,55 @@ def _counter_per_dispatch(folder: str, counter: str):
                 if row["Counter_Name"] != counter:
                     continue
                 key = (path, row["Dispatch_Id"])
-                name, val = row["Kernel_Name"], float(row["Counter_Value"])
-                if key in per:
-                    per[key] = (name, per[key][1] + val)
-                else:
-                    per[key] = (name, val)
+                name = (row["Kernel_Name"], int(float(row.get("Grid_Size") or 0)))
+                val = float(row["Counter_Value"])
+                per[key] = (name, per[key][1] + val) if key in per else (name, val)
     out = {}
     for name, val in per.values():
         out.setdefault(name, []).append(val)
     return out
 
 
+# Kernels whose HBM traffic is summarized from the counter runs of the step
+# (--no-large --no-formats): key -> (kernel name fragment, grid work-items or
+# None for any, algorithmic read bytes, algorithmic write bytes). Step shape:
+# M = N = K = 4096, r = 64; decode shapes: gate/up 11008 x 4096 and down
+# 4096 x 11008 at M = 1 and 4 (one launch shape), r = 64.
+def _traffic_kernels():
+    M = N = K = 4096
+    r = rp = 64
+
+    def nf4_bytes(n, k):
+        nb = n * k // 64
+        return n * k // 2 + nb + 4 * ((nb + 255) // 256) + 4
+
+    def gemv(n, k):   # weight, X (M = 1), fp32 A and B; Y
+        return (nf4_bytes(n, k) + k * 2 + r * k * 4 + n * r * 4, n * 2)
+
+    return {
+        "fwd_gemm": ("k_fwd_big", None, M * K * 2 + nf4_bytes(N, K) + 2 * M * rp * 2, M * N * 2),
+        "bwd_dx_gemm": ("k_dx_big", None, M * N * 2 + nf4_bytes(N, K) + 2 * M * rp * 2, M * K * 2),
+        "dequant_bf16": ("k_dequant<true, true>", None, nf4_bytes(N, K), N * K * 2),
+        "adapter_down": ("k_adapter_down", None, None, None),
+        "adapter_finish": ("k_adapter_finish", None, None, None),
+        "grad": ("k_grad(", None, M * K * 2 + M * N * 2 + 2 * M * rp * 2, r * K * 4 + N * r * 4),
+        "grad_finish": ("k_grad_finish", None, None, r * K * 4 + N * r * 4),
+    }
+
+
+def _gemv_alg_bytes():
+    """Algorithmic bytes of one decode GEMV call at M = 1, r = 64: the NF4 +
+    DQ weight, X, the fp32 adapter factors, and Y (the 7B gate / up and down
+    shapes have the same totals up to X and Y, 8 or 22 KB)."""
+    n, k, r = 11008, 4096, 64
+    nb = n * k // 64
+    return n * k // 2 + nb + 4 * ((nb + 255) // 256) + 4 + k * 2 + r * (n + k) * 4, n * 2
+
+
 def write_traffic(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str, path: str = None):
-    """Calibrated HBM bytes per launch of the two dequant-GEMMs of the step
-    (the Llama-7B attention shape, M = N = K = 4096, r = 64).
+    """Calibrated HBM bytes per launch of the step's kernels (the Llama-7B
+    attention shape, M = N = K = 4096, r = 64) and of the decode GEMV at the
+    7B MLP shapes.
 
     FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch; each is scaled by
     the factor that makes the 1 GiB copy of --calib-copy read (write) exactly
@@ -142,39 +178,50 @@ def write_traffic(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_
     cal_f = max(v for vals in _counter_per_dispatch(cal_fetch_dir, "FETCH_SIZE").values() for v in vals)
     cal_w = max(v for vals in _counter_per_dispatch(cal_write_dir, "WRITE_SIZE").values() for v in vals)
     ff, fw = gib / (cal_f * 1024), gib / (cal_w * 1024)
-    M = N = K = 4096
-    rp = 64
-    # the counter runs time the step only (--no-large), so every dispatch of
-    # the two kernels is one of the step's
     fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
-    nb = N * K // 64
-    nf4 = N * K // 2 + nb + 4 * ((nb + 255) // 256) + 4
-    act, out = M * K * 2, M * N * 2
     data = {"calibration": {"copy_bytes_each_way": gib, "fetch_kib_read": cal_f, "write_kib_read": cal_w,
                             "fetch_factor": ff, "write_factor": fw}}
-    for key, kname in (("fwd_gemm", "k_fwd_big"), ("bwd_dx_gemm", "k_dx_big")):
-        fv = [v for n, vals in fetch.items() if kname in n for v in vals]
-        wv = [v for n, vals in write.items() if kname in n for v in vals]
+
+    def pick(table, frag, grid):
+        return [v for (n, g), vals in table.items() if frag in n and (grid is None or g == grid) for v in vals]
+
+    kernels = _traffic_kernels()
+    # one entry per launch shape of the decode GEMV (grid work-items)
+    for (n, g) in sorted(set(fetch) | set(write)):
+        if "k_gemv<" in n:
+            tmpl = n[n.index("k_gemv<"):n.index(">", n.index("k_gemv<")) + 1]
+            kernels[f"gemv {tmpl} grid {g}"] = (tmpl, g) + _gemv_alg_bytes()
+    for key, (kname, grid, alg_r, alg_w) in kernels.items():
+        fv, wv = pick(fetch, kname, grid), pick(write, kname, grid)
         if not fv or not wv:
-            raise SystemExit(f"{kname} missing from the counter runs")
+            print(f"{kname} (grid {grid}) missing from the counter runs", file=sys.stderr)
+            continue
         f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
-        data[key] = {
-            "kernel": kname,
+        ent = {
+            "kernel": kname if grid is None else f"{kname} grid {grid}",
             "fetch_kib_per_dispatch": f_kib,
             "write_kib_per_dispatch": w_kib,
             "dispatches": [len(fv), len(wv)],
+            "read_bytes": f_kib * 1024 * ff,
+            "write_bytes": w_kib * 1024 * fw,
             "bytes_per_launch": f_kib * 1024 * ff + w_kib * 1024 * fw,
-            "algorithmic_read_bytes": act + nf4 + 2 * M * rp * 2,
-            "algorithmic_write_bytes": out,
-            "source_hash": kernel_source_hash(key),
+            "algorithmic_read_bytes": alg_r,
+            "algorithmic_write_bytes": alg_w,
         }
+        if key in KERNEL_SOURCES:
+            ent["source_hash"] = kernel_source_hash(key)
+        data[key] = ent
     if path is None:
         path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
         json.dump(data, f, indent=1)
         f.write("\n")
-    print(json.dumps({k: (v["bytes_per_launch"] if "bytes_per_launch" in v else v) for k, v in data.items()}))
+    for k, v in data.items():
+        if "bytes_per_launch" in v:
+            ar = v["algorithmic_read_bytes"]
+            print(f"{k:16s} read {v['read_bytes'] / 1e6:9.2f} MB (alg {ar / 1e6 if ar else float('nan'):8.2f})  "
+                  f"write {v['write_bytes'] / 1e6:8.2f} MB  dispatches {v['dispatches']}")
 
 
 def decoder_layer_row(qb, dev, ev_time):
@@ -814,6 +861,18 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _cpu_model() -> str:
+    """The host CPU's model name (the first processor of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, step_flops, seconds):
     """Time the oracle (as it stands) for whole steps of the same workload on
     this host: quantize + dequantize (NumPy, one thread) and the fp64
@@ -841,8 +900,10 @@ def cpu_baseline(wl, step_flops, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = (time.perf_counter() - t0) / nsteps
-    log(f"cpu oracle: {dt:.2f} s per step on {threads} BLAS threads")
+    cpu_model = _cpu_model()
+    log(f"cpu oracle: {dt:.2f} s per step on {threads} BLAS threads ({cpu_model})")
     return {"value": step_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model, "host_logical_cpus": os.cpu_count(),
             "sample": f"{nsteps} whole oracle step(s) of the same workload (quantize, dequantize, "
                       f"fp64 fwd+bwd at M=4096), {dt:.2f} s per step",
             "s_per_step": dt}
