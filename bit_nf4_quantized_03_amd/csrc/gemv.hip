@@ -290,19 +290,31 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
   float *cs = reinterpret_cast<float *>(smem + kLutBytes);   // [RN][nblk] block constants
   __bf16 *xs = reinterpret_cast<__bf16 *>(smem + kXOffset);
 
-  // ---- prologue: the X slice and the block constants are read, staged in
-  // LDS and published before any code word is requested. They are small and
-  // mostly L2 hits, and issued behind the whole grid's code stream they
-  // would wait for it. Then every code word of the slice is requested at
-  // once, and quad-piece jq waits for its own code words only, so the decode
-  // runs while the rest of the slice streams in. Quad-pieces past the slice
-  // and a second block past the end of the chunk read a clamped, valid block
-  // and are scaled by 0.
+  // ---- prologue: the X slice and the block constants are requested first:
+  // they are small and mostly L2 hits, and issued behind the code stream they
+  // would wait for it (vector-memory counts retire in order). Every code word
+  // of the slice is requested at once, and quad-piece jq waits for its own
+  // code words only, so the decode runs while the rest of the slice streams
+  // in. Quad-pieces past the slice and a second block past the end of the
+  // chunk read a clamped, valid block and are scaled by 0.
   XStage<kXPieces> xst;
   xst.load(p.X, p.K, M, blk0 * kBlock, nblk * kBlock, nqp * 128);
   ScaleStage<kDq> sst;
   sst.load(p, static_cast<int64_t>(s) * RN, RN, kb, blk0, nblk);
   const float mu = kDq ? p.dq_mean[0] : 0.0f;
+  // With one row tile of X (M <= 8) the code words are requested right
+  // behind the X and constant loads, before the prologue's table and LDS
+  // stores: those wait only for the older loads, so the prologue runs while
+  // the code stream arrives. With two row tiles the prologue holds more
+  // registers and the requests go out after it (measured faster there).
+  auto blk_of = [&](int jq) { return min(2 * (q0 + min(jq, max(nq - 1, 0))) + half, nblk - 1); };
+  uint4 cw[NQ];
+  auto request_codes = [&]() {
+#pragma unroll
+    for (int jq = 0; jq < NQ; ++jq)
+      cw[jq] = *reinterpret_cast<const uint4 *>(p.codes + (rowblk + blk0 + blk_of(jq)) * (kBlock / 2) + 16 * (g & 1));
+  };
+  if constexpr (MT == 1) request_codes();
 
   // ---- the level-pair table, the X slice and the block constants into
   // LDS. Entry (byte e, copy c) at e * 16 + c holds (level[e >> 4],
@@ -324,11 +336,7 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
   // the zero row the A operand reads where it is zero (inactive lanes)
   reinterpret_cast<uint2 *>(smem + p.zoff)[tid] = make_uint2(0u, 0u);
   __syncthreads();
-  auto blk_of = [&](int jq) { return min(2 * (q0 + min(jq, max(nq - 1, 0))) + half, nblk - 1); };
-  uint4 cw[NQ];
-#pragma unroll
-  for (int jq = 0; jq < NQ; ++jq)
-    cw[jq] = *reinterpret_cast<const uint4 *>(p.codes + (rowblk + blk0 + blk_of(jq)) * (kBlock / 2) + 16 * (g & 1));
+  if constexpr (MT != 1) request_codes();
 
   // ---- decode + MFMA, quad-piece by quad-piece
   const float *crow = cs + (16 * t + ln) * nblk;   // this lane's weight row in the region
