@@ -28,12 +28,15 @@
 // strip's arrival counter; the last of the C to arrive sums the C partials in
 // chunk order, resets the counter and finishes the strip.
 //
-// Adapter workgroups. Unit u = (16 adapter columns, a range of the
-// reduction) forms that piece of H = X A^T with the fp32 rows of A rounded to
-// bf16 as MFMA operands, writes it, and marks it published in one flag word
-// per strip. A strip's finisher waits for its U flags (bounded), resets them,
-// sums the H pieces in a fixed order, and adds bf16(s H) bf16(B)^T on the
-// MFMA to its outputs before rounding Y to bf16.
+// Adapter workgroups. Unit u = (column group jg of 16 adapter columns, a
+// range hk of the reduction) forms that piece of H = X A^T with the fp32 rows
+// of A rounded to bf16 as MFMA operands, writes it and bumps its column
+// group's arrival counter. The last of the group's HK units to arrive resets
+// the counter, sums the group's pieces in range order into the final H
+// columns and marks them published in one flag word per strip. A strip's
+// finisher waits for its rp / 16 flags (bounded), resets them, reads H and
+// adds bf16(s H) bf16(B)^T on the MFMA to its outputs before rounding Y to
+// bf16.
 //
 // Cross-workgroup data (partials, H pieces, counters, flags) is written with
 // write-through stores (agent-scope relaxed atomic stores, sc1), made
@@ -90,7 +93,9 @@ struct GemvParams {
   __bf16 *Y;               // [M][N]
   float *part;             // [S][C][M][16 T] split partials (C > 1)
   float *hpart;            // [HK][M][rp] pieces of H
-  uint32_t *flags;         // [S][U]
+  float *hfin;             // [M][rp] H, summed by each column group's last unit
+  uint32_t *flags;         // [S][G], G = rp / 16 column groups
+  uint32_t *hctr;          // [G] adapter arrival counters
   uint32_t *ctr;           // [S]
   uint32_t *err;           // [1]
   int64_t M, N, K;
@@ -256,9 +261,23 @@ __device__ void adapter_unit(const GemvParams &p, char *smem) {
     }
   }
   wait_all_memory();
+  __syncthreads();   // this unit's piece is complete
+  uint32_t *last = reinterpret_cast<uint32_t *>(smem + kXOffset - 4);
+  if (tid == 0) *last = __hip_atomic_fetch_add(p.hctr + jg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (*last != static_cast<uint32_t>(p.HK - 1)) return;
+  // the group's last unit: H[m][16 jg + c] = sum over the HK pieces in range order
+  if (tid == 0) st_wt(p.hctr + jg, 0u);
+  for (int i = tid; i < M * 16; i += kGvThreads) {   // element (m, c) = (i / 16, i % 16) of the group
+    const int64_t off = static_cast<int64_t>(i >> 4) * p.rp + 16 * jg + (i & 15);
+    float v[1];
+    sum_wt<1>(p.hpart + off, static_cast<int64_t>(M) * p.rp, p.HK, 0, 0, 1, v);
+    st_wt(p.hfin + off, v[0]);
+  }
+  wait_all_memory();
   __syncthreads();
   // published: one flag per strip
-  for (int s = tid; s < p.S; s += kGvThreads) st_wt(p.flags + static_cast<int64_t>(s) * p.U + u, 1u);
+  for (int s = tid; s < p.S; s += kGvThreads) st_wt(p.flags + static_cast<int64_t>(s) * (p.rp / 16) + jg, 1u);
 }
 
 // ------------------------------------------------------------- weight strips
@@ -458,12 +477,11 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
   __bf16 *hs = xs;   // [MT16 * 16][rp + 8]
   const int hstride = p.rp + 8;
   if (p.r > 0) {
+    const int G = p.rp / 16;   // column groups: one flag each (at most 16)
     if (w == 0) {
-      uint32_t *fl = p.flags + static_cast<int64_t>(s) * p.U;
+      uint32_t *fl = p.flags + static_cast<int64_t>(s) * G;
       for (int spins = 0;; ++spins) {
-        bool mine = true;
-        for (int u0 = 0; u0 < p.U; u0 += 64)
-          if (u0 + lane < p.U) mine = mine && ld_wt(fl + u0 + lane) != 0u;
+        const bool mine = lane >= G || ld_wt(fl + lane) != 0u;
         if (__all(mine)) break;
         if (spins >= kSpinLimit) {
           if (lane == 0) atomicOr(p.err, 1u);
@@ -471,21 +489,14 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
         }
         __builtin_amdgcn_s_sleep(2);
       }
-      for (int u0 = 0; u0 < p.U; u0 += 64)
-        if (u0 + lane < p.U) st_wt(fl + u0 + lane, 0u);
+      if (lane < G) st_wt(fl + lane, 0u);
     }
     __syncthreads();
     const int nh = M * p.rp;   // H[m][j], m < M
-    for (int i = tid; i < 16 * MT16 * p.rp; i += 2 * kGvThreads) {
-      float v[2];
-      sum_wt<2>(p.hpart, static_cast<int64_t>(nh), p.HK, i, kGvThreads, nh, v);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int e = i + j * kGvThreads;
-        if (e >= 16 * MT16 * p.rp) continue;
-        const int m = e / p.rp, jj = e - m * p.rp;
-        hs[m * hstride + jj] = static_cast<__bf16>(e < nh && jj < p.r ? p.scale * v[j] : 0.0f);
-      }
+    for (int e = tid; e < 16 * MT16 * p.rp; e += kGvThreads) {
+      const int m = e / p.rp, jj = e - m * p.rp;
+      const float h = e < nh ? ld_wt(p.hfin + e) : 0.0f;
+      hs[m * hstride + jj] = static_cast<__bf16>(e < nh && jj < p.r ? p.scale * h : 0.0f);
     }
   }
   __syncthreads();
@@ -614,13 +625,16 @@ size_t part_bytes(const GemvPlan &pl, int64_t M) {
 
 bool gemv_sync_fits(int64_t M, int64_t N, int64_t K, int r) {
   const GemvPlan pl = gemv_plan(M, N, K, r);
-  return static_cast<size_t>(pl.S) * (pl.U + 1) * sizeof(uint32_t) + 256 <= kLinearSyncBytes;
+  // error word and strip counters, flags [S][G], adapter counters [G]
+  const int64_t G = pl.rp / 16;
+  return (64 + static_cast<size_t>(pl.S) * (G + 1) + G) * sizeof(uint32_t) <= kLinearSyncBytes;
 }
 
 size_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
   const GemvPlan pl = gemv_plan(M, N, K, r);
   return kLinearSyncBytes + part_bytes(pl, M) +
-         align_up(static_cast<size_t>(pl.HK) * M * pl.rp * sizeof(float), 256);
+         align_up(static_cast<size_t>(pl.HK) * M * pl.rp * sizeof(float), 256) +
+         align_up(static_cast<size_t>(M) * pl.rp * sizeof(float), 256);
 }
 
 hipError_t launch_gemv(const LinearArgs &a, const void *X, const float *A, const float *B, void *Y, void *ws,
@@ -653,13 +667,16 @@ hipError_t launch_gemv(const LinearArgs &a, const void *X, const float *A, const
   p.xstride = pl.xstride;
   p.zoff = pl.zoff;
   p.tab = format_tables(a.format);
-  // sync words: [0] error, [64 ..) strip counters [S], then flags [S][U]
+  // sync words: [0] error, [64 ..) strip counters [S], flags [S][G], adapter counters [G]
   char *base = static_cast<char *>(ws);
   p.err = reinterpret_cast<uint32_t *>(base);
   p.ctr = p.err + 64;
   p.flags = p.ctr + pl.S;
+  p.hctr = p.flags + static_cast<int64_t>(pl.S) * (pl.rp / 16);
   p.part = reinterpret_cast<float *>(base + kLinearSyncBytes);
   p.hpart = reinterpret_cast<float *>(base + kLinearSyncBytes + part_bytes(pl, a.M));
+  p.hfin = reinterpret_cast<float *>(base + kLinearSyncBytes + part_bytes(pl, a.M) +
+                                     align_up(static_cast<size_t>(pl.HK) * a.M * pl.rp * sizeof(float), 256));
   const unsigned grid = static_cast<unsigned>(pl.U + pl.S * pl.C);
   const int mt = static_cast<int>(ceil_div(a.M, 8));
   const bool dq = fmt_dq(a.format);
