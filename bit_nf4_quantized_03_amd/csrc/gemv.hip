@@ -322,10 +322,10 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
   sst.load(p, static_cast<int64_t>(s) * RN, RN, kb, blk0, nblk);
   const float mu = kDq ? p.dq_mean[0] : 0.0f;
   // With one row tile of X (M <= 8) the code words are requested right
-  // behind the X and constant loads, before the prologue's table and LDS
-  // stores: those wait only for the older loads, so the prologue runs while
-  // the code stream arrives. With two row tiles the prologue holds more
-  // registers and the requests go out after it (measured faster there).
+  // after the table is built, before the prologue's LDS stores of X and the
+  // constants: those wait only for the older loads, so the prologue finishes
+  // while the code stream arrives. With two row tiles the prologue holds
+  // more registers and the requests go out after it (measured faster there).
   auto blk_of = [&](int jq) { return min(2 * (q0 + min(jq, max(nq - 1, 0))) + half, nblk - 1); };
   uint4 cw[NQ];
   auto request_codes = [&]() {
@@ -333,7 +333,6 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
     for (int jq = 0; jq < NQ; ++jq)
       cw[jq] = *reinterpret_cast<const uint4 *>(p.codes + (rowblk + blk0 + blk_of(jq)) * (kBlock / 2) + 16 * (g & 1));
   };
-  if constexpr (MT == 1) request_codes();
 
   // ---- the level-pair table, the X slice and the block constants into
   // LDS. Entry (byte e, copy c) at e * 16 + c holds (level[e >> 4],
@@ -350,6 +349,7 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) lut[tid + kGvThreads * i] = pack_bf16x2(odd ? p.tab.lv[2 * i + 1] : p.tab.lv[2 * i], lo);
   }
+  if constexpr (MT == 1) request_codes();
   xst.store(p.xstride, xs);
   sst.store(mu, cs);
   // the zero row the A operand reads where it is zero (inactive lanes)
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
     }
   }
 
-  // ---- adapter: wait for the U pieces of H, sum them, bf16(s H) into LDS
+  // ---- adapter: wait for the column groups' flags, then bf16(s H) into LDS
   __bf16 *hs = xs;   // [MT16 * 16][rp + 8]
   const int hstride = p.rp + 8;
   if (p.r > 0) {
