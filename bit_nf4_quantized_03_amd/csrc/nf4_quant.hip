@@ -103,6 +103,15 @@ const CodeLut *code_lut(int format) {
   return luts.ok ? &luts.lut[(format & kFmtFp4) ? 1 : 0] : nullptr;
 }
 
+// The weight is read once and the codes are written once: streaming
+// (non-temporal) loads and stores, which keep them from displacing data that
+// is reused in the caches.
+__device__ __forceinline__ uint4 load_stream(const uint8_t *p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
 template <bool kBf16>
 struct InTraits;
 template <>
@@ -206,7 +215,7 @@ __device__ __forceinline__ float code_lane(const uint4 &raw, int64_t e, int64_t 
     word = byte[1] << 8 | byte[0];
   const int64_t byte0 = e / 2;
   if (!kGuard || e + kEpl <= n) {
-    if (kBf16) *reinterpret_cast<uint32_t *>(codes + byte0) = word;
+    if (kBf16) __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(codes + byte0));
     else *reinterpret_cast<uint16_t *>(codes + byte0) = static_cast<uint16_t>(word);
   } else {
     const int64_t nbytes = (n + 1) / 2;
@@ -247,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void k_absmax_codes(const uint8_t *__rest
   auto load = [&](int64_t d, uint4 *raw) {
     if (full(d)) {
 #pragma unroll
-      for (int p = 0; p < kPasses; ++p) raw[p] = *reinterpret_cast<const uint4 *>(W + elem(d, p) * kEsz);
+      for (int p = 0; p < kPasses; ++p) raw[p] = load_stream(W + elem(d, p) * kEsz);
     } else {
 #pragma unroll
       for (int p = 0; p < kPasses; ++p) {
@@ -279,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void k_absmax_codes(const uint8_t *__rest
   // compiler would wait for every load before the LDS store)
   if (d < nd && full(d)) {
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) raw[p] = *reinterpret_cast<const uint4 *>(W + elem(d, p) * kEsz);
+    for (int p = 0; p < kPasses; ++p) raw[p] = load_stream(W + elem(d, p) * kEsz);
     write_lut();
   } else {
     if (d < nd) load(d, raw);
@@ -531,7 +540,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict_
           bf16x8 pk;
 #pragma unroll
           for (int j = 0; j < 8; ++j) pk[j] = static_cast<__bf16>(v[j]);
-          *reinterpret_cast<bf16x8 *>(o) = pk;
+          // written once and not read again here: a streaming (non-temporal) store
+          __builtin_nontemporal_store(pk, reinterpret_cast<bf16x8 *>(o));
         } else {
           for (int j = 0; j < 8; ++j)
             if (e + j < n) o[j] = static_cast<__bf16>(v[j]);
