@@ -430,7 +430,9 @@ def main():
     dom = max(("fwd_gemm", "bwd_dx_gemm"), key=lambda k: rows[k]["us"])
 
     # ------------------------------- quantize / dequantize with rotation
-    R = max(2, ROTATE_BYTES // (2 * n + stored))
+    # enough distinct weights that the data each call reads (the bf16 weight
+    # for quantize, the codes for dequantize) exceeds the rotation bound
+    R = max(2, ROTATE_BYTES // (2 * n + stored) + 1, ROTATE_BYTES // stored + 1)
     Ws = [W] + [W.clone() for _ in range(R - 1)]
     qs = [qb.NF4Weight.empty(N, K, dev) for _ in range(R)]
     outs = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(R)]
@@ -484,6 +486,7 @@ def main():
     for k in ("quantize", "dequantize_bf16"):
         rows[k]["frac_of_hbm_peak"] = rows[k]["gbs"] / HBM_PEAK_GBS
     rows["quantize"]["rotation"] = R
+    rows["dequantize_bf16"]["rotation"] = R
     del Ws, qs, outs
     torch.cuda.empty_cache()
 
@@ -751,18 +754,21 @@ def main():
             del qm, Xm, dYm, Am, Bm, wsm, Ym, dXm, dAm, dBm
             torch.cuda.empty_cache()
 
-    # dequantize alone at the 65B shapes (bf16 and fp32 out), two rotating sets
+    # dequantize alone at the 65B shapes (bf16 and fp32 out), rotating over
+    # enough weights that the codes read exceed the rotation bound (the
+    # streaming output stores leave the codes in the last-level cache otherwise)
     dq_solo = {}
     if not args.no_large:
         for name, (Nq, Kq) in (("up65b", (22016, 8192)), ("attn65b", (8192, 8192))):
             st = qb.qlora_nf4_storage_bytes(Nq, Kq)
-            qs2 = [qb.qlora_nf4_quantize(dev_normal((Nq, Kq), 0.02, 500 + i)) for i in range(2)]
+            Rq = max(2, ROTATE_BYTES // st + 1)
+            qs2 = [qb.qlora_nf4_quantize(dev_normal((Nq, Kq), 0.02, 500 + i)) for i in range(Rq)]
             for dt, esz in ((torch.bfloat16, 2), (torch.float32, 4)):
-                outs2 = [torch.empty((Nq, Kq), dtype=dt, device=dev) for _ in range(2)]
-                ms = ev_time(lambda: [qb.qlora_nf4_dequantize(qs2[i], dt, out=outs2[i]) for i in range(2)], 5) / 2
+                outs2 = [torch.empty((Nq, Kq), dtype=dt, device=dev) for _ in range(Rq)]
+                ms = ev_time(lambda: [qb.qlora_nf4_dequantize(qs2[i], dt, out=outs2[i]) for i in range(Rq)], 3) / Rq
                 byts = st + esz * Nq * Kq
                 key = f"{name}_{'bf16' if esz == 2 else 'f32'}"
-                dq_solo[key] = {"N": Nq, "K": Kq, "us": ms * 1e3, "bytes": byts,
+                dq_solo[key] = {"N": Nq, "K": Kq, "us": ms * 1e3, "bytes": byts, "rotation": Rq,
                                 "gbs": byts / (ms * 1e-3) / 1e9,
                                 "frac_of_hbm_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
                 log(f"dequantize {key}: {ms * 1e3:.1f} us, {dq_solo[key]['gbs']:.0f} GB/s")
