@@ -5,7 +5,13 @@
 // block-wise dequantization of the 4-bit base in the forward pass; capability
 // "LoRA on the quantized base": a frozen base plus a full-precision adapter).
 //
-// Grid = U adapter workgroups, then S x C weight workgroups.
+// Two kernels. One row of X with K <= 16384 (single-token decode) takes the
+// row-stream kernel k_gemv_rows further down: no matrix cores, X in
+// registers, the levels through a byte-indexed table and v_dot2_f32_bf16.
+// Everything else (M = 2 .. 32, longer rows, or an adapter whose published
+// columns would not fit the synchronization words) takes k_gemv, below.
+//
+// k_gemv: grid = U adapter workgroups, then S x C weight workgroups.
 //
 // Weight workgroups. Strip s owns 16 T consecutive weight rows (outputs n);
 // its C workgroups split the reduction into chunks whose slice of X fits in
@@ -63,6 +69,7 @@ namespace qnf4 {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kGvWaves = 8;
 constexpr int kGvThreads = 64 * kGvWaves;
@@ -107,6 +114,7 @@ struct GemvParams {
   int hstep;               // blocks per adapter step (16, or 8 when M > 16)
   int xstride;             // bf16 per X row in LDS
   int zoff;                // byte offset in LDS of a zero row of kZeroBytes
+  int rs_nw, rs_P, rs_RW;  // row-stream path: waves per row, rows per pass, rows per workgroup
   Nf4Tables tab;
 };
 
@@ -542,6 +550,343 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
     }
 }
 
+// ------------------------------------------------------- row-stream path
+// One row of X (M = 1) and K <= 16384: no matrix cores, two workgroups per
+// CU. Workgroup b owns 8 P consecutive weight rows, whole: 8 passes of P
+// rows. A row is split into K / 32 chunks of 16 code bytes (32 elements,
+// half a 64-block); thread (row slot rs, chunk slot j) reads chunk j of row
+// rs of every pass, so the 64 lanes of a wave read 1 KB of one row per load
+// instruction and each thread's 32 elements of X stay in registers for the
+// whole call. Every load of the workgroup (X slice, A row, B rows, then the
+// 8 passes' code chunks, int8 constants and DQ scales) is issued at the
+// start, in the order it is needed; the passes are then consumed in order,
+// with no branch between them. A code byte becomes its bf16 level pair
+// through a table in LDS (address: one byte permute of the code word with
+// the lane's copy offset), v_dot2_f32_bf16 multiplies the pair with the X
+// pair in the register, and the chunk's sum is scaled by its block constant
+// c_b. The 8 passes' sums are reduce-scattered across the wave (three
+// halving exchanges, then three full ones); one lane per row writes the
+// wave's partial to LDS, and the waves of a row are added in wave order at
+// the end.
+//
+// Adapter: column j of H = X A^T is formed in fp32 by the row slot that owns
+// it (workgroup b, slot rs: columns b + Gw (rs + P t)), round t = 0 from the
+// X registers and the A row loaded at the start, after the first passes,
+// rounds t > 0 after all passes. A column is published as one write-through
+// store of its value into every workgroup's own slot (a word that is zero
+// until published: +0 is stored as -0), so it needs no wait for earlier
+// stores and no counter. After its passes every workgroup waits (bounded)
+// until its r words are nonzero, clears them, and adds s (X A^T) B^T in fp32
+// to its rows, B rows having been loaded at the start. So every word is zero
+// between calls.
+constexpr int kRsEntry = 256;                  // bytes between table entries
+constexpr int kRsLds = 256 * kRsEntry;         // 64 KB: 32 copies of an entry fill the first half of its stride
+constexpr int kRsAux = 256 * 32;               // floats in the second halves (partials, B rows, s H)
+constexpr int kRsPasses = 8;                   // passes per workgroup (of P rows each)
+constexpr int kRsBpre = 4;                     // B values per thread loaded at the start: RW r <= 4 * 512
+constexpr int kRsMaxChunks = 64 * kGvWaves;    // K <= 16384
+constexpr int kRsHword0 = 256;                 // sync word of the H slots: [Gw][r] fp32 bits, 0 = not yet published
+
+__device__ __forceinline__ float *rs_aux(char *smem, int i) {
+  return reinterpret_cast<float *>(smem + (i >> 5) * kRsEntry + 128 + 4 * (i & 31));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// Raw buffer loads: a load whose offset lies past the buffer's end returns
+// zero without a memory access, so every load of the row-stream kernel is
+// issued unconditionally (no branch around a load, whose join would make the
+// compiler wait for every load in flight) and the ones that must not happen
+// get kOob.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t buf_b32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ int buf_i8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return static_cast<int>(static_cast<int8_t>(__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0)));
+}
+
+// fp32(s / 127) for s >= 0 in three operations: the product with fp32(1/127)
+// corrected once by its fused remainder. Equal to the correctly rounded
+// quotient for every finite fp32 s (checked exhaustively on the host; only
+// s = -0 differs, in the sign of the zero).
+__device__ __forceinline__ float div127(float s) {
+  const float c = 1.0f / 127.0f;
+  const float q0 = s * c;
+  return __builtin_fmaf(__builtin_fmaf(-q0, 127.0f, s), c, q0);
+}
+
+template <bool kDq>
+__global__ __launch_bounds__(kGvThreads, 4) void k_gemv_rows(GemvParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[kRsLds];
+  constexpr int NP = kRsPasses;   // passes per workgroup
+  constexpr int D = 4;            // passes in flight
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nw = p.rs_nw, P = p.rs_P, RW = p.rs_RW, Gw = p.S;
+  const int C = static_cast<int>(p.K / 32);
+  const int64_t kb = p.K / kBlock;
+  const int b = blockIdx.x;
+  const int64_t n0 = static_cast<int64_t>(b) * RW;
+  const int rows = static_cast<int>(min<int64_t>(RW, p.N - n0));
+  const int rs = w / nw, wr = w - rs * nw;
+  const bool wave_on = rs < P;   // uniform per wave
+  const int j = wr * 64 + lane;
+  const bool jon = wave_on && j < C;
+  // aux floats: row partials [nw][RW], B rows [RW][r], s H [r], H partials [8 waves], H columns [P]
+  const int a_b = nw * RW, a_h = a_b + RW * p.r, a_hp = a_h + p.r;
+  const int jcol = b + Gw * rs;   // this slot's first adapter column
+  const bool producer = p.r > 0 && wave_on && jcol < p.r;
+
+  // ---- small requests first: DQ mean, X slice (zero for idle lanes), A row
+  // of the slot's first column, B rows. All are vector loads: a scalar load
+  // would hold up the first barrier (which waits for every scalar and LDS
+  // access) until it came back from behind the grid's code stream.
+  const float mu = kDq ? __uint_as_float(buf_b32(buf(p.dq_mean, 4), 0)) : 0.0f;
+  uint32_t xr[16];
+  {
+    const __amdgpu_buffer_rsrc_t bx = buf(p.X, p.K * 2);
+    const uint32_t off = jon ? static_cast<uint32_t>(64 * j) : kOob;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = buf_b128(bx, off + 16u * q);
+      xr[4 * q] = v.x;
+      xr[4 * q + 1] = v.y;
+      xr[4 * q + 2] = v.z;
+      xr[4 * q + 3] = v.w;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t ba = buf(p.A, p.r > 0 ? static_cast<int64_t>(p.r) * p.K * 4 : 0);
+  float4 arow[8];
+  {
+    const uint32_t off = producer && jon ? static_cast<uint32_t>((static_cast<int64_t>(jcol) * p.K + 32 * j) * 4) : kOob;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 v = buf_b128(ba, off + 16u * i);
+      arow[i] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+    }
+  }
+  const int nbe = rows * p.r;
+  float bpre[kRsBpre];
+  {
+    const __amdgpu_buffer_rsrc_t bbr = buf(p.r > 0 ? p.B + n0 * p.r : p.B, static_cast<int64_t>(nbe) * 4);
+#pragma unroll
+    for (int i = 0; i < kRsBpre; ++i) {
+      const int e = tid + kGvThreads * i;
+      bpre[i] = __uint_as_float(buf_b32(bbr, e < nbe ? static_cast<uint32_t>(e) * 4u : kOob));
+    }
+  }
+
+  // ---- the passes' loads, D ahead (the first D before the table is built,
+  // so the code stream starts at once): code chunk, int8 constant, DQ scale
+  uint4 cw[D];
+  int qv[D];
+  float fv[D];
+  const int64_t gblk0 = n0 * kb;
+  const __amdgpu_buffer_rsrc_t bc = buf(p.codes + n0 * (p.K / 2), static_cast<int64_t>(rows) * (p.K / 2));
+  const __amdgpu_buffer_rsrc_t bq = kDq ? buf(p.absmax_q + gblk0, static_cast<int64_t>(rows) * kb)
+                                        : buf(p.absmax + gblk0, static_cast<int64_t>(rows) * kb * 4);
+  const __amdgpu_buffer_rsrc_t bs = buf(p.dq_scale, kDq ? (p.N * kb + kDqBlock - 1) / kDqBlock * 4 : 0);
+  auto issue = [&](int i) {
+    const int rl = i * P + rs, slot = i % D;
+    const bool ok = jon && i < NP && rl < rows;
+    const uint32_t lb = static_cast<uint32_t>(rl * kb + (j >> 1));   // block within the workgroup's rows
+    cw[slot] = buf_b128(bc, ok ? lb * 32u + 16u * (j & 1) : kOob);
+    if constexpr (kDq) {
+      qv[slot] = buf_i8(bq, ok ? lb : kOob);
+      fv[slot] = __uint_as_float(buf_b32(bs, ok ? static_cast<uint32_t>((gblk0 + lb) / kDqBlock) * 4u : kOob));
+    } else {
+      fv[slot] = __uint_as_float(buf_b32(bq, ok ? lb * 4u : kOob));
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < D; ++i) issue(i);
+
+  // ---- table: entry e (code byte) = (bf16 level[e >> 4], bf16 level[e & 15]),
+  // copy c at byte e * 256 + 4 c. Thread tid writes copies 4 (tid % 8) .. + 3
+  // of entries tid / 8 + 64 i, so that a half-wave's 16-byte stores cover all
+  // banks. The levels are kernel-argument constants picked by selects.
+  {
+    const int e0 = tid >> 3, lo_i = e0 & 15;
+    const int hi0 = __builtin_amdgcn_readfirstlane(e0 >> 4);   // wave-uniform
+    float lo = p.tab.lv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) lo = lo_i == i ? p.tab.lv[i] : lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float hi = p.tab.lv[4 * i];
+#pragma unroll
+      for (int h = 1; h < 4; ++h) hi = hi0 == h ? p.tab.lv[4 * i + h] : hi;
+      const uint32_t v = pack_bf16x2(hi, lo);
+      *reinterpret_cast<uint4 *>(smem + (e0 + 64 * i) * kRsEntry + 16 * (tid & 7)) = make_uint4(v, v, v, v);
+    }
+  }
+  __syncthreads();   // table ready (waits for LDS and scalar accesses only)
+
+  // ---- the slot's adapter column over this wave's chunks, parked in LDS
+  auto h_partial = [&]() {
+    float h = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 a = arow[i];
+      h = __builtin_fmaf(bf16_lo(xr[2 * i]), a.x, h);
+      h = __builtin_fmaf(bf16_hi(xr[2 * i]), a.y, h);
+      h = __builtin_fmaf(bf16_lo(xr[2 * i + 1]), a.z, h);
+      h = __builtin_fmaf(bf16_hi(xr[2 * i + 1]), a.w, h);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) h += __shfl_xor(h, off, 64);
+    if (lane == 0) *rs_aux(smem, a_hp + w) = h;
+  };
+  uint32_t *hw = p.err + kRsHword0;   // [Gw][r] fp32 bits, 0 until published
+  // publish round t's columns: H[0][js] = the slot's waves' partials in wave
+  // order, into every workgroup's slot (call after a barrier that follows
+  // h_partial; ends with one)
+  auto publish = [&](int t) {
+    if (tid < P) {
+      float hv = 0.0f;
+      for (int ww = 0; ww < nw; ++ww) hv += *rs_aux(smem, a_hp + tid * nw + ww);
+      *rs_aux(smem, a_hp + kGvWaves + tid) = hv;
+    }
+    __syncthreads();
+    for (int srs = 0; srs < P; ++srs) {
+      const int js = b + Gw * (srs + P * t);
+      if (js >= p.r) break;
+      const uint32_t hb = __float_as_uint(*rs_aux(smem, a_hp + kGvWaves + srs));
+      const uint32_t word = hb == 0u ? 0x80000000u : hb;   // +0 published as -0
+      for (int g = tid; g < Gw; g += kGvThreads) st_wt(hw + static_cast<int64_t>(g) * p.r + js, word);
+    }
+    __syncthreads();
+  };
+
+  // ---- passes: 4 accumulators per pass (one per code word); after pass 1
+  // the adapter columns (their X and A requests were issued before the
+  // passes', so they have arrived); then the reduce-scatter of the 8 sums
+  const uint32_t lane4 = 4u * static_cast<uint32_t>(lane & 31);
+  float v[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    if (wave_on) {   // uniform; no load inside
+      const int slot = i % D;
+      const uint4 c = cw[slot];
+      const float cb = kDq ? __fadd_rn(__fmul_rn(static_cast<float>(qv[slot]), div127(fv[slot])), mu) : fv[slot];
+      float sq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t wq = q == 0 ? c.x : q == 1 ? c.y : q == 2 ? c.z : c.w;
+        float s = 0.0f;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const uint32_t addr = __builtin_amdgcn_perm(wq, lane4, 0x0C0C0400u | (static_cast<uint32_t>(bb) << 8));
+          const uint32_t pr = *reinterpret_cast<const uint32_t *>(smem + addr);
+          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr), __builtin_bit_cast(bf16x2_t, xr[4 * q + bb]),
+                                              s, false);
+        }
+        sq[q] = s;
+      }
+      v[i] = cb * ((sq[0] + sq[1]) + (sq[2] + sq[3]));
+    }
+    issue(i + D);
+    if (i == 1 && b < p.r) {   // workgroup-uniform: it owns adapter columns
+      if (producer) h_partial();
+      __syncthreads();
+      publish(0);
+    }
+  }
+  if (wave_on) {
+#pragma unroll
+    for (int st = 0; st < 3; ++st) {
+      const int mask = 32 >> st, half = 4 >> st;
+      const bool hi = (lane & mask) != 0;
+#pragma unroll
+      for (int u = 0; u < half; ++u) {
+        const float keep = hi ? v[u + half] : v[u];
+        const float give = hi ? v[u] : v[u + half];
+        v[u] = keep + __shfl_xor(give, mask, 64);
+      }
+    }
+    float t = v[0];
+    t += __shfl_xor(t, 4, 64);
+    t += __shfl_xor(t, 2, 64);
+    t += __shfl_xor(t, 1, 64);
+    // lanes 8 i .. 8 i + 7 hold pass i
+    const int rl = (lane >> 3) * P + rs;
+    if ((lane & 7) == 0 && rl < rows) *rs_aux(smem, wr * RW + rl) = t;
+  }
+
+  if (p.r > 0) {
+    // ---- rounds t > 0 of this workgroup's columns (r > Gw P)
+    for (int t = 1; b + Gw * P * t < p.r; ++t) {
+      __syncthreads();   // round t - 1's partials have been read
+      const int jt = jcol + Gw * P * t;
+      if (wave_on && jt < p.r) {   // wave-uniform
+        const uint32_t off = jon ? static_cast<uint32_t>((static_cast<int64_t>(jt) * p.K + 32 * j) * 4) : kOob;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint4 v = buf_b128(ba, off + 16u * i);
+          arow[i] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+        }
+        h_partial();
+      }
+      __syncthreads();
+      publish(t);
+    }
+    // ---- B rows into LDS; wait until every H word is flagged, s H into LDS
+#pragma unroll
+    for (int i = 0; i < kRsBpre; ++i) {
+      const int e = tid + kGvThreads * i;
+      if (e < nbe) *rs_aux(smem, a_b + e) = bpre[i];
+    }
+    if (w == 0) {
+      uint32_t *mine = hw + static_cast<int64_t>(b) * p.r;
+      for (int j0 = 0; j0 < p.r; j0 += 64) {
+        const int jj = j0 + lane;
+        uint32_t hv = 0;
+        for (int spins = 0;; ++spins) {
+          if (jj < p.r) hv = ld_wt(mine + jj);
+          if (__all(jj >= p.r || hv != 0u)) break;
+          if (spins >= kSpinLimit) {
+            if (lane == 0) atomicOr(p.err, 1u);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        if (jj < p.r) {
+          *rs_aux(smem, a_h + jj) = p.scale * __uint_as_float(hv);
+          st_wt(mine + jj, 0u);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- outputs: 16 threads per row (32 rows at a time); the adapter term
+  // over j = seg, seg + 16, ... then summed across the 16, added to the
+  // row's wave partials in wave order
+  for (int r0 = 0; r0 < rows; r0 += kGvThreads / 16) {
+    const int rl = r0 + tid / 16, seg = tid & 15;
+    float ad = 0.0f;
+    if (rl < rows)
+      for (int jj = seg; jj < p.r; jj += 16) ad = __builtin_fmaf(*rs_aux(smem, a_h + jj), *rs_aux(smem, a_b + rl * p.r + jj), ad);
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) ad += __shfl_xor(ad, off, 16);
+    if (seg == 0 && rl < rows) {
+      float y = 0.0f;
+      for (int ww = 0; ww < nw; ++ww) y += *rs_aux(smem, ww * RW + rl);
+      p.Y[n0 + rl] = static_cast<__bf16>(y + ad);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ planning
 
 struct GemvPlan {
@@ -549,7 +894,34 @@ struct GemvPlan {
   int U, HK, hb, hstep, rp;
   int xstride, zoff;
   size_t lds;
+  bool rows;          // row-stream path (S = its workgroups)
+  int nw, P, RW;
 };
+
+// Row-stream plan (M = 1): 8 passes of P rows per workgroup, fewer when the
+// B rows or the LDS aux space would not hold them.
+bool rows_plan(int64_t M, int64_t N, int64_t K, int r, GemvPlan &pl) {
+  const int64_t C = K / 32;
+  if (M != 1 || C > kRsMaxChunks || r > 256) return false;
+  const int nw = static_cast<int>(ceil_div(C, 64));
+  const int P = std::max(1, kGvWaves / nw);
+  auto fits = [&](int64_t rw) {
+    return rw * r <= kRsBpre * kGvThreads && nw * rw + rw * r + r + kGvWaves + P <= kRsAux;
+  };
+  int64_t RW = static_cast<int64_t>(P) * kRsPasses;
+  while (RW > P && !fits(RW)) RW -= P;
+  // every workgroup's H slot in the synchronization words
+  if (!fits(RW) || (kRsHword0 + ceil_div(N, RW) * r) * 4 > static_cast<int64_t>(kLinearSyncBytes)) return false;
+  pl.rows = true;
+  pl.nw = nw;
+  pl.P = P;
+  pl.RW = static_cast<int>(RW);
+  pl.S = static_cast<int>(ceil_div(N, RW));
+  pl.C = 1;
+  pl.U = 0;
+  pl.lds = 0;
+  return true;
+}
 
 GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int r) {
   GemvPlan pl{};
@@ -591,6 +963,7 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K, int r) {
   const size_t hbytes = static_cast<size_t>(16 * mt16) * (pl.rp + 8) * 2;
   pl.zoff = static_cast<int>(align_up(kXOffset + std::max(xbytes, hbytes), 16));
   pl.lds = pl.zoff + kZeroBytes;
+  rows_plan(M, N, K, r, pl);
   return pl;   // pl.lds <= kGvLdsMax: X slice <= kXLdsMax, adapter X <= 32 x 520 x 2, H <= 32 x 264 x 2
 }
 
@@ -617,6 +990,11 @@ void launch_mt(int nq, bool dq, unsigned grid, size_t lds, hipStream_t s, const 
   else launch_mt_nq<MT, 16>(dq, grid, lds, s, p);
 }
 
+template <bool kDq>
+void launch_rows(unsigned grid, hipStream_t s, const GemvParams &p) {
+  hipLaunchKernelGGL((k_gemv_rows<kDq>), dim3(grid), dim3(kGvThreads), 0, s, p);
+}
+
 size_t part_bytes(const GemvPlan &pl, int64_t M) {
   return pl.C > 1 ? align_up(static_cast<size_t>(pl.S) * pl.C * M * 16 * pl.T * sizeof(float), 256) : 0;
 }
@@ -625,6 +1003,7 @@ size_t part_bytes(const GemvPlan &pl, int64_t M) {
 
 bool gemv_sync_fits(int64_t M, int64_t N, int64_t K, int r) {
   const GemvPlan pl = gemv_plan(M, N, K, r);
+  if (pl.rows) return true;   // error word and two counters
   // error word and strip counters, flags [S][G], adapter counters [G]
   const int64_t G = pl.rp / 16;
   return (64 + static_cast<size_t>(pl.S) * (G + 1) + G) * sizeof(uint32_t) <= kLinearSyncBytes;
@@ -666,6 +1045,9 @@ hipError_t launch_gemv(const LinearArgs &a, const void *X, const float *A, const
   p.hstep = pl.hstep;
   p.xstride = pl.xstride;
   p.zoff = pl.zoff;
+  p.rs_nw = pl.nw;
+  p.rs_P = pl.P;
+  p.rs_RW = pl.RW;
   p.tab = format_tables(a.format);
   // sync words: [0] error, [64 ..) strip counters [S], flags [S][G], adapter counters [G]
   char *base = static_cast<char *>(ws);
@@ -681,7 +1063,10 @@ hipError_t launch_gemv(const LinearArgs &a, const void *X, const float *A, const
   const int mt = static_cast<int>(ceil_div(a.M, 8));
   const bool dq = fmt_dq(a.format);
   prof_begin(kProfFwdGemm, s);
-  if (mt == 1) launch_mt<1>(pl.nq_max, dq, grid, pl.lds, s, p);
+  if (pl.rows) {
+    if (dq) launch_rows<true>(grid, s, p);
+    else launch_rows<false>(grid, s, p);
+  } else if (mt == 1) launch_mt<1>(pl.nq_max, dq, grid, pl.lds, s, p);
   else if (mt == 2) launch_mt<2>(pl.nq_max, dq, grid, pl.lds, s, p);
   else launch_mt<4>(pl.nq_max, dq, grid, pl.lds, s, p);
   prof_end(kProfFwdGemm, s);

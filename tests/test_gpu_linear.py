@@ -94,7 +94,7 @@ def test_tiny_fwd_bwd(qb, cb):
     _bwd(qb, c, "tiny")
 
 
-@pytest.mark.parametrize("M", [1, 4, 16, 17, 33, 130, 300])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 16, 17, 33, 130, 300])
 @pytest.mark.parametrize("r", [0, 8, 64, 72])
 def test_ragged_m_and_rank(qb, cb, M, r):
     wl = synth.make_linear_workload("ragged", M=M, N=320, K=448, r=r, alpha=16.0,
@@ -117,7 +117,7 @@ def test_max_rank(qb, cb, M):
     _bwd(qb, c, f"max rank M={M}")
 
 
-@pytest.mark.parametrize("M", [1, 7, 16, 23, 32])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 7, 16, 23, 32])
 @pytest.mark.parametrize("r", [0, 8, 72])
 def test_decode_split_k_ragged(qb, cb, M, r):
     """Skinny-M forward with several K splits, a short last split, K not a
@@ -126,6 +126,17 @@ def test_decode_split_k_ragged(qb, cb, M, r):
                                     seed=7000 + M * 10 + r, w_dtype="bf16")
     c = Case(qb, wl, cb)
     _fwd(qb, c, f"decode-ragged M={M} r={r}")
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_decode_long_rows(qb, cb, M):
+    """K = 16448 (514 chunks of 32 elements per row, past what the row-stream
+    decode keeps in registers): the matrix-core decode path at M <= 4, with
+    r = 9."""
+    wl = synth.make_linear_workload("decode-long", M=M, N=128, K=16448, r=9, alpha=16.0,
+                                    seed=7100 + M, w_dtype="bf16")
+    c = Case(qb, wl, cb)
+    _fwd(qb, c, f"decode-long M={M}")
 
 
 def test_identity_input_gives_exact_weight(qb, cb):
