@@ -582,9 +582,12 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
 constexpr int kRsEntry = 256;                  // bytes between table entries
 constexpr int kRsLds = 256 * kRsEntry;         // 64 KB: 32 copies of an entry fill the first half of its stride
 constexpr int kRsAux = 256 * 32;               // floats in the second halves (partials, B rows, s H)
-constexpr int kRsPasses = 8;                   // passes per workgroup (of P rows each)
-constexpr int kRsBpre = 4;                     // B values per thread loaded at the start: RW r <= 4 * 512
-constexpr int kRsMaxChunks = 64 * kGvWaves;    // K <= 16384
+constexpr int kRsThreads = 1024;               // one workgroup per CU: 16 waves
+constexpr int kRsWaves = kRsThreads / 64;
+constexpr int kRsPasses = 8;                   // passes per workgroup at most (of P rows each)
+constexpr int kRsBpre = 4;                     // B values per thread loaded at the start: RW r <= 4 * 1024
+constexpr int kRsMaxChunks = 64 * 8;           // K <= 16384: at most 8 waves per row
+constexpr int kRsCus = 256;                    // compute units of the GPU
 constexpr int kRsHword0 = 256;                 // sync word of the H slots: [Gw][r] fp32 bits, 0 = not yet published
 
 __device__ __forceinline__ float *rs_aux(char *smem, int i) {
@@ -627,9 +630,9 @@ __device__ __forceinline__ float div127(float s) {
 }
 
 template <bool kDq>
-__global__ __launch_bounds__(kGvThreads, 4) void k_gemv_rows(GemvParams p) {
+__global__ __launch_bounds__(kRsThreads) void k_gemv_rows(GemvParams p) {
   __shared__ __attribute__((aligned(16))) char smem[kRsLds];
-  constexpr int NP = kRsPasses;   // passes per workgroup
+  constexpr int NP = kRsPasses;   // passes per workgroup at most
   constexpr int D = 4;            // passes in flight
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nw = p.rs_nw, P = p.rs_P, RW = p.rs_RW, Gw = p.S;
@@ -638,11 +641,12 @@ __global__ __launch_bounds__(kGvThreads, 4) void k_gemv_rows(GemvParams p) {
   const int b = blockIdx.x;
   const int64_t n0 = static_cast<int64_t>(b) * RW;
   const int rows = static_cast<int>(min<int64_t>(RW, p.N - n0));
+  const int npass = (rows + P - 1) / P;
   const int rs = w / nw, wr = w - rs * nw;
   const bool wave_on = rs < P;   // uniform per wave
   const int j = wr * 64 + lane;
   const bool jon = wave_on && j < C;
-  // aux floats: row partials [nw][RW], B rows [RW][r], s H [r], H partials [8 waves], H columns [P]
+  // aux floats: row partials [nw][RW], B rows [RW][r], s H [r], H partials [16 waves], H columns [P]
   const int a_b = nw * RW, a_h = a_b + RW * p.r, a_hp = a_h + p.r;
   const int jcol = b + Gw * rs;   // this slot's first adapter column
   const bool producer = p.r > 0 && wave_on && jcol < p.r;
@@ -681,7 +685,7 @@ __global__ __launch_bounds__(kGvThreads, 4) void k_gemv_rows(GemvParams p) {
     const __amdgpu_buffer_rsrc_t bbr = buf(p.r > 0 ? p.B + n0 * p.r : p.B, static_cast<int64_t>(nbe) * 4);
 #pragma unroll
     for (int i = 0; i < kRsBpre; ++i) {
-      const int e = tid + kGvThreads * i;
+      const int e = tid + kRsThreads * i;
       bpre[i] = __uint_as_float(buf_b32(bbr, e < nbe ? static_cast<uint32_t>(e) * 4u : kOob));
     }
   }
@@ -698,7 +702,7 @@ __global__ __launch_bounds__(kGvThreads, 4) void k_gemv_rows(GemvParams p) {
   const __amdgpu_buffer_rsrc_t bs = buf(p.dq_scale, kDq ? (p.N * kb + kDqBlock - 1) / kDqBlock * 4 : 0);
   auto issue = [&](int i) {
     const int rl = i * P + rs, slot = i % D;
-    const bool ok = jon && i < NP && rl < rows;
+    const bool ok = jon && i < npass && rl < rows;
     const uint32_t lb = static_cast<uint32_t>(rl * kb + (j >> 1));   // block within the workgroup's rows
     cw[slot] = buf_b128(bc, ok ? lb * 32u + 16u * (j & 1) : kOob);
     if constexpr (kDq) {
@@ -711,23 +715,24 @@ __global__ __launch_bounds__(kGvThreads, 4) void k_gemv_rows(GemvParams p) {
 #pragma unroll
   for (int i = 0; i < D; ++i) issue(i);
 
+
   // ---- table: entry e (code byte) = (bf16 level[e >> 4], bf16 level[e & 15]),
   // copy c at byte e * 256 + 4 c. Thread tid writes copies 4 (tid % 8) .. + 3
-  // of entries tid / 8 + 64 i, so that a half-wave's 16-byte stores cover all
+  // of entries tid / 8 + 128 i, so that a half-wave's 16-byte stores cover all
   // banks. The levels are kernel-argument constants picked by selects.
   {
     const int e0 = tid >> 3, lo_i = e0 & 15;
-    const int hi0 = __builtin_amdgcn_readfirstlane(e0 >> 4);   // wave-uniform
+    const int hi0 = __builtin_amdgcn_readfirstlane(e0 >> 4);   // wave-uniform, 0 .. 7
     float lo = p.tab.lv[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) lo = lo_i == i ? p.tab.lv[i] : lo;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float hi = p.tab.lv[4 * i];
+    for (int i = 0; i < 2; ++i) {
+      float hi = p.tab.lv[8 * i];
 #pragma unroll
-      for (int h = 1; h < 4; ++h) hi = hi0 == h ? p.tab.lv[4 * i + h] : hi;
+      for (int h = 1; h < 8; ++h) hi = hi0 == h ? p.tab.lv[8 * i + h] : hi;
       const uint32_t v = pack_bf16x2(hi, lo);
-      *reinterpret_cast<uint4 *>(smem + (e0 + 64 * i) * kRsEntry + 16 * (tid & 7)) = make_uint4(v, v, v, v);
+      *reinterpret_cast<uint4 *>(smem + (e0 + 128 * i) * kRsEntry + 16 * (tid & 7)) = make_uint4(v, v, v, v);
     }
   }
   __syncthreads();   // table ready (waits for LDS and scalar accesses only)
@@ -755,15 +760,15 @@ __global__ __launch_bounds__(kGvThreads, 4) void k_gemv_rows(GemvParams p) {
     if (tid < P) {
       float hv = 0.0f;
       for (int ww = 0; ww < nw; ++ww) hv += *rs_aux(smem, a_hp + tid * nw + ww);
-      *rs_aux(smem, a_hp + kGvWaves + tid) = hv;
+      *rs_aux(smem, a_hp + kRsWaves + tid) = hv;
     }
     __syncthreads();
     for (int srs = 0; srs < P; ++srs) {
       const int js = b + Gw * (srs + P * t);
       if (js >= p.r) break;
-      const uint32_t hb = __float_as_uint(*rs_aux(smem, a_hp + kGvWaves + srs));
+      const uint32_t hb = __float_as_uint(*rs_aux(smem, a_hp + kRsWaves + srs));
       const uint32_t word = hb == 0u ? 0x80000000u : hb;   // +0 published as -0
-      for (int g = tid; g < Gw; g += kGvThreads) st_wt(hw + static_cast<int64_t>(g) * p.r + js, word);
+      for (int g = tid; g < Gw; g += kRsThreads) st_wt(hw + static_cast<int64_t>(g) * p.r + js, word);
     }
     __syncthreads();
   };
@@ -774,8 +779,10 @@ __global__ __launch_bounds__(kGvThreads, 4) void k_gemv_rows(GemvParams p) {
   const uint32_t lane4 = 4u * static_cast<uint32_t>(lane & 31);
   float v[NP];
 #pragma unroll
+  for (int i = 0; i < NP; ++i) v[i] = 0.0f;
+#pragma unroll
   for (int i = 0; i < NP; ++i) {
-    if (wave_on) {   // uniform; no load inside
+    if (wave_on && i < npass) {   // uniform; no load inside
       const int slot = i % D;
       const uint4 c = cw[slot];
       const float cb = kDq ? __fadd_rn(__fmul_rn(static_cast<float>(qv[slot]), div127(fv[slot])), mu) : fv[slot];
@@ -843,7 +850,7 @@ __global__ __launch_bounds__(kGvThreads, 4) void k_gemv_rows(GemvParams p) {
     // ---- B rows into LDS; wait until every H word is flagged, s H into LDS
 #pragma unroll
     for (int i = 0; i < kRsBpre; ++i) {
-      const int e = tid + kGvThreads * i;
+      const int e = tid + kRsThreads * i;
       if (e < nbe) *rs_aux(smem, a_b + e) = bpre[i];
     }
     if (w == 0) {
@@ -869,10 +876,10 @@ __global__ __launch_bounds__(kGvThreads, 4) void k_gemv_rows(GemvParams p) {
   }
   __syncthreads();
 
-  // ---- outputs: 16 threads per row (32 rows at a time); the adapter term
+  // ---- outputs: 16 threads per row (64 rows at a time); the adapter term
   // over j = seg, seg + 16, ... then summed across the 16, added to the
   // row's wave partials in wave order
-  for (int r0 = 0; r0 < rows; r0 += kGvThreads / 16) {
+  for (int r0 = 0; r0 < rows; r0 += kRsThreads / 16) {
     const int rl = r0 + tid / 16, seg = tid & 15;
     float ad = 0.0f;
     if (rl < rows)
@@ -898,17 +905,19 @@ struct GemvPlan {
   int nw, P, RW;
 };
 
-// Row-stream plan (M = 1): 8 passes of P rows per workgroup, fewer when the
-// B rows or the LDS aux space would not hold them.
+// Row-stream plan (M = 1): one workgroup per CU, each with the same number
+// of passes (at most 8) of P rows; fewer rows per workgroup when the B rows or
+// the LDS aux space would not hold them.
 bool rows_plan(int64_t M, int64_t N, int64_t K, int r, GemvPlan &pl) {
   const int64_t C = K / 32;
   if (M != 1 || C > kRsMaxChunks || r > 256) return false;
   const int nw = static_cast<int>(ceil_div(C, 64));
-  const int P = std::max(1, kGvWaves / nw);
+  const int P = std::max(1, kRsWaves / nw);
   auto fits = [&](int64_t rw) {
-    return rw * r <= kRsBpre * kGvThreads && nw * rw + rw * r + r + kGvWaves + P <= kRsAux;
+    return rw * r <= kRsBpre * kRsThreads && nw * rw + rw * r + r + kRsWaves + P <= kRsAux;
   };
-  int64_t RW = static_cast<int64_t>(P) * kRsPasses;
+  const int64_t npass = std::min<int64_t>(kRsPasses, ceil_div(ceil_div(N, static_cast<int64_t>(P)), static_cast<int64_t>(kRsCus)));
+  int64_t RW = P * npass;
   while (RW > P && !fits(RW)) RW -= P;
   // every workgroup's H slot in the synchronization words
   if (!fits(RW) || (kRsHword0 + ceil_div(N, RW) * r) * 4 > static_cast<int64_t>(kLinearSyncBytes)) return false;
@@ -992,7 +1001,7 @@ void launch_mt(int nq, bool dq, unsigned grid, size_t lds, hipStream_t s, const 
 
 template <bool kDq>
 void launch_rows(unsigned grid, hipStream_t s, const GemvParams &p) {
-  hipLaunchKernelGGL((k_gemv_rows<kDq>), dim3(grid), dim3(kGvThreads), 0, s, p);
+  hipLaunchKernelGGL((k_gemv_rows<kDq>), dim3(grid), dim3(kRsThreads), 0, s, p);
 }
 
 size_t part_bytes(const GemvPlan &pl, int64_t M) {
