@@ -189,9 +189,11 @@ def write_traffic(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_
     kernels = _traffic_kernels()
     # one entry per launch shape of the decode GEMV (grid work-items)
     for (n, g) in sorted(set(fetch) | set(write)):
-        if "k_gemv<" in n:
-            tmpl = n[n.index("k_gemv<"):n.index(">", n.index("k_gemv<")) + 1]
-            kernels[f"gemv {tmpl} grid {g}"] = (tmpl, g) + _gemv_alg_bytes()
+        for frag in ("k_gemv_rows<", "k_gemv<"):
+            if frag in n:
+                tmpl = n[n.index(frag):n.index(">", n.index(frag)) + 1]
+                kernels[f"gemv {tmpl} grid {g}"] = (tmpl, g) + _gemv_alg_bytes()
+                break
     for key, (kname, grid, alg_r, alg_w) in kernels.items():
         fv, wv = pick(fetch, kname, grid), pick(write, kname, grid)
         if not fv or not wv:
