@@ -143,13 +143,14 @@ def test_up65b_shape_sampled(qb, cb):
         assert np.array_equal(codes[r], nf4.pack_codes(c)), f"row {r}"
 
 
-@pytest.mark.parametrize("rows,cols", [(4096, 5120), (11008, 4096), (8192, 8192)])
+@pytest.mark.parametrize("rows,cols", [(4096, 5120), (11008, 4096), (8192, 8192), (4160, 4160)])
 def test_dq_mean_single_chunk_tree(qb, cb, rows, cols):
-    """Tensors of 1025 to 8192 DQ blocks (nd = 1280, 2752, 4096), whose mean
-    is completed in one chunk of the fp64 tree with register runs of 8 and
-    16 partials: codes, DQ codes, DQ scales, the mean and both dequantized
-    outputs compared in full. 11008 x 4096 is the 7B MLP weight, 8192 x 8192
-    the 65B attention projection of the whole-model stack."""
+    """Tensors of 1025 to 8192 DQ blocks (nd = 1280, 2752, 4096, and 1057
+    with a last DQ block of 64 constants), whose mean is completed in one
+    chunk of the fp64 tree with register runs of 8 and 16 partials: codes,
+    DQ codes, DQ scales, the mean and both dequantized outputs compared in
+    full. 11008 x 4096 is the 7B MLP weight, 8192 x 8192 the 65B attention
+    projection of the whole-model stack."""
     rng = np.random.default_rng(rows + cols)
     bits = synth.normal_bf16(rng, (rows, cols), 0.02)
     _check_quant(qb, gu.dev_bf16(bits), synth.bf16_to_f32(bits), (rows, cols), cb, f"{rows}x{cols}")
