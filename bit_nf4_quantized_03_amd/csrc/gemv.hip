@@ -17,7 +17,7 @@
 // its C workgroups split the reduction into chunks whose slice of X fits in
 // LDS (C = 1 whenever all of X fits). The 8 waves of a workgroup take T row
 // tiles of 16 x KS = 8 / T reduction slices. Each lane issues the code loads
-// of its whole slice at once (16 bytes per quad-piece: 128 elements of its
+// of its slice in two halves (16 bytes per quad-piece: 128 elements of its
 // row = two 64-blocks; lane group g = lane / 16 holds bytes 16 g .. 16 g + 15,
 // i.e. half g % 2 of block g / 2), then decodes byte by byte through a table
 // of bf16 level pairs in LDS into the B operand of v_mfma_f32_16x16x32_bf16.
@@ -319,10 +319,10 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
 
   // ---- prologue: the X slice and the block constants are requested first:
   // they are small and mostly L2 hits, and issued behind the code stream they
-  // would wait for it (vector-memory counts retire in order). Every code word
-  // of the slice is requested at once, and quad-piece jq waits for its own
-  // code words only, so the decode runs while the rest of the slice streams
-  // in. Quad-pieces past the slice and a second block past the end of the
+  // would wait for it (vector-memory counts retire in order). The code words
+  // of the slice are requested in two halves, and quad-piece jq waits for its
+  // own code words only, so the decode runs while the rest of the slice
+  // streams in. Quad-pieces past the slice and a second block past the end of the
   // chunk read a clamped, valid block and are scaled by 0.
   XStage<kXPieces> xst;
   xst.load(p.X, p.K, M, blk0 * kBlock, nblk * kBlock, nqp * 128);
@@ -336,11 +336,16 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
   // more registers and the requests go out after it (measured faster there).
   auto blk_of = [&](int jq) { return min(2 * (q0 + min(jq, max(nq - 1, 0))) + half, nblk - 1); };
   uint4 cw[NQ];
-  auto request_codes = [&]() {
+  // quad-pieces [j0, j1) of the slice; the first half goes out in the
+  // prologue, the second half once the first quad-piece is decoded (all at
+  // once streamed about 5 % slower at M = 4: fewer requests in flight per CU)
+  auto request_range = [&](int j0, int j1) {
 #pragma unroll
     for (int jq = 0; jq < NQ; ++jq)
-      cw[jq] = *reinterpret_cast<const uint4 *>(p.codes + (rowblk + blk0 + blk_of(jq)) * (kBlock / 2) + 16 * (g & 1));
+      if (jq >= j0 && jq < j1)
+        cw[jq] = *reinterpret_cast<const uint4 *>(p.codes + (rowblk + blk0 + blk_of(jq)) * (kBlock / 2) + 16 * (g & 1));
   };
+  auto request_codes = [&]() { request_range(0, NQ / 2); };
 
   // ---- the level-pair table, the X slice and the block constants into
   // LDS. Entry (byte e, copy c) at e * 16 + c holds (level[e >> 4],
@@ -383,6 +388,7 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma clang loop unroll(full)
   for (int jq = 0; jq < NQ; ++jq) {
+    if (jq == 0) request_range(NQ / 2, NQ);
     if (jq >= nq) continue;   // uniform
     const int bi = 2 * (q0 + jq) + half;
     // every LDS read of the quad-piece is issued before its first MFMA, so
