@@ -21,7 +21,7 @@
 //                   which completes the same fp64 tree over the per-DQ-block
 //                   partials (the mean), then the block's scale and int8 codes.
 //   k_tree_mean     larger tensors: one workgroup completes the tree (the mean),
-//   k_dq_codes      then one workgroup per DQ block: scale and int8 codes.
+//   k_dq_codes      then one wave per DQ block: scale and int8 codes.
 //   k_dequant       one workgroup per DQ block: per-block scales in LDS, then
 //                   4-byte code loads expanded to fp32 or bf16 stores.
 #include <algorithm>
@@ -449,15 +449,55 @@ __global__ __launch_bounds__(kThreads) void k_tree_mean(const double *__restrict
   if (threadIdx.x == 0) dq_mean[0] = mu;
 }
 
-// ... and one workgroup per DQ block reads it.
+// ... and one wave per DQ block reads it: 4 constants per lane, the block's
+// max |a - mean| by lane exchanges (max is exact in any order), no barrier;
+// the same arithmetic per constant as dq_block.
 __global__ __launch_bounds__(kThreads) void k_dq_codes(const float *__restrict__ absmax_ws, int64_t nb,
-                                                       const float *__restrict__ dq_mean,
+                                                       int64_t nd, const float *__restrict__ dq_mean,
                                                        int8_t *__restrict__ absmax_q,
                                                        float *__restrict__ dq_scale) {
-  __shared__ float wmax[kThreads / 64];
-  const int64_t b = static_cast<int64_t>(blockIdx.x) * kDqBlock + threadIdx.x;
-  const float a = b < nb ? absmax_ws[b] : 0.0f;
-  dq_block(a, nb, blockIdx.x, dq_mean[0], absmax_q, dq_scale, wmax);
+  const int lane = threadIdx.x & 63;
+  const int64_t d = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  if (d >= nd) return;   // wave-uniform
+  const float mu = dq_mean[0];
+  const int64_t b0 = d * kDqBlock + 4 * lane;
+  float a[4];
+  if (b0 + 4 <= nb) {
+    const float4 v = *reinterpret_cast<const float4 *>(absmax_ws + b0);
+    a[0] = v.x;
+    a[1] = v.y;
+    a[2] = v.z;
+    a[3] = v.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = b0 + j < nb ? absmax_ws[b0 + j] : 0.0f;
+  }
+  float dv[4], m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    dv[j] = b0 + j < nb ? __fsub_rn(a[j], mu) : 0.0f;
+    m = fmaxf(m, fabsf(dv[j]));
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const float s2 = m;
+  uint32_t packed = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int q = 0;
+    if (s2 > 0.0f) {
+      q = static_cast<int>(rintf(__fmul_rn(__fdiv_rn(dv[j], s2), 127.0f)));
+      q = min(max(q, -127), 127);
+    }
+    packed |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * j);
+  }
+  if (b0 + 4 <= nb) {
+    *reinterpret_cast<uint32_t *>(absmax_q + b0) = packed;
+  } else {
+    for (int j = 0; j < 4; ++j)
+      if (b0 + j < nb) absmax_q[b0 + j] = static_cast<int8_t>(packed >> (8 * j));
+  }
+  if (lane == 0) dq_scale[d] = s2;
 }
 
 // ------------------------------------------------------------ dequantize
@@ -614,7 +654,8 @@ hipError_t launch_quantize(const void *W, bool w_bf16, int64_t n, int format, ui
                        dq_scale);
   } else {
     hipLaunchKernelGGL(k_tree_mean, dim3(1), dim3(kThreads), 0, s, part, nd, nb, dq_mean);
-    hipLaunchKernelGGL(k_dq_codes, dim3(nd), dim3(kThreads), 0, s, absmax_out, nb, dq_mean, absmax_q, dq_scale);
+    hipLaunchKernelGGL(k_dq_codes, dim3(ceil_div(nd, kThreads / 64)), dim3(kThreads), 0, s, absmax_out, nb, nd, dq_mean,
+                       absmax_q, dq_scale);
   }
   return hipGetLastError();
 }
