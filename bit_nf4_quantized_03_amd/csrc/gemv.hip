@@ -88,6 +88,7 @@ constexpr int kSpinLimit = 1 << 16;              // polls of about 1 us: a wait 
 constexpr int kStripTarget = 512;                // weight workgroups: two per CU
 constexpr int kGvLdsMax = kXOffset + kXLdsMax + kZeroBytes + 1024;   // dynamic LDS bound of every plan
 
+
 struct GemvParams {
   const __bf16 *X;         // [M][K]
   const uint8_t *codes;    // [N][K/2]
@@ -557,23 +558,32 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
 }
 
 // ------------------------------------------------------- row-stream path
-// One row of X (M = 1) and K <= 16384: no matrix cores, two workgroups per
-// CU. Workgroup b owns 8 P consecutive weight rows, whole: 8 passes of P
-// rows. A row is split into K / 32 chunks of 16 code bytes (32 elements,
-// half a 64-block); thread (row slot rs, chunk slot j) reads chunk j of row
-// rs of every pass, so the 64 lanes of a wave read 1 KB of one row per load
-// instruction and each thread's 32 elements of X stay in registers for the
-// whole call. Every load of the workgroup (X slice, A row, B rows, then the
-// 8 passes' code chunks, int8 constants and DQ scales) is issued at the
-// start, in the order it is needed; the passes are then consumed in order,
-// with no branch between them. A code byte becomes its bf16 level pair
-// through a table in LDS (address: one byte permute of the code word with
-// the lane's copy offset), v_dot2_f32_bf16 multiplies the pair with the X
-// pair in the register, and the chunk's sum is scaled by its block constant
-// c_b. The 8 passes' sums are reduce-scattered across the wave (three
-// halving exchanges, then three full ones); one lane per row writes the
-// wave's partial to LDS, and the waves of a row are added in wave order at
-// the end.
+// One row of X (M = 1) and K <= 16384: no matrix cores, one 1024-thread
+// workgroup per CU. Workgroup b owns up to 8 P consecutive weight rows,
+// whole: passes of P rows. A row is split into K / 32 chunks of 16 code bytes
+// (32 elements, half a 64-block); thread (row slot rs, chunk slot j) reads
+// chunk j of row rs of every pass, so the 64 lanes of a wave read 1 KB of one
+// row per load instruction and each thread's 32 elements of X stay in
+// registers for the whole call.
+//
+// Requests are few and early. At the start of a call every wave of the chip
+// issues its loads at once, and each vector-memory instruction costs the
+// address unit time (64 addresses), out-of-range ones too, so the kernel
+// spends as few instructions as the data allow, and waves that have nothing
+// to fetch skip a request by a wave-uniform branch: X is fetched once per
+// workgroup (16 bytes a thread) and staged in LDS; the int8 constants of the
+// workgroup's blocks arrive as one word per thread with their DQ scales and
+// the mean, and become c_b in LDS; B rows come 16 bytes a thread (when
+// r % 4 == 0); A rows only in the waves that form an adapter column. These
+// small requests go out first, then the first D passes' code chunks, one
+// instruction per pass (the int8 constant and DQ scale of every pass, read
+// per lane, had cost two more). A code byte becomes its bf16 level pair
+// through a table in LDS (address: one byte permute of the code word with the
+// lane's copy offset), v_dot2_f32_bf16 multiplies the pair with the X pair in
+// the register, and the chunk's sum is scaled by its block constant c_b from
+// LDS. The passes' sums are reduce-scattered across the wave (three halving
+// exchanges, then three full ones); one lane per row writes the wave's
+// partial to LDS, and the waves of a row are added in wave order at the end.
 //
 // Adapter: column j of H = X A^T is formed in fp32 by the row slot that owns
 // it (workgroup b, slot rs: columns b + Gw (rs + P t)), round t = 0 from the
@@ -594,6 +604,9 @@ constexpr int kRsPasses = 8;                   // passes per workgroup at most (
 constexpr int kRsBpre = 4;                     // B values per thread loaded at the start: RW r <= 4 * 1024
 constexpr int kRsMaxChunks = 64 * 8;           // K <= 16384: at most 8 waves per row
 constexpr int kRsCus = 256;                    // compute units of the GPU
+constexpr int kRsXBytes = 16384 * 2;           // X row in LDS (K <= 16384)
+constexpr int kRsMaxBlocks = 4096;             // blocks of a workgroup's rows (c_b in LDS)
+constexpr int kRsLdsTotal = kRsLds + kRsXBytes + kRsMaxBlocks * 4;   // 112 KB of dynamic LDS
 constexpr int kRsHword0 = 256;                 // sync word of the H slots: [Gw][r] fp32 bits, 0 = not yet published
 
 __device__ __forceinline__ float *rs_aux(char *smem, int i) {
@@ -637,9 +650,9 @@ __device__ __forceinline__ float div127(float s) {
 
 template <bool kDq>
 __global__ __launch_bounds__(kRsThreads) void k_gemv_rows(GemvParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[kRsLds];
+  extern __shared__ __attribute__((aligned(16))) char smem[];   // kRsLdsTotal bytes
   constexpr int NP = kRsPasses;   // passes per workgroup at most
-  constexpr int D = 2;            // passes in flight (more were slower: 4 by 8 %, 6 by 15 %)
+  constexpr int D = 2;            // passes in flight
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nw = p.rs_nw, P = p.rs_P, RW = p.rs_RW, Gw = p.S;
   const int C = static_cast<int>(p.K / 32);
@@ -656,71 +669,104 @@ __global__ __launch_bounds__(kRsThreads) void k_gemv_rows(GemvParams p) {
   const int a_b = nw * RW, a_h = a_b + RW * p.r, a_hp = a_h + p.r;
   const int jcol = b + Gw * rs;   // this slot's first adapter column
   const bool producer = p.r > 0 && wave_on && jcol < p.r;
+  char *const xs = smem + kRsLds;                                           // X, bf16 [K]
+  float *const cs = reinterpret_cast<float *>(smem + kRsLds + kRsXBytes);   // c_b of the rows' blocks
+  const int nblk = static_cast<int>(rows * kb);                             // <= kRsMaxBlocks
+  const int64_t gblk0 = n0 * kb;
 
-  // ---- small requests first: DQ mean, X slice (zero for idle lanes), A row
-  // of the slot's first column, B rows. All are vector loads: a scalar load
-  // would hold up the first barrier (which waits for every scalar and LDS
-  // access) until it came back from behind the grid's code stream.
-  const float mu = kDq ? __uint_as_float(buf_b32(buf(p.dq_mean, 4), 0)) : 0.0f;
-  uint32_t xr[16];
+  // ---- small requests first, in as few vector-memory instructions as the
+  // data allow: each instruction costs the wave's address unit time (64
+  // addresses), out-of-range ones too, and at the start of the call every
+  // wave of the chip issues them at once. Waves that have nothing to fetch
+  // skip a request by a wave-uniform branch.
+  //   X: 16 bytes per thread, staged in LDS (K / 512 instructions per
+  //      workgroup instead of four per wave);
+  //   block constants: four blocks per thread (int8 codes as one word, their
+  //      DQ scales, the mean), made into c_b in LDS;
+  //   B rows: four floats per thread (one 16-byte load when r % 4 == 0);
+  //   A row: the producer waves only.
+  const int xch = static_cast<int>(p.K / 8);   // 16-byte pieces of X (<= 2 per thread)
+  uint4 xv[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
   {
     const __amdgpu_buffer_rsrc_t bx = buf(p.X, p.K * 2);
-    const uint32_t off = jon ? static_cast<uint32_t>(64 * j) : kOob;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = buf_b128(bx, off + 16u * q);
-      xr[4 * q] = v.x;
-      xr[4 * q + 1] = v.y;
-      xr[4 * q + 2] = v.z;
-      xr[4 * q + 3] = v.w;
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + kRsThreads * i;
+      if (w * 64 + kRsThreads * i < xch) xv[i] = buf_b128(bx, c < xch ? 16u * c : kOob);
+    }
+  }
+  uint32_t qw = 0;   // int8 codes of blocks 4 tid .. + 3 (DQ), or unused
+  int qt[3] = {0, 0, 0};   // the bytes of a last, partial word (one lane)
+  float cv[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // DQ: scales of the first and last of them, mean; else c_b
+  if (w * 256 < nblk) {   // wave-uniform
+    if constexpr (kDq) {
+      const int full = nblk >> 2;
+      qw = buf_b32(buf(p.absmax_q + gblk0, nblk), tid < full ? 4u * tid : kOob);
+      if (tid == full && (nblk & 3)) {   // the last, partial word: one lane of one wave
+#pragma unroll
+        for (int i = 0; i < 3; ++i) qt[i] = buf_i8(buf(p.absmax_q + gblk0, nblk), i < (nblk & 3) ? 4u * tid + i : kOob);
+      }
+      const __amdgpu_buffer_rsrc_t bs = buf(p.dq_scale, (p.N * kb + kDqBlock - 1) / kDqBlock * 4);
+      const bool own = 4 * tid < nblk;
+      const int64_t g0 = gblk0 + 4 * tid, g1 = gblk0 + min(4 * tid + 3, nblk - 1);
+      cv[0] = __uint_as_float(buf_b32(bs, own ? static_cast<uint32_t>(g0 / kDqBlock) * 4u : kOob));
+      cv[1] = __uint_as_float(buf_b32(bs, own ? static_cast<uint32_t>(g1 / kDqBlock) * 4u : kOob));
+      cv[2] = __uint_as_float(buf_b32(buf(p.dq_mean, 4), 0));
+    } else {
+      const __amdgpu_buffer_rsrc_t ba32 = buf(p.absmax + gblk0, static_cast<int64_t>(nblk) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = 4 * tid + i;
+        cv[i] = __uint_as_float(buf_b32(ba32, g < nblk ? 4u * g : kOob));
+      }
+    }
+  }
+  const int nbe = rows * p.r;
+  const bool b4 = (p.r & 3) == 0;   // B rows as 16-byte loads: element 4 tid + i, else tid + 1024 i
+  float bpre[kRsBpre] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (p.r > 0) {
+    const __amdgpu_buffer_rsrc_t bbr = buf(p.B + n0 * p.r, static_cast<int64_t>(nbe) * 4);
+    if (b4) {
+      if (w * 256 < nbe) {   // wave-uniform
+        const uint4 v = buf_b128(bbr, 4 * tid < nbe ? 16u * tid : kOob);
+        bpre[0] = __uint_as_float(v.x);
+        bpre[1] = __uint_as_float(v.y);
+        bpre[2] = __uint_as_float(v.z);
+        bpre[3] = __uint_as_float(v.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kRsBpre; ++i) {
+        const int e = tid + kRsThreads * i;
+        bpre[i] = __uint_as_float(buf_b32(bbr, e < nbe ? static_cast<uint32_t>(e) * 4u : kOob));
+      }
     }
   }
   const __amdgpu_buffer_rsrc_t ba = buf(p.A, p.r > 0 ? static_cast<int64_t>(p.r) * p.K * 4 : 0);
   float4 arow[8];
-  {
-    const uint32_t off = producer && jon ? static_cast<uint32_t>((static_cast<int64_t>(jcol) * p.K + 32 * j) * 4) : kOob;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) arow[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (producer) {   // wave-uniform
+    const uint32_t off = jon ? static_cast<uint32_t>((static_cast<int64_t>(jcol) * p.K + 32 * j) * 4) : kOob;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint4 v = buf_b128(ba, off + 16u * i);
       arow[i] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
     }
   }
-  const int nbe = rows * p.r;
-  float bpre[kRsBpre];
-  {
-    const __amdgpu_buffer_rsrc_t bbr = buf(p.r > 0 ? p.B + n0 * p.r : p.B, static_cast<int64_t>(nbe) * 4);
-#pragma unroll
-    for (int i = 0; i < kRsBpre; ++i) {
-      const int e = tid + kRsThreads * i;
-      bpre[i] = __uint_as_float(buf_b32(bbr, e < nbe ? static_cast<uint32_t>(e) * 4u : kOob));
-    }
-  }
 
-  // ---- the passes' loads, D ahead (the first D before the table is built,
-  // so the code stream starts at once): code chunk, int8 constant, DQ scale
+  // ---- the passes' code chunks, D ahead (the first D before the tables are
+  // built, so the code stream starts at once); one instruction per pass
   uint4 cw[D];
-  int qv[D];
-  float fv[D];
-  const int64_t gblk0 = n0 * kb;
   const __amdgpu_buffer_rsrc_t bc = buf(p.codes + n0 * (p.K / 2), static_cast<int64_t>(rows) * (p.K / 2));
-  const __amdgpu_buffer_rsrc_t bq = kDq ? buf(p.absmax_q + gblk0, static_cast<int64_t>(rows) * kb)
-                                        : buf(p.absmax + gblk0, static_cast<int64_t>(rows) * kb * 4);
-  const __amdgpu_buffer_rsrc_t bs = buf(p.dq_scale, kDq ? (p.N * kb + kDqBlock - 1) / kDqBlock * 4 : 0);
   auto issue = [&](int i) {
     const int rl = i * P + rs, slot = i % D;
     const bool ok = jon && i < npass && rl < rows;
     const uint32_t lb = static_cast<uint32_t>(rl * kb + (j >> 1));   // block within the workgroup's rows
     cw[slot] = buf_b128(bc, ok ? lb * 32u + 16u * (j & 1) : kOob);
-    if constexpr (kDq) {
-      qv[slot] = buf_i8(bq, ok ? lb : kOob);
-      fv[slot] = __uint_as_float(buf_b32(bs, ok ? static_cast<uint32_t>((gblk0 + lb) / kDqBlock) * 4u : kOob));
-    } else {
-      fv[slot] = __uint_as_float(buf_b32(bq, ok ? lb * 4u : kOob));
-    }
   };
 #pragma unroll
   for (int i = 0; i < D; ++i) issue(i);
-
 
   // ---- table: entry e (code byte) = (bf16 level[e >> 4], bf16 level[e & 15]),
   // copy c at byte e * 256 + 4 c. Thread tid writes copies 4 (tid % 8) .. + 3
@@ -741,7 +787,43 @@ __global__ __launch_bounds__(kRsThreads) void k_gemv_rows(GemvParams p) {
       *reinterpret_cast<uint4 *>(smem + (e0 + 128 * i) * kRsEntry + 16 * (tid & 7)) = make_uint4(v, v, v, v);
     }
   }
-  __syncthreads();   // table ready (waits for LDS and scalar accesses only)
+  // ---- X and the block constants c_b into LDS
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + kRsThreads * i;
+    if (c < xch) *reinterpret_cast<uint4 *>(xs + 16 * c) = xv[i];
+  }
+  if (4 * tid < nblk) {
+    float c4[4];
+    if constexpr (kDq) {
+      const int64_t dlo = (gblk0 + 4 * tid) / kDqBlock;
+      const float klo = div127(cv[0]), khi = div127(cv[1]);
+      qw |= (static_cast<uint32_t>(qt[0]) & 0xFFu) | ((static_cast<uint32_t>(qt[1]) & 0xFFu) << 8) |
+            ((static_cast<uint32_t>(qt[2]) & 0xFFu) << 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float q = static_cast<float>(static_cast<int8_t>((qw >> (8 * i)) & 0xFFu));
+        const float k = (gblk0 + 4 * tid + i) / kDqBlock == dlo ? klo : khi;
+        c4[i] = __fadd_rn(__fmul_rn(q, k), cv[2]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c4[i] = cv[i];
+    }
+    *reinterpret_cast<float4 *>(cs + 4 * tid) = make_float4(c4[0], c4[1], c4[2], c4[3]);
+  }
+  __syncthreads();   // table, X and c_b ready (waits for LDS and scalar accesses only)
+
+  // this thread's 32 elements of X (zero for idle lanes)
+  uint32_t xr[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = jon ? *reinterpret_cast<const uint4 *>(xs + 64 * j + 16 * q) : make_uint4(0, 0, 0, 0);
+    xr[4 * q] = v.x;
+    xr[4 * q + 1] = v.y;
+    xr[4 * q + 2] = v.z;
+    xr[4 * q + 3] = v.w;
+  }
 
   // ---- the slot's adapter column over this wave's chunks, parked in LDS
   auto h_partial = [&]() {
@@ -791,7 +873,8 @@ __global__ __launch_bounds__(kRsThreads) void k_gemv_rows(GemvParams p) {
     if (wave_on && i < npass) {   // uniform; no load inside
       const int slot = i % D;
       const uint4 c = cw[slot];
-      const float cb = kDq ? __fadd_rn(__fmul_rn(static_cast<float>(qv[slot]), div127(fv[slot])), mu) : fv[slot];
+      const int rl = i * P + rs;
+      const float cb = cs[jon && rl < rows ? rl * kb + (j >> 1) : 0];
       float sq[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -856,7 +939,7 @@ __global__ __launch_bounds__(kRsThreads) void k_gemv_rows(GemvParams p) {
     // ---- B rows into LDS; wait until every H word is flagged, s H into LDS
 #pragma unroll
     for (int i = 0; i < kRsBpre; ++i) {
-      const int e = tid + kRsThreads * i;
+      const int e = b4 ? 4 * tid + i : tid + kRsThreads * i;
       if (e < nbe) *rs_aux(smem, a_b + e) = bpre[i];
     }
     if (w == 0) {
@@ -926,7 +1009,9 @@ bool rows_plan(int64_t M, int64_t N, int64_t K, int r, GemvPlan &pl) {
   int64_t RW = P * npass;
   while (RW > P && !fits(RW)) RW -= P;
   // every workgroup's H slot in the synchronization words
-  if (!fits(RW) || (kRsHword0 + ceil_div(N, RW) * r) * 4 > static_cast<int64_t>(kLinearSyncBytes)) return false;
+  if (!fits(RW) || RW * (K / kBlock) > kRsMaxBlocks ||
+      (kRsHword0 + ceil_div(N, RW) * r) * 4 > static_cast<int64_t>(kLinearSyncBytes))
+    return false;
   pl.rows = true;
   pl.nw = nw;
   pl.P = P;
@@ -1007,7 +1092,10 @@ void launch_mt(int nq, bool dq, unsigned grid, size_t lds, hipStream_t s, const 
 
 template <bool kDq>
 void launch_rows(unsigned grid, hipStream_t s, const GemvParams &p) {
-  hipLaunchKernelGGL((k_gemv_rows<kDq>), dim3(grid), dim3(kRsThreads), 0, s, p);
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_rows<kDq>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kRsLdsTotal);
+  (void)attr;
+  hipLaunchKernelGGL((k_gemv_rows<kDq>), dim3(grid), dim3(kRsThreads), kRsLdsTotal, s, p);
 }
 
 size_t part_bytes(const GemvPlan &pl, int64_t M) {
@@ -1089,3 +1177,4 @@ hipError_t launch_gemv(const LinearArgs &a, const void *X, const float *A, const
 }
 
 }  // namespace qnf4
+

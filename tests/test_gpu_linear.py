@@ -128,6 +128,20 @@ def test_decode_split_k_ragged(qb, cb, M, r):
     _fwd(qb, c, f"decode-ragged M={M} r={r}")
 
 
+@pytest.mark.parametrize("K", [4160, 11072])
+@pytest.mark.parametrize("r", [1, 3, 9])
+def test_decode_one_row_odd_rank(qb, cb, K, r):
+    """One row of X with a rank that is not a multiple of 4 (the row-stream
+    kernel then reads the B rows with single-word loads), and workgroups whose
+    rows hold a block count that is not a multiple of 4, so the last word of
+    their int8 constants is partial: N = 64 with K = 4160 (65 blocks a row, 5
+    rows a workgroup) and K = 11072 (173 blocks a row, 2 rows a workgroup)."""
+    wl = synth.make_linear_workload("decode-odd-rank", M=1, N=64, K=K, r=r, alpha=16.0,
+                                    seed=7200 + K + r, w_dtype="bf16")
+    c = Case(qb, wl, cb)
+    _fwd(qb, c, f"decode-odd-rank K={K} r={r}")
+
+
 @pytest.mark.parametrize("M", [1, 3])
 def test_decode_long_rows(qb, cb, M):
     """K = 16448 (514 chunks of 32 elements per row, past what the row-stream
