@@ -242,14 +242,17 @@ int qlora_linear_fwd_noalloc(const void *X, int64_t M, const qlora_nf4_weight *W
   if (st != QLORA_OK) return st;
   if (!aligned16(X) || !aligned16(Y))
     return fail(QLORA_ERR_ALIGN, "%s: X and Y must be 16-byte aligned", fn);
-  const size_t need = qnf4::linear_fwd_ws_bytes(M, W->rows, W->cols, r);
+  // split partials of the large-tile forward only where they fit the scratch
+  size_t need = qnf4::linear_fwd_ws_bytes(M, W->rows, W->cols, r, true);
+  const bool split = need <= qnf4::kNoAllocScratchBytes;
+  if (!split) need = qnf4::linear_fwd_ws_bytes(M, W->rows, W->cols, r, false);
   if (need > qnf4::kNoAllocScratchBytes)
     return fail(QLORA_ERR_WORKSPACE, "%s: these sizes need %zu bytes of scratch, more than the %zu the library holds",
                 fn, need, qnf4::kNoAllocScratchBytes);
   void *scratch = nullptr;
   hipError_t e = qnf4::noalloc_scratch(&scratch);
   if (e != hipSuccess) return hip_status(e, fn);
-  e = qnf4::linear_fwd(make_args(M, W, r, scale), X, A, B, Y, scratch, static_cast<hipStream_t>(stream));
+  e = qnf4::linear_fwd(make_args(M, W, r, scale), X, A, B, Y, scratch, static_cast<hipStream_t>(stream), split);
   return hip_status(e, fn);
 }
 

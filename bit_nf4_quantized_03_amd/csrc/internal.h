@@ -89,15 +89,19 @@ constexpr size_t kLinearSyncBytes = QLORA_LINEAR_SYNC_BYTES;
 
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int r);
 // Workspace of the forward call alone (the backward's buffers left out).
-size_t linear_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r);
+// allow_split as for linear_fwd below.
+size_t linear_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r, bool allow_split = true);
 
 // The no-allocation forward's scratch: a file-scope device array of
 // kNoAllocScratchBytes, its address on the current device (taken once per
 // device, with that device current).
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 hipError_t noalloc_scratch(void **ptr);
+// allow_split = false keeps the large-tile forward to one pass over the
+// reduction (no split partials in the workspace), for a caller whose scratch
+// is bounded.
 hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const float *B,
-                      void *Y, void *ws, hipStream_t s);
+                      void *Y, void *ws, hipStream_t s, bool allow_split = true);
 hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const float *A,
                       const float *B, void *dX, float *dA, float *dB, void *ws,
                       hipStream_t s);

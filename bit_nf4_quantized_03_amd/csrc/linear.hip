@@ -50,6 +50,8 @@ struct FwdParams {
   void *Y;              // bf16 [M, N]
   int64_t M, N, K;
   int rp;
+  float *part;          // fp32 [S][M][N] split partials (S > 1)
+  int S, per;           // reduction splits, 64-deep steps per split
 };
 
 // Large-M forward: one 256 x 256 tile of Y per workgroup (XCD-aware order),
@@ -63,24 +65,31 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void k_fwd_big(FwdParams p, Nf4Ta
   const BigSmem smem{sa0, sa1, sb0, sb1};
   __shared__ float2 lv_tab[256 * kLvCopies];
   const float2 *lv = load_level_pairs(lv_tab, tab);
+  // workgroup -> (reduction split z, output tile)
+  const int tiles_m = static_cast<int>((p.M + 255) / 256), tiles_n = static_cast<int>((p.N + 255) / 256);
+  const int tiles = tiles_m * tiles_n;
+  const int z = static_cast<int>(blockIdx.x) / tiles;
   int tm, tn;
-  tile_of(blockIdx.x, static_cast<int>((p.M + 255) / 256), static_cast<int>((p.N + 255) / 256), tm, tn);
+  tile_of(static_cast<int>(blockIdx.x) - z * tiles, tiles_m, tiles_n, tm, tn);
   const int64_t n0 = static_cast<int64_t>(tn) * 256;
   const int64_t m0 = static_cast<int64_t>(tm) * 256;
+  const int s0 = z * p.per, s1 = min(static_cast<int>(p.K / kBK), s0 + p.per);
   __syncthreads();
   Acc<Cfg> acc;
   acc.zero();
   {
-    DirectRowsT<T> da(p.X, p.K, p.M, m0);
+    DirectRowsT<T> da(static_cast<const __bf16 *>(p.X) + static_cast<int64_t>(s0) * kBK, p.K, p.M, m0);
     Nf4RowBigT<T> l0(p.codes, p.cs, p.N, p.K, n0), l1 = l0;
-    auto load = [](Nf4RowBigT<T> &l, int s) { l.load(static_cast<int64_t>(s) * kBK); };
-    big_mainloop_nf4<Cfg>(acc, da, l0, l1, load, static_cast<int>(p.K / kBK), smem, lv);
+    auto load = [s0](Nf4RowBigT<T> &l, int s) { l.load(static_cast<int64_t>(s0 + s) * kBK); };
+    big_mainloop_nf4<Cfg>(acc, da, l0, l1, load, s1 - s0, smem, lv);
   }
-  if (p.rp > 0) {
+  if (p.rp > 0 && z == 0) {
     DirectRowsT<T> da(p.Hs, p.rp, p.M, m0), db(p.Bb, p.rp, p.N, n0);
     big_mainloop_dense<Cfg>(acc, da, db, p.rp / kBK, smem);
   }
-  if (m0 + 256 <= p.M && n0 + 256 <= p.N)
+  if (p.S > 1)
+    store_f32<Cfg>(acc, p.part + static_cast<int64_t>(z) * p.M * p.N, p.N, p.M, p.N, m0, n0);
+  else if (m0 + 256 <= p.M && n0 + 256 <= p.N)
     store_bf16<Cfg, false>(acc, static_cast<__bf16 *>(p.Y), p.N, p.M, p.N, m0, n0, 1.0f);
   else
     store_bf16<Cfg, true>(acc, static_cast<__bf16 *>(p.Y), p.N, p.M, p.N, m0, n0, 1.0f);
@@ -99,6 +108,8 @@ struct DxParams {
   void *dX;             // bf16 [M, K]
   int64_t M, N, K;
   int rp;
+  float *part;          // fp32 [S][M][K] split partials (S > 1)
+  int S, per;           // reduction splits, 64-deep steps per split
 };
 
 // Input gradient: one 256 x 256 tile of dX per workgroup (XCD-aware order),
@@ -113,25 +124,32 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void k_dx_big(DxParams p, Nf4Tabl
   const BigSmem smem{sa0, sa1, sb0, sb1};
   __shared__ float2 lv_tab[256 * kLvCopies];
   const float2 *lv = load_level_pairs(lv_tab, tab);
+  // workgroup -> (reduction split z, output tile)
+  const int tiles_m = static_cast<int>((p.M + 255) / 256), tiles_k = static_cast<int>((p.K + 255) / 256);
+  const int tiles = tiles_m * tiles_k;
+  const int z = static_cast<int>(blockIdx.x) / tiles;
   int tm, tn;
-  tile_of(blockIdx.x, static_cast<int>((p.M + 255) / 256), static_cast<int>((p.K + 255) / 256), tm, tn);
+  tile_of(static_cast<int>(blockIdx.x) - z * tiles, tiles_m, tiles_k, tm, tn);
   const int64_t k0 = static_cast<int64_t>(tn) * 256;
   const int64_t m0 = static_cast<int64_t>(tm) * 256;
+  const int s0 = z * p.per, s1 = min(static_cast<int>(p.N / kBK), s0 + p.per);
   __syncthreads();
   Acc<Cfg> acc;
   acc.zero();
   {
-    DirectRowsT<T> da(p.dY, p.N, p.M, m0);
+    DirectRowsT<T> da(static_cast<const __bf16 *>(p.dY) + static_cast<int64_t>(s0) * kBK, p.N, p.M, m0);
     Nf4TransBigT<T> l0(p.codes, p.cs, p.K, k0), l1 = l0;
     const int64_t K = p.K;
-    auto load = [K](Nf4TransBigT<T> &l, int s) { l.load(static_cast<int64_t>(s) * kBK, K); };
-    big_mainloop_nf4<Cfg>(acc, da, l0, l1, load, static_cast<int>(p.N / kBK), smem, lv);
+    auto load = [K, s0](Nf4TransBigT<T> &l, int s) { l.load(static_cast<int64_t>(s0 + s) * kBK, K); };
+    big_mainloop_nf4<Cfg>(acc, da, l0, l1, load, s1 - s0, smem, lv);
   }
-  if (p.rp > 0) {
+  if (p.rp > 0 && z == 0) {
     DirectRowsT<T> da(p.dHb, p.rp, p.M, m0), db(p.Atb, p.rp, p.K, k0);
     big_mainloop_dense<Cfg>(acc, da, db, p.rp / kBK, smem);
   }
-  if (m0 + 256 <= p.M && k0 + 256 <= p.K)
+  if (p.S > 1)
+    store_f32<Cfg>(acc, p.part + static_cast<int64_t>(z) * p.M * p.K, p.K, p.M, p.K, m0, k0);
+  else if (m0 + 256 <= p.M && k0 + 256 <= p.K)
     store_bf16<Cfg, false>(acc, static_cast<__bf16 *>(p.dX), p.K, p.M, p.K, m0, k0, 1.0f);
   else
     store_bf16<Cfg, true>(acc, static_cast<__bf16 *>(p.dX), p.K, p.M, p.K, m0, k0, 1.0f);
@@ -581,6 +599,16 @@ __global__ __launch_bounds__(256) void k_grad_finish(GradFinishParams p) {
   }
 }
 
+// Split reduction of the large-tile GEMMs when few output tiles would leave
+// most of the GPU idle: out = bf16(sum of the S fp32 partials, in split
+// order), four elements per thread.
+__global__ __launch_bounds__(256) void k_split_out(const float *part, int S, int64_t plane, __bf16 *out) {
+  const int64_t e = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (e >= plane) return;
+  const float4 v = split_sum4(part, plane, e, S);
+  *reinterpret_cast<uint2 *>(out + e) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+}
+
 // ------------------------------------------------------------- tile configs
 constexpr int kSmallM = 32;
 constexpr int kTargetGroups = 512;
@@ -616,10 +644,30 @@ struct Carve {
 struct Plan {
   int rp;
   Split down, hb, dh, ga, gb;   // forward H; backward H and dY B; dA; dB
+  Split fs, xs;                 // reduction splits of the forward and dX GEMMs
   bool small;
 };
 
-Plan make_plan(int64_t M, int64_t N, int64_t K, int r) {
+constexpr int kCus = 256;                             // compute units of the GPU
+constexpr int kMinSplitSteps = 4;                     // 64-deep steps per split at least
+constexpr size_t kSplitPartMax = size_t(128) << 20;   // bytes of fp32 partials at most
+
+// Reduction splits of a large-tile GEMM with `tiles` 256 x 256 output tiles
+// of an M x cols output over `steps` 64-deep steps: none while the tiles fill
+// half the GPU or more; otherwise as many as keep every workgroup in one
+// round on the compute units, each split at least kMinSplitSteps long.
+Split gemm_split(int64_t tiles, int steps, int64_t M, int64_t cols, bool allow) {
+  int S = 1;
+  if (allow && tiles * 2 <= kCus) {
+    S = static_cast<int>(std::min<int64_t>(kCus / tiles, steps / kMinSplitSteps));
+    while (S > 1 && static_cast<size_t>(S) * M * cols * sizeof(float) > kSplitPartMax) --S;
+    S = std::max(S, 1);
+  }
+  const int per = static_cast<int>(ceil_div(steps, S));
+  return {static_cast<int>(ceil_div(steps, per)), per};
+}
+
+Plan make_plan(int64_t M, int64_t N, int64_t K, int r, bool allow_split = true) {
   Plan pl;
   pl.rp = static_cast<int>(ceil_div(r, kBK) * kBK);
   pl.small = M <= kSmallM && gemv_sync_fits(M, N, K, r);
@@ -633,10 +681,13 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int r) {
   const int msteps = static_cast<int>(ceil_div(M, kBK));
   pl.ga = choose_split(grid_blocks(pl.rp, 64) * grid_blocks(K, 256), msteps, 8);
   pl.gb = choose_split(grid_blocks(N, 256) * grid_blocks(pl.rp, 64), msteps, 8);
+  pl.fs = gemm_split(grid_blocks(M, 256) * grid_blocks(N, 256), ksteps, M, N, allow_split);
+  pl.xs = gemm_split(grid_blocks(M, 256) * grid_blocks(K, 256), nsteps, M, K, allow_split);
   return pl;
 }
 
 struct Buffers {
+  float *part;   // split partials of the large-tile GEMMs
   float *cs;
   float *down_part;
   __bf16 *Hs;
@@ -655,6 +706,9 @@ Buffers carve(void *ws, const Plan &pl, int64_t M, int64_t N, int64_t K, size_t 
   const int64_t nb = ceil_div(N * K, kBlock);
   const int rp = pl.rp;
   b.cs = c.take<float>(nb);
+  const size_t part = std::max(pl.fs.splits > 1 ? static_cast<size_t>(pl.fs.splits) * M * N : 0,
+                               pl.xs.splits > 1 ? static_cast<size_t>(pl.xs.splits) * M * K : 0);
+  b.part = part ? c.take<float>(part) : nullptr;
   if (rp > 0) {
     b.down_part = c.take<float>(static_cast<size_t>(std::max(pl.down.splits, pl.hb.splits)) * M * rp);
     b.Hs = c.take<__bf16>(static_cast<size_t>(M) * rp);
@@ -749,8 +803,8 @@ size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
   return pl.small ? std::max(bytes, gemv_ws_bytes(M, N, K, r)) : bytes;
 }
 
-size_t linear_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
-  const Plan pl = make_plan(M, N, K, r);
+size_t linear_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r, bool allow_split) {
+  const Plan pl = make_plan(M, N, K, r, allow_split);
   if (pl.small) return gemv_ws_bytes(M, N, K, r);
   size_t bytes = 0;
   carve(nullptr, pl, M, N, K, &bytes);
@@ -758,17 +812,23 @@ size_t linear_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
 }
 
 hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const float *B, void *Y,
-                      void *ws, hipStream_t s) {
-  const Plan pl = make_plan(a.M, a.N, a.K, a.r);
+                      void *ws, hipStream_t s, bool allow_split) {
+  const Plan pl = make_plan(a.M, a.N, a.K, a.r, allow_split);
   if (pl.small) return launch_gemv(a, X, A, B, Y, ws, s);
   const Buffers b = carve(ws, pl, a.M, a.N, a.K, nullptr);
   hipError_t err = run_adapter_pre(a, pl, b, X, nullptr, A, B, false, s);
   if (err != hipSuccess) return err;
-  FwdParams fp{X, a.codes, block_scales(a, b), b.Hs, b.Bb, Y, a.M, a.N, a.K, pl.rp};
-  dim3 g(grid_blocks(a.N, 256) * grid_blocks(a.M, 256), 1, 1);
+  FwdParams fp{X, a.codes, block_scales(a, b), b.Hs, b.Bb, Y, a.M, a.N, a.K, pl.rp, b.part, pl.fs.splits,
+               pl.fs.steps_per_split};
+  dim3 g(grid_blocks(a.N, 256) * grid_blocks(a.M, 256) * pl.fs.splits, 1, 1);
   prof_begin(kProfFwdGemm, s);
   hipLaunchKernelGGL(k_fwd_big<CfgBig8>, g, dim3(CfgBig8::kThreads), 0, s, fp, format_tables(a.format));
   prof_end(kProfFwdGemm, s);
+  if (pl.fs.splits > 1) {
+    const int64_t plane = a.M * a.N;
+    hipLaunchKernelGGL(k_split_out, dim3(grid_blocks(plane / 4, 256)), dim3(256), 0, s, b.part, pl.fs.splits,
+                       plane, static_cast<__bf16 *>(Y));
+  }
   return hipGetLastError();
 }
 
@@ -780,11 +840,17 @@ hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const 
   hipError_t err = run_adapter_pre(a, pl, b, X, dY, A, B, true, s);
   if (err != hipSuccess) return err;
   {
-    DxParams dp{dY, a.codes, block_scales(a, b), b.dHb, b.Atb, dX, a.M, a.N, a.K, pl.rp};
-    dim3 g(grid_blocks(a.K, 256) * grid_blocks(a.M, 256), 1, 1);
+    DxParams dp{dY, a.codes, block_scales(a, b), b.dHb, b.Atb, dX, a.M, a.N, a.K, pl.rp, b.part, pl.xs.splits,
+                pl.xs.steps_per_split};
+    dim3 g(grid_blocks(a.K, 256) * grid_blocks(a.M, 256) * pl.xs.splits, 1, 1);
     prof_begin(kProfBwdDx, s);
     hipLaunchKernelGGL(k_dx_big<CfgDx>, g, dim3(CfgDx::kThreads), 0, s, dp, tab);
     prof_end(kProfBwdDx, s);
+    if (pl.xs.splits > 1) {
+      const int64_t plane = a.M * a.K;
+      hipLaunchKernelGGL(k_split_out, dim3(grid_blocks(plane / 4, 256)), dim3(256), 0, s, b.part, pl.xs.splits,
+                         plane, static_cast<__bf16 *>(dX));
+    }
   }
   if (pl.rp > 0) {
     GradParams gp{};

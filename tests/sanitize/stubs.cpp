@@ -35,13 +35,13 @@ hipError_t launch_dequantize(const uint8_t *, int, const int8_t *, const float *
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
   return static_cast<size_t>(M + N + K + r) * 16 + kLinearSyncBytes;
 }
-size_t linear_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r) { return linear_ws_bytes(M, N, K, r); }
+size_t linear_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r, bool) { return linear_ws_bytes(M, N, K, r); }
 hipError_t noalloc_scratch(void **ptr) {
   static unsigned char fake[256];
   *ptr = fake;
   return hipSuccess;
 }
-hipError_t linear_fwd(const LinearArgs &, const void *, const float *, const float *, void *, void *, hipStream_t) {
+hipError_t linear_fwd(const LinearArgs &, const void *, const float *, const float *, void *, void *, hipStream_t, bool) {
   return reached();
 }
 hipError_t linear_bwd(const LinearArgs &, const void *, const void *, const float *, const float *, void *, float *,

@@ -173,6 +173,43 @@ def test_identity_input_gives_exact_weight(qb, cb):
     assert np.array_equal(gu.host_bf16_bits(dX), nf4.f32_to_bf16_rne(What))
 
 
+@pytest.mark.parametrize("M,N,K,r", [(33, 512, 2048, 64), (100, 832, 2048, 0), (256, 768, 1024, 8),
+                                     (300, 512, 2048, 72), (128, 4096, 4096, 64)])
+def test_mid_m_split_reduction(qb, cb, M, N, K, r):
+    """33 <= M <= 300: few 256 x 256 output tiles, so the large-tile GEMMs
+    split their reduction (forward over K, dX over N) into up to 16 ranges of
+    at least four 64-deep steps, write fp32 partials and sum them in split
+    order into bf16. Splits here: forward 8, 8, 4, 8, 16; dX 2, 3, 3, 2, 16
+    (N = 832 is 13 steps: dX splits of 5, 5 and 3 steps)."""
+    wl = synth.make_linear_workload("midm", M=M, N=N, K=K, r=r, alpha=16.0,
+                                    seed=7300 + M + r, w_dtype="bf16")
+    c = Case(qb, wl, cb)
+    _fwd(qb, c, f"mid-M M={M} N={N} K={K} r={r}")
+    _bwd(qb, c, f"mid-M M={M} N={N} K={K} r={r}")
+
+
+def test_identity_input_exact_with_split_reduction(qb, cb):
+    """X = I (M = K = 512, N = 256) and dY = I (M = N = 512, K = 256): two
+    output tiles, so both GEMMs split their reduction in two; the partial
+    without the nonzero product adds +0, so Y = bf16(W-hat^T) and
+    dX = bf16(W-hat) still hold bit for bit."""
+    import torch
+    rng = np.random.default_rng(5)
+    for N, K in ((256, 512), (512, 256)):
+        w = synth.normal_f32(rng, (N, K), 0.02)
+        q = qb.qlora_nf4_quantize(gu.dev_f32(w))
+        What = nf4.dequantize(nf4.quantize(w, cb), cb)
+        if K == 512:
+            gu.announce("identity fwd, split reduction")
+            Y = qb.qlora_linear_fwd(torch.eye(K, dtype=torch.bfloat16, device="cuda"), q)
+            assert np.array_equal(gu.host_bf16_bits(Y), nf4.f32_to_bf16_rne(What.T.copy()))
+        else:
+            gu.announce("identity bwd, split reduction")
+            dY = torch.eye(N, dtype=torch.bfloat16, device="cuda")
+            dX, _, _ = qb.qlora_linear_bwd(dY, torch.zeros((N, K), dtype=torch.bfloat16, device="cuda"), q)
+            assert np.array_equal(gu.host_bf16_bits(dX), nf4.f32_to_bf16_rne(What))
+
+
 def test_zero_scale_and_zero_adapter(qb, cb):
     wl = synth.make_linear_workload("zs", M=64, N=256, K=256, r=8, alpha=0.0, seed=9)
     c = Case(qb, wl, cb)
