@@ -120,6 +120,28 @@ struct GemvParams {
 };
 
 
+// Raw buffer loads: a load whose offset lies past the buffer's end returns
+// zero without a memory access, so every load of the row-stream kernel is
+// issued unconditionally (no branch around a load, whose join would make the
+// compiler wait for every load in flight) and the ones that must not happen
+// get kOob.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t buf_b32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ int buf_i8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return static_cast<int>(static_cast<int8_t>(__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0)));
+}
+
 // X[0:M][k0 : k0 + len) (len a multiple of 64) staged into LDS rows of
 // `stride` bf16, zero from len up to `width` (a multiple of 8): at most XP
 // 16-byte pieces per thread. load() issues the reads (stripes with no piece
@@ -329,7 +351,10 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
   xst.load(p.X, p.K, M, blk0 * kBlock, nblk * kBlock, nqp * 128);
   ScaleStage<kDq> sst;
   sst.load(p, static_cast<int64_t>(s) * RN, RN, kb, blk0, nblk);
-  const float mu = kDq ? p.dq_mean[0] : 0.0f;
+  // a vector load: a scalar one would hold up the prologue's barrier (which
+  // waits for scalar accesses too) until it came back from behind the code
+  // stream
+  const float mu = kDq ? __uint_as_float(buf_b32(buf(p.dq_mean, 4), 0)) : 0.0f;
   // With one row tile of X (M <= 8) the code words are requested right
   // after the table is built, before the prologue's LDS stores of X and the
   // constants: those wait only for the older loads, so the prologue finishes
@@ -340,11 +365,17 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
   // quad-pieces [j0, j1) of the slice; the first half goes out in the
   // prologue, the second half once the first quad-piece is decoded (all at
   // once streamed about 5 % slower at M = 4: fewer requests in flight per CU)
+  // (raw buffer loads from the strip's rows: plain loads were moved past the
+  // prologue's barrier by the compiler, so the code stream started only after
+  // the X slice and the constants had arrived)
+  const int64_t nrow0 = static_cast<int64_t>(s) * RN;   // the strip's first row
+  const __amdgpu_buffer_rsrc_t bcw =
+      buf(p.codes + nrow0 * kb * (kBlock / 2), min<int64_t>(RN, p.N - nrow0) * kb * (kBlock / 2));
+  const uint32_t cwoff = static_cast<uint32_t>(((n - nrow0) * kb + blk0) * (kBlock / 2)) + 16u * (g & 1);
   auto request_range = [&](int j0, int j1) {
 #pragma unroll
     for (int jq = 0; jq < NQ; ++jq)
-      if (jq >= j0 && jq < j1)
-        cw[jq] = *reinterpret_cast<const uint4 *>(p.codes + (rowblk + blk0 + blk_of(jq)) * (kBlock / 2) + 16 * (g & 1));
+      if (jq >= j0 && jq < j1) cw[jq] = buf_b128(bcw, cwoff + static_cast<uint32_t>(blk_of(jq)) * (kBlock / 2));
   };
   auto request_codes = [&]() { request_range(0, NQ / 2); };
 
@@ -616,27 +647,6 @@ __device__ __forceinline__ float *rs_aux(char *smem, int i) {
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
-// Raw buffer loads: a load whose offset lies past the buffer's end returns
-// zero without a memory access, so every load of the row-stream kernel is
-// issued unconditionally (no branch around a load, whose join would make the
-// compiler wait for every load in flight) and the ones that must not happen
-// get kOob.
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-constexpr uint32_t kOob = 0x80000000u;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf(const void *base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ uint32_t buf_b32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-__device__ __forceinline__ int buf_i8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return static_cast<int>(static_cast<int8_t>(__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0)));
-}
 
 // fp32(s / 127) for s >= 0 in three operations: the product with fp32(1/127)
 // corrected once by its fused remainder. Equal to the correctly rounded
