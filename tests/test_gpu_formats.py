@@ -121,12 +121,15 @@ def linear_case(qb, fmt, M, N, K, r, seed):
 
 
 @pytest.mark.parametrize("fmt", list(FORMATS))
-@pytest.mark.parametrize("M,K", [(1, 2240), (7, 2240), (16, 448), (32, 2240), (130, 448), (300, 448)])
+@pytest.mark.parametrize("M,K", [(1, 2240), (7, 2240), (16, 448), (32, 2240), (130, 448), (300, 448),
+                                 (100, 2048)])
 @pytest.mark.parametrize("r", [0, 72])
 def test_linear_fwd_bwd(qb, fmt, M, K, r):
     """Decode path (M <= 32; K = 2240: several K splits, absmax bytes not
     dword aligned) and the large-tile path (M > 32) forward, and the backward
-    at every M (small M runs the large-tile kernels on partial tiles)."""
+    at every M (small M runs the large-tile kernels on partial tiles). At
+    M = 100, K = 2048 the forward's two output tiles split the reduction in
+    eight."""
     N = 320
     wl, q, What = linear_case(qb, fmt, M, N, K, r, seed=fmt * 1000 + M * 10 + r)
     X = gu.dev_bf16(wl.X)
