@@ -487,9 +487,15 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
   }
 
   // ---- B rows of the adapter's up projection for the output waves (slice 0),
-  // loaded now so that they travel during the waits below (first 64 columns)
+  // loaded now so that they travel during the waits below (first 64 columns).
+  // The adapter flags are polled by a wave that loads no B rows when there is
+  // one (T < 8: the last wave), since a poll completes only after every load
+  // its wave issued before (vector-memory loads retire in order); with T = 8
+  // every wave is an output wave and wave 0 polls behind its B rows (asking
+  // for them after the poll instead measured slower).
   float bpre[16];
   const bool out_wave = ks == 0;
+  const bool poller = w == (T < kGvWaves ? kGvWaves - 1 : 0);
   if (p.r > 0 && out_wave) {
     const float *brow = p.B + n * p.r;
 #pragma unroll
@@ -524,7 +530,7 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
   const int hstride = p.rp + 8;
   if (p.r > 0) {
     const int G = p.rp / 16;   // column groups: one flag each (at most 16)
-    if (w == 0) {
+    if (poller) {
       uint32_t *fl = p.flags + static_cast<int64_t>(s) * G;
       for (int spins = 0;; ++spins) {
         const bool mine = lane >= G || ld_wt(fl + lane) != 0u;
