@@ -460,6 +460,25 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[mt][e] = __builtin_fmaf(cb, ta[mt][e] + tb[mt][e], acc[mt][e]);
   }
+  // ---- B rows of the adapter's up projection for the output waves (slice 0),
+  // requested as soon as the main loop's registers are free, so that they
+  // travel during the slice sums and the waits below (first 64 columns).
+  // The adapter flags are polled by a wave that loads no B rows when there is
+  // one (T < 8: the last wave), since a poll completes only after every load
+  // its wave issued before (vector-memory loads retire in order); with T = 8
+  // every wave is an output wave and wave 0 polls behind its B rows (asking
+  // for them after the poll instead measured slower).
+  float bpre[16];
+  const bool out_wave = ks == 0;
+  const bool poller = w == (T < kGvWaves ? kGvWaves - 1 : 0);
+  if (p.r > 0 && out_wave) {
+    const float *brow = p.B + n * p.r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bpre[8 * h + i] = brow[min(32 * h + 8 * g + i, p.r - 1)];
+  }
+
   // the two blocks' rows: lanes l and l + 32 hold the same outputs
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -484,24 +503,6 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
     float v = red[i];
     for (int k2 = 1; k2 < KS; ++k2) v += red[k2 * M * RN + i];
     bsum[i] = v;
-  }
-
-  // ---- B rows of the adapter's up projection for the output waves (slice 0),
-  // loaded now so that they travel during the waits below (first 64 columns).
-  // The adapter flags are polled by a wave that loads no B rows when there is
-  // one (T < 8: the last wave), since a poll completes only after every load
-  // its wave issued before (vector-memory loads retire in order); with T = 8
-  // every wave is an output wave and wave 0 polls behind its B rows (asking
-  // for them after the poll instead measured slower).
-  float bpre[16];
-  const bool out_wave = ks == 0;
-  const bool poller = w == (T < kGvWaves ? kGvWaves - 1 : 0);
-  if (p.r > 0 && out_wave) {
-    const float *brow = p.B + n * p.r;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) bpre[8 * h + i] = brow[min(32 * h + 8 * g + i, p.r - 1)];
   }
 
   // ---- split reduction: the last of the strip's C workgroups finishes it
@@ -544,8 +545,12 @@ __global__ __launch_bounds__(kGvThreads, 2) void k_gemv(GemvParams p) {
       if (lane < G) st_wt(fl + lane, 0u);
     }
     __syncthreads();
+    // H is read by the waves that load no B rows when there are such (T < 8),
+    // so that its loads do not retire behind theirs
     const int nh = M * p.rp;   // H[m][j], m < M
-    for (int e = tid; e < 16 * MT16 * p.rp; e += kGvThreads) {
+    const int h0 = T < kGvWaves ? 64 * T : 0;
+    for (int e = tid - h0; e < 16 * MT16 * p.rp; e += kGvThreads - h0) {
+      if (e < 0) break;
       const int m = e / p.rp, jj = e - m * p.rp;
       const float h = e < nh ? ld_wt(p.hfin + e) : 0.0f;
       hs[m * hstride + jj] = static_cast<__bf16>(e < nh && jj < p.r ? p.scale * h : 0.0f);
