@@ -4,9 +4,12 @@ called through the C ABI) against the workspace forward qlora_linear_fwd.
 Both run the same kernels, so the bar is bit-identical outputs (tighter than
 the 2e-2 bar of the forward itself). Calls come back to back on one stream,
 each smaller than the one before it (a split-reduction decode shape, a small
-decode shape, then a large-tile shape and a decode shape again), so the
-library's one scratch array is reused with the previous call's contents in
-it."""
+decode shape, then a large-tile shape, a large-tile shape whose GEMM splits
+its reduction, and a decode shape again), so the library's one scratch array
+is reused with the previous call's contents in it. Where the split partials
+would not fit the scratch, the allocation-free forward runs the reduction in
+one pass: then it differs from the workspace forward only in the order of the
+fp32 sums, and the bar is the forward's own."""
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -37,7 +40,8 @@ def _case(qb, M, N, K, r, seed):
 def test_noalloc_matches_workspace_forward(qb):
     import torch
     from tests import gpu_util as gu
-    shapes = [(16, 4096, 11008, 64), (1, 320, 2240, 72), (300, 320, 448, 72), (4, 1024, 576, 8)]
+    shapes = [(16, 4096, 11008, 64), (1, 320, 2240, 72), (300, 320, 448, 72), (64, 512, 2048, 8),
+              (4, 1024, 576, 8)]
     for i, (M, N, K, r) in enumerate(shapes):
         q, X, A, B = _case(qb, M, N, K, r, 100 + i)
         gu.announce(f"noalloc fwd M={M} N={N} K={K} r={r}")
@@ -50,6 +54,32 @@ def test_noalloc_matches_workspace_forward(qb):
         torch.cuda.synchronize()
         assert torch.equal(Y1, Y0), f"M={M} N={N} K={K} r={r}: allocation-free forward differs"
         assert torch.equal(Y2, Y0), f"M={M} N={N} K={K} r={r}: second allocation-free call differs"
+
+
+def test_noalloc_one_pass_where_split_partials_do_not_fit(qb):
+    """M = 256 at 4096 x 4096: the workspace forward splits the reduction in
+    16 (64 MiB of partials, more than the scratch holds with the rest), the
+    allocation-free one runs it in one pass. Two allocation-free calls agree
+    bit for bit; against the workspace forward the relative Frobenius
+    difference is within the regression bound of the forward (5e-3), and
+    every 256 x 256 tile within the 2e-2 bar."""
+    import torch
+    from tests import gpu_util as gu
+    M, N, K, r = 256, 4096, 4096, 64
+    q, X, A, B = _case(qb, M, N, K, r, 200)
+    gu.announce(f"noalloc one-pass fwd M={M} N={N} K={K} r={r}")
+    Y0 = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    Y1 = torch.empty_like(Y0)
+    Y2 = torch.empty_like(Y0)
+    qb.qlora_linear_fwd_noalloc(X, q, A, B, 0.25, out=Y1)
+    qb.qlora_linear_fwd_noalloc(X, q, A, B, 0.25, out=Y2)
+    qb.qlora_linear_fwd(X, q, A, B, 0.25, out=Y0)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2), "second allocation-free call differs"
+    a, b = gu.host_bf16_f32(Y1), gu.host_bf16_f32(Y0)
+    e = gu.rel_fro(a, b)
+    assert e <= 5e-3, f"one-pass vs split forward rel diff {e}"
+    assert gu.max_tile_rel(a, b) <= 2e-2
 
 
 def test_noalloc_refuses_oversized_call(qb):
