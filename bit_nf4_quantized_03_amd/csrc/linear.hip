@@ -20,6 +20,9 @@
 //                     transposed (reduction over out_features)
 //   k_grad            split-M partials of dA = dHb^T X and dB = dY^T Hs
 //   k_grad_finish     fixed-order sums of those partials
+//   k_split_out       when the output tiles fill less than half the GPU, the
+//                     two GEMMs above split their reduction into fp32 partials
+//                     and this sums them in split order into bf16
 // Small M (decode, M <= 32) runs the single-launch weight-streaming kernel of
 // gemv.hip instead.
 #include <algorithm>
@@ -56,7 +59,10 @@ struct FwdParams {
 
 // Large-M forward: one 256 x 256 tile of Y per workgroup (XCD-aware order),
 // run with eight waves (CfgBig8): two waves per SIMD cover each other's
-// waits, at 128 x 64 accumulators per wave.
+// waits, at 128 x 64 accumulators per wave. With S > 1 the grid holds S
+// copies of the tiles, copy z running reduction steps [z per, (z + 1) per)
+// and writing its fp32 partial tile (z = 0 adds the adapter steps);
+// k_split_out sums them.
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::kThreads, 1) void k_fwd_big(FwdParams p, Nf4Tables tab) {
   constexpr int T = Cfg::kThreads;
@@ -115,7 +121,8 @@ struct DxParams {
 // Input gradient: one 256 x 256 tile of dX per workgroup (XCD-aware order),
 // run with eight waves as the forward is: the transposed decode gives each
 // thread half an 8 x 8 unit (four rows n), which keeps the kernel within the
-// registers two waves per SIMD leave.
+// registers two waves per SIMD leave. Split reduction (over N) as in the
+// forward.
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::kThreads, 1) void k_dx_big(DxParams p, Nf4Tables tab) {
   constexpr int T = Cfg::kThreads;
