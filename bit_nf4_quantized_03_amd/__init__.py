@@ -24,7 +24,7 @@ __all__ = [
     "QLORA_FMT_NF4_DQ", "QLORA_FMT_NF4", "QLORA_FMT_FP4_DQ", "QLORA_FMT_FP4",
     "qlora_nf4_merge_workspace_bytes", "qlora_nf4_merge",
     "qlora_adamw_workspace_bytes", "qlora_adamw_step", "linear_workspace", "LINEAR_SYNC_BYTES",
-    "qlora_linear_fwd_noalloc",
+    "qlora_linear_fwd_noalloc", "qlora_linear_fwd_save", "qlora_linear_bwd_saved",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora_nf4.so")
@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "qlora_weight_storage_bytes", "qlora_format_levels",
     "qlora_nf4_merge_workspace_bytes", "qlora_nf4_merge",
     "qlora_adamw_workspace_bytes", "qlora_adamw_step", "qlora_linear_fwd_noalloc",
+    "qlora_linear_fwd_save", "qlora_linear_bwd_saved",
 )
 
 
@@ -87,6 +88,9 @@ def _load():
         "qlora_linear_fwd": (ctypes.c_int, [vp, i64, wp, vp, vp, i32, f32, vp, vp, sz, vp]),
         "qlora_linear_bwd": (ctypes.c_int, [vp, vp, i64, wp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
         "qlora_linear_fwd_noalloc": (ctypes.c_int, [vp, i64, wp, vp, vp, i32, f32, vp, vp]),
+        "qlora_linear_fwd_save": (ctypes.c_int, [vp, i64, wp, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
+        "qlora_linear_bwd_saved": (ctypes.c_int,
+                                   [vp, vp, vp, i64, wp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
         "qlora_nf4_merge_workspace_bytes": (sz, [i64, i64, i32]),
         "qlora_nf4_merge": (ctypes.c_int, [wp, vp, vp, i32, f32, wp, vp, sz, vp]),
         "qlora_adamw_workspace_bytes": (sz, [i64, ctypes.c_int]),
@@ -435,18 +439,38 @@ def qlora_linear_fwd(X, W: NF4Weight, A=None, B=None, scale: float = 0.0, ws=Non
     return out
 
 
-def qlora_linear_bwd(dY, X, W: NF4Weight, A=None, B=None, scale: float = 0.0, ws=None,
-                     outs: Optional[Tuple] = None):
-    """(dX, dA, dB) of the QLoRA linear layer; the base weight gets no gradient."""
+def qlora_linear_fwd_save(X, W: NF4Weight, A, B, scale: float, ws=None, out=None, hs=None):
+    """(Y, Hs): qlora_linear_fwd's Y and the adapter activations Hs =
+    bf16(scale X A^T) [M, r] that qlora_linear_bwd_saved takes (r >= 1)."""
     torch = _torch()
     M = _activation("X", X, W)
     K, N = W.cols, W.rows
-    _need_cuda("dY", dY, torch.bfloat16, (M, N), W.device)
     r = _adapter(W, A, B, W.device)
+    if r == 0:
+        raise ValueError("qlora_linear_fwd_save needs an adapter (r >= 1)")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    else:
+        _need_cuda("out", out, torch.bfloat16, (M, N), W.device)
+    if hs is None:
+        hs = torch.empty((M, r), dtype=torch.bfloat16, device=X.device)
+    else:
+        _need_cuda("hs", hs, torch.bfloat16, (M, r), W.device)
+    ws = _linear_ws(M, N, K, r, X.device, ws)
+    st = W.c_struct()
+    _check("qlora_linear_fwd_save",
+           lib.qlora_linear_fwd_save(_ptr(X), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale),
+                                     _ptr(out), _ptr(hs), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream_ptr(X.device)))
+    return out, hs
+
+
+def _bwd_outs(M, N, K, r, W, device, outs):
+    torch = _torch()
     if outs is None:
-        dX = torch.empty((M, K), dtype=torch.bfloat16, device=X.device)
-        dA = torch.empty((r, K), dtype=torch.float32, device=X.device) if r else None
-        dB = torch.empty((N, r), dtype=torch.float32, device=X.device) if r else None
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=device)
+        dA = torch.empty((r, K), dtype=torch.float32, device=device) if r else None
+        dB = torch.empty((N, r), dtype=torch.float32, device=device) if r else None
     else:
         dX, dA, dB = outs
         _need_cuda("dX", dX, torch.bfloat16, (M, K), W.device)
@@ -455,12 +479,46 @@ def qlora_linear_bwd(dY, X, W: NF4Weight, A=None, B=None, scale: float = 0.0, ws
             _need_cuda("dB", dB, torch.float32, (N, r), W.device)
         elif dA is not None or dB is not None:
             raise ValueError("without an adapter dA and dB must be None")
+    return dX, dA, dB
+
+
+def qlora_linear_bwd(dY, X, W: NF4Weight, A=None, B=None, scale: float = 0.0, ws=None,
+                     outs: Optional[Tuple] = None):
+    """(dX, dA, dB) of the QLoRA linear layer; the base weight gets no gradient."""
+    torch = _torch()
+    M = _activation("X", X, W)
+    K, N = W.cols, W.rows
+    _need_cuda("dY", dY, torch.bfloat16, (M, N), W.device)
+    r = _adapter(W, A, B, W.device)
+    dX, dA, dB = _bwd_outs(M, N, K, r, W, X.device, outs)
     ws = _linear_ws(M, N, K, r, X.device, ws)
     st = W.c_struct()
     _check("qlora_linear_bwd",
            lib.qlora_linear_bwd(_ptr(dY), _ptr(X), M, ctypes.byref(st), _ptr(A), _ptr(B), r,
                                 float(scale), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream_ptr(X.device)))
+    return dX, dA, dB
+
+
+def qlora_linear_bwd_saved(dY, X, Hs, W: NF4Weight, A, B, scale: float, ws=None,
+                           outs: Optional[Tuple] = None):
+    """qlora_linear_bwd with the Hs of qlora_linear_fwd_save (same X, A and
+    scale): the adapter activations are not formed again (r >= 1)."""
+    torch = _torch()
+    M = _activation("X", X, W)
+    K, N = W.cols, W.rows
+    _need_cuda("dY", dY, torch.bfloat16, (M, N), W.device)
+    r = _adapter(W, A, B, W.device)
+    if r == 0:
+        raise ValueError("qlora_linear_bwd_saved needs an adapter (r >= 1)")
+    _need_cuda("Hs", Hs, torch.bfloat16, (M, r), W.device)
+    dX, dA, dB = _bwd_outs(M, N, K, r, W, X.device, outs)
+    ws = _linear_ws(M, N, K, r, X.device, ws)
+    st = W.c_struct()
+    _check("qlora_linear_bwd_saved",
+           lib.qlora_linear_bwd_saved(_ptr(dY), _ptr(X), _ptr(Hs), M, ctypes.byref(st), _ptr(A), _ptr(B),
+                                      r, float(scale), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream_ptr(X.device)))
     return dX, dA, dB
 
 

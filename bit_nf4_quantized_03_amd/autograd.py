@@ -1,7 +1,10 @@
 """torch.autograd wrapper of the QLoRA linear layer.
 
-Marshalling only: the forward is one ``qlora_linear_fwd`` call and the
-backward one ``qlora_linear_bwd`` call (QLoRA vs ChatGPT page, capability
+Marshalling only: the forward is one ``qlora_linear_fwd_save`` call, which
+also keeps the adapter activations bf16(scale X A^T) [M, r], and the backward
+one ``qlora_linear_bwd_saved`` call that takes them instead of forming them
+again (``qlora_linear_fwd`` / ``qlora_linear_bwd`` without an adapter)
+(QLoRA vs ChatGPT page, capability
 "training pipeline": the 4-bit base is frozen and dequantized on the fly,
 gradients go to the low-rank adapter and the input). It lets a caller compose
 projections into a larger model with autograd, recompute them under
@@ -14,7 +17,7 @@ from __future__ import annotations
 
 import torch
 
-from . import NF4Weight, qlora_linear_bwd, qlora_linear_fwd
+from . import NF4Weight, qlora_linear_bwd, qlora_linear_bwd_saved, qlora_linear_fwd, qlora_linear_fwd_save
 
 
 class QLoRALinearFn(torch.autograd.Function):
@@ -22,16 +25,22 @@ class QLoRALinearFn(torch.autograd.Function):
     def forward(ctx, X, A, B, W: NF4Weight, scale: float):
         lead = X.shape[:-1]
         X2 = X.reshape(-1, X.shape[-1]).contiguous()
-        Y = qlora_linear_fwd(X2, W, A, B, scale)
-        ctx.save_for_backward(X2, A, B)
+        if A is not None:
+            Y, Hs = qlora_linear_fwd_save(X2, W, A, B, scale)
+        else:
+            Y, Hs = qlora_linear_fwd(X2, W, A, B, scale), None
+        ctx.save_for_backward(X2, A, B, Hs)
         ctx.W, ctx.scale, ctx.lead = W, scale, lead
         return Y.reshape(*lead, W.rows)
 
     @staticmethod
     def backward(ctx, dY):
-        X2, A, B = ctx.saved_tensors
+        X2, A, B, Hs = ctx.saved_tensors
         dY2 = dY.reshape(-1, ctx.W.rows).to(torch.bfloat16).contiguous()
-        dX, dA, dB = qlora_linear_bwd(dY2, X2, ctx.W, A, B, ctx.scale)
+        if Hs is not None:
+            dX, dA, dB = qlora_linear_bwd_saved(dY2, X2, Hs, ctx.W, A, B, ctx.scale)
+        else:
+            dX, dA, dB = qlora_linear_bwd(dY2, X2, ctx.W, A, B, ctx.scale)
         return dX.reshape(*ctx.lead, ctx.W.cols), dA, dB, None, None
 
 

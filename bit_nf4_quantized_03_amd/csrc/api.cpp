@@ -103,6 +103,29 @@ qnf4::LinearArgs make_args(int64_t M, const qlora_nf4_weight *W, int32_t r, floa
   return a;
 }
 
+// The checks and the call of both backward entry points (Hs = NULL: the
+// backward forms the adapter activations itself).
+int linear_bwd_checked(const char *fn, const void *dY, const void *X, const void *Hs, int64_t M,
+                       const qlora_nf4_weight *W, const float *A, const float *B, int32_t r, float scale,
+                       void *dX, float *dA, float *dB, void *ws, size_t ws_bytes, void *stream) {
+  if (!dY || !X || !dX) return fail(QLORA_ERR_NULL, "%s: dY, X and dX must not be NULL", fn);
+  int st = check_linear_common(fn, M, W, A, B, r);
+  if (st != QLORA_OK) return st;
+  if (r > 0 && (!dA || !dB)) return fail(QLORA_ERR_NULL, "%s: r > 0 needs dA and dB", fn);
+  if (r == 0 && (dA || dB)) return fail(QLORA_ERR_SHAPE, "%s: r = 0 needs dA = dB = NULL", fn);
+  if (!aligned16(dY) || !aligned16(X) || !aligned16(dX) || (dA && !aligned16(dA)) ||
+      (dB && !aligned16(dB)))
+    return fail(QLORA_ERR_ALIGN, "%s: tensors must be 16-byte aligned", fn);
+  const size_t need = qnf4::linear_ws_bytes(M, W->rows, W->cols, r);
+  if (!ws || ws_bytes < need)
+    return fail(QLORA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need,
+                ws ? ws_bytes : size_t(0));
+  if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  hipError_t e = qnf4::linear_bwd(make_args(M, W, r, scale), dY, X, A, B, dX, dA, dB, ws,
+                                  static_cast<hipStream_t>(stream), Hs);
+  return hip_status(e, fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -212,26 +235,43 @@ int qlora_linear_fwd(const void *X, int64_t M, const qlora_nf4_weight *W, const 
   return hip_status(e, fn);
 }
 
-int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qlora_nf4_weight *W,
-                     const float *A, const float *B, int32_t r, float scale, void *dX, float *dA,
-                     float *dB, void *ws, size_t ws_bytes, void *stream) {
-  const char *fn = "qlora_linear_bwd";
-  if (!dY || !X || !dX) return fail(QLORA_ERR_NULL, "%s: dY, X and dX must not be NULL", fn);
+int qlora_linear_fwd_save(const void *X, int64_t M, const qlora_nf4_weight *W, const float *A,
+                          const float *B, int32_t r, float scale, void *Y, void *Hs, void *ws,
+                          size_t ws_bytes, void *stream) {
+  const char *fn = "qlora_linear_fwd_save";
+  if (!X || !Y) return fail(QLORA_ERR_NULL, "%s: X and Y must not be NULL", fn);
   int st = check_linear_common(fn, M, W, A, B, r);
   if (st != QLORA_OK) return st;
-  if (r > 0 && (!dA || !dB)) return fail(QLORA_ERR_NULL, "%s: r > 0 needs dA and dB", fn);
-  if (r == 0 && (dA || dB)) return fail(QLORA_ERR_SHAPE, "%s: r = 0 needs dA = dB = NULL", fn);
-  if (!aligned16(dY) || !aligned16(X) || !aligned16(dX) || (dA && !aligned16(dA)) ||
-      (dB && !aligned16(dB)))
-    return fail(QLORA_ERR_ALIGN, "%s: tensors must be 16-byte aligned", fn);
+  if (r == 0) return fail(QLORA_ERR_SHAPE, "%s: r = 0 has no adapter activations to keep", fn);
+  if (!Hs) return fail(QLORA_ERR_NULL, "%s: Hs must not be NULL", fn);
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(Hs))
+    return fail(QLORA_ERR_ALIGN, "%s: X, Y and Hs must be 16-byte aligned", fn);
   const size_t need = qnf4::linear_ws_bytes(M, W->rows, W->cols, r);
   if (!ws || ws_bytes < need)
     return fail(QLORA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need,
                 ws ? ws_bytes : size_t(0));
   if (!aligned16(ws)) return fail(QLORA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
-  hipError_t e = qnf4::linear_bwd(make_args(M, W, r, scale), dY, X, A, B, dX, dA, dB, ws,
-                                  static_cast<hipStream_t>(stream));
+  hipError_t e = qnf4::linear_fwd(make_args(M, W, r, scale), X, A, B, Y, ws,
+                                  static_cast<hipStream_t>(stream), true, Hs);
   return hip_status(e, fn);
+}
+
+int qlora_linear_bwd_saved(const void *dY, const void *X, const void *Hs, int64_t M,
+                           const qlora_nf4_weight *W, const float *A, const float *B, int32_t r,
+                           float scale, void *dX, float *dA, float *dB, void *ws, size_t ws_bytes,
+                           void *stream) {
+  const char *fn = "qlora_linear_bwd_saved";
+  if (!Hs) return fail(QLORA_ERR_NULL, "%s: Hs must not be NULL", fn);
+  if (!aligned16(Hs)) return fail(QLORA_ERR_ALIGN, "%s: Hs must be 16-byte aligned", fn);
+  if (r == 0) return fail(QLORA_ERR_SHAPE, "%s: r = 0 has no adapter activations", fn);
+  return linear_bwd_checked(fn, dY, X, Hs, M, W, A, B, r, scale, dX, dA, dB, ws, ws_bytes, stream);
+}
+
+int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qlora_nf4_weight *W,
+                     const float *A, const float *B, int32_t r, float scale, void *dX, float *dA,
+                     float *dB, void *ws, size_t ws_bytes, void *stream) {
+  return linear_bwd_checked("qlora_linear_bwd", dY, X, nullptr, M, W, A, B, r, scale, dX, dA, dB, ws,
+                            ws_bytes, stream);
 }
 
 int qlora_linear_fwd_noalloc(const void *X, int64_t M, const qlora_nf4_weight *W, const float *A,

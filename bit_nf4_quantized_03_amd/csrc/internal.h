@@ -100,11 +100,13 @@ hipError_t noalloc_scratch(void **ptr);
 // allow_split = false keeps the large-tile forward to one pass over the
 // reduction (no split partials in the workspace), for a caller whose scratch
 // is bounded.
+// hs_out (optional): the adapter activations bf16(s X A^T) [M][r] for a later
+// linear_bwd (hs_in), so that the backward does not form them again.
 hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const float *B,
-                      void *Y, void *ws, hipStream_t s, bool allow_split = true);
+                      void *Y, void *ws, hipStream_t s, bool allow_split = true, void *hs_out = nullptr);
 hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const float *A,
                       const float *B, void *dX, float *dA, float *dB, void *ws,
-                      hipStream_t s);
+                      hipStream_t s, const void *hs_in = nullptr);
 
 // ------------------------------------------------------------------- merge
 // W' = fp32(w-hat + s B A) (rank sum in fp64) into the workspace, then

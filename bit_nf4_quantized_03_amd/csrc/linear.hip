@@ -616,6 +616,24 @@ __global__ __launch_bounds__(256) void k_split_out(const float *part, int S, int
   *reinterpret_cast<uint2 *>(out + e) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
 }
 
+// dst[m][j] = src[m][j] for j < ncopy, 0 for ncopy <= j < ndst (the saved
+// adapter activations between the caller's [M][r] and the kernels' [M][rp]).
+__global__ __launch_bounds__(256) void k_cols_copy(const __bf16 *src, int64_t sld, __bf16 *dst, int64_t dld,
+                                                   int64_t M, int ncopy, int ndst) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= M * ndst) return;
+  const int64_t m = i / ndst;
+  const int j = static_cast<int>(i - m * ndst);
+  dst[m * dld + j] = j < ncopy ? src[m * sld + j] : static_cast<__bf16>(0.0f);
+}
+
+hipError_t cols_copy(const __bf16 *src, int64_t sld, __bf16 *dst, int64_t dld, int64_t M, int ncopy, int ndst,
+                     hipStream_t s) {
+  hipLaunchKernelGGL(k_cols_copy, dim3(static_cast<unsigned>(ceil_div(M * ndst, static_cast<int64_t>(256)))),
+                     dim3(256), 0, s, src, sld, dst, dld, M, ncopy, ndst);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------- tile configs
 constexpr int kSmallM = 32;
 constexpr int kTargetGroups = 512;
@@ -651,6 +669,7 @@ struct Carve {
 struct Plan {
   int rp;
   Split down, hb, dh, ga, gb;   // forward H; backward H and dY B; dA; dB
+  Split dhs;                    // backward dY B alone (H saved by the forward)
   Split fs, xs;                 // reduction splits of the forward and dX GEMMs
   bool small;
 };
@@ -685,6 +704,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int r, bool allow_split = true) 
   pl.down = choose_split(skinny_tiles, ksteps, 64, kDownGroups);
   pl.hb = choose_split(skinny_tiles, ksteps, 64, kDownGroups / 2);
   pl.dh = choose_split(skinny_tiles, nsteps, 64, kDownGroups / 2);
+  pl.dhs = choose_split(skinny_tiles, nsteps, 64, kDownGroups);
   const int msteps = static_cast<int>(ceil_div(M, kBK));
   pl.ga = choose_split(grid_blocks(pl.rp, 64) * grid_blocks(K, 256), msteps, 8);
   pl.gb = choose_split(grid_blocks(N, 256) * grid_blocks(pl.rp, 64), msteps, 8);
@@ -720,7 +740,7 @@ Buffers carve(void *ws, const Plan &pl, int64_t M, int64_t N, int64_t K, size_t 
     b.down_part = c.take<float>(static_cast<size_t>(std::max(pl.down.splits, pl.hb.splits)) * M * rp);
     b.Hs = c.take<__bf16>(static_cast<size_t>(M) * rp);
     b.Bb = c.take<__bf16>(static_cast<size_t>(N) * rp);
-    b.dh_part = c.take<float>(static_cast<size_t>(pl.dh.splits) * M * rp);
+    b.dh_part = c.take<float>(static_cast<size_t>(std::max(pl.dh.splits, pl.dhs.splits)) * M * rp);
     b.dHb = c.take<__bf16>(static_cast<size_t>(M) * rp);
     b.Atb = c.take<__bf16>(static_cast<size_t>(K) * rp);
     b.ga_part = c.take<float>(static_cast<size_t>(pl.ga.splits) * rp * K);
@@ -737,8 +757,14 @@ const float *block_scales(const LinearArgs &a, const Buffers &b) { return fmt_dq
 // The work before a big GEMM: the split partials of H = X A^T and (backward)
 // dY B, then one launch with their sums, the block scales and the bf16 adapter
 // operand of the GEMM (Bb forward, Atb backward).
+// With h_given (backward only) the forward's bf16(s H) is supplied by the
+// caller: no H partials or sums, and dY B takes every down-projection
+// workgroup.
 hipError_t run_adapter_pre(const LinearArgs &a, const Plan &pl, const Buffers &b, const void *X,
-                           const void *dY, const float *A, const float *B, bool backward, hipStream_t s) {
+                           const void *dY, const float *A, const float *B, bool backward, hipStream_t s,
+                           bool h_given = false) {
+  const bool skip_h = backward && h_given;
+  const Split &dhp = skip_h ? pl.dhs : pl.dh;
   const bool lora = pl.rp > 0;
   if (lora) {
     DownParams dp{};
@@ -756,10 +782,10 @@ hipError_t run_adapter_pre(const LinearArgs &a, const Plan &pl, const Buffers &b
     dp.jt = pl.rp / 64;
     dp.mt = static_cast<int>(ceil_div(a.M, kDownRows));
     const Split &hs = backward ? pl.hb : pl.down;
-    dp.h_splits = hs.splits;
+    dp.h_splits = skip_h ? 0 : hs.splits;
     dp.h_steps = hs.steps_per_split;
-    dp.dh_splits = backward ? pl.dh.splits : 0;
-    dp.dh_steps = pl.dh.steps_per_split;
+    dp.dh_splits = backward ? dhp.splits : 0;
+    dp.dh_steps = dhp.steps_per_split;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k_adapter_down),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        static_cast<int>(kDownLds));
@@ -776,7 +802,7 @@ hipError_t run_adapter_pre(const LinearArgs &a, const Plan &pl, const Buffers &b
   fp.r = a.r;
   fp.rp = pl.rp;
   fp.h_splits = backward ? pl.hb.splits : pl.down.splits;
-  fp.dh_splits = pl.dh.splits;
+  fp.dh_splits = dhp.splits;
   fp.scale = a.scale;
   fp.absmax_q = a.absmax_q;
   fp.dq_scale = a.dq_scale;
@@ -790,7 +816,7 @@ hipError_t run_adapter_pre(const LinearArgs &a, const Plan &pl, const Buffers &b
   fp.N = a.N;
   fp.K = a.K;
   const int64_t sums = lora ? grid_blocks(a.M * pl.rp / 4, 256) : 0;
-  fp.g_h = sums;
+  fp.g_h = skip_h ? 0 : sums;
   fp.g_dh = backward ? sums : 0;
   // without DQ the stored fp32 constants are the block scales themselves
   fp.g_cs = fmt_dq(a.format) ? grid_blocks(ceil_div(fp.nb, kScaleBlocksPerThread), 256) : 0;
@@ -819,12 +845,29 @@ size_t linear_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r, bool allow_sp
 }
 
 hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const float *B, void *Y,
-                      void *ws, hipStream_t s, bool allow_split) {
+                      void *ws, hipStream_t s, bool allow_split, void *hs_out) {
   const Plan pl = make_plan(a.M, a.N, a.K, a.r, allow_split);
-  if (pl.small) return launch_gemv(a, X, A, B, Y, ws, s);
-  const Buffers b = carve(ws, pl, a.M, a.N, a.K, nullptr);
+  const bool save = hs_out != nullptr && pl.rp > 0;
+  if (pl.small) {
+    hipError_t err = launch_gemv(a, X, A, B, Y, ws, s);
+    if (err != hipSuccess || !save) return err;
+    // the decode kernel forms H inside; the saved activations come from the
+    // down-projection kernels, after it (they reuse its workspace)
+    const Buffers b = carve(ws, pl, a.M, a.N, a.K, nullptr);
+    err = run_adapter_pre(a, pl, b, X, nullptr, A, B, false, s);
+    if (err != hipSuccess) return err;
+    return cols_copy(b.Hs, pl.rp, static_cast<__bf16 *>(hs_out), a.r, a.M, a.r, a.r, s);
+  }
+  Buffers b = carve(ws, pl, a.M, a.N, a.K, nullptr);
+  // with r a multiple of 64 the caller's [M][r] is the kernels' [M][rp]
+  const bool direct = save && a.r == pl.rp;
+  if (direct) b.Hs = static_cast<__bf16 *>(hs_out);
   hipError_t err = run_adapter_pre(a, pl, b, X, nullptr, A, B, false, s);
   if (err != hipSuccess) return err;
+  if (save && !direct) {
+    err = cols_copy(b.Hs, pl.rp, static_cast<__bf16 *>(hs_out), a.r, a.M, a.r, a.r, s);
+    if (err != hipSuccess) return err;
+  }
   FwdParams fp{X, a.codes, block_scales(a, b), b.Hs, b.Bb, Y, a.M, a.N, a.K, pl.rp, b.part, pl.fs.splits,
                pl.fs.steps_per_split};
   dim3 g(grid_blocks(a.N, 256) * grid_blocks(a.M, 256) * pl.fs.splits, 1, 1);
@@ -840,12 +883,22 @@ hipError_t linear_fwd(const LinearArgs &a, const void *X, const float *A, const 
 }
 
 hipError_t linear_bwd(const LinearArgs &a, const void *dY, const void *X, const float *A,
-                      const float *B, void *dX, float *dA, float *dB, void *ws, hipStream_t s) {
+                      const float *B, void *dX, float *dA, float *dB, void *ws, hipStream_t s,
+                      const void *hs_in) {
   const Plan pl = make_plan(a.M, a.N, a.K, a.r);
-  const Buffers b = carve(ws, pl, a.M, a.N, a.K, nullptr);
+  Buffers b = carve(ws, pl, a.M, a.N, a.K, nullptr);
   const Nf4Tables &tab = format_tables(a.format);
-  hipError_t err = run_adapter_pre(a, pl, b, X, dY, A, B, true, s);
+  const bool given = hs_in != nullptr && pl.rp > 0;
+  hipError_t err = run_adapter_pre(a, pl, b, X, dY, A, B, true, s, given);
   if (err != hipSuccess) return err;
+  if (given) {   // the forward's bf16(s H): used in place, or padded to rp columns
+    if (a.r == pl.rp) {
+      b.Hs = const_cast<__bf16 *>(static_cast<const __bf16 *>(hs_in));
+    } else {
+      err = cols_copy(static_cast<const __bf16 *>(hs_in), a.r, b.Hs, pl.rp, a.M, a.r, pl.rp, s);
+      if (err != hipSuccess) return err;
+    }
+  }
   {
     DxParams dp{dY, a.codes, block_scales(a, b), b.dHb, b.Atb, dX, a.M, a.N, a.K, pl.rp, b.part, pl.xs.splits,
                 pl.xs.steps_per_split};

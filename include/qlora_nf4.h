@@ -198,6 +198,9 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
  * adapter activations enter them rounded to bf16. For M > 32 the base enters
  * as bf16(w_i); for M <= 32 (the decode path) it enters as bf16(level) and
  * the fp32 block scale c_b multiplies each block's partial product. M >= 1.
+ * When the 256 x 256 output tiles of M > 32 fill less than half of the GPU,
+ * the reduction over K is split into fp32 partials in the workspace, summed
+ * in a fixed order before the rounding to bf16 (results stay deterministic).
  * The decode path is one kernel launch; its workgroups exchange partial sums
  * through the workspace and wait for one another with bounded spins (see
  * QLORA_LINEAR_SYNC_BYTES for the workspace's leading words).
@@ -223,6 +226,32 @@ int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qlora_nf4_w
                      void *stream);
 
 /*
+ * qlora_linear_fwd that also keeps the adapter activations for the backward,
+ * as a training step saves its activations (QLoRA vs ChatGPT page,
+ * capability "training pipeline"):
+ *   Hs     bf16 [M, r] (device, 16-byte aligned, overwritten) = bf16(scale *
+ *          X A^T), the rounded value the forward multiplies by B^T
+ * r must be at least 1. Other arguments, results and errors as
+ * qlora_linear_fwd (Y is bit-identical to its Y).
+ */
+int qlora_linear_fwd_save(const void *X, int64_t M, const qlora_nf4_weight *W,
+                          const float *A, const float *B, int32_t r, float scale,
+                          void *Y, void *Hs, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * qlora_linear_bwd with the adapter activations Hs of qlora_linear_fwd_save
+ * (same X, A and scale; bf16 [M, r], device, read only): the backward then
+ * does not read X to form them again (X is still read for dA). Results as
+ * qlora_linear_bwd up to the order of fp32 sums in H (the forward and the
+ * backward split the reduction over K differently); with the Hs of the same
+ * forward the call is deterministic. r must be at least 1.
+ */
+int qlora_linear_bwd_saved(const void *dY, const void *X, const void *Hs, int64_t M,
+                           const qlora_nf4_weight *W, const float *A, const float *B,
+                           int32_t r, float scale, void *dX, float *dA, float *dB,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
  * qlora_linear_fwd without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation). The same kernels and results as
@@ -231,6 +260,10 @@ int qlora_linear_bwd(const void *dY, const void *X, int64_t M, const qlora_nf4_w
  * the call allocates nothing. Sizes whose forward needs more scratch than
  * that fail with QLORA_ERR_WORKSPACE before anything is launched (every
  * M <= 32 call of the 7B and 65B shapes fits, and M = 4096 at 4096 x 4096).
+ * Where qlora_linear_fwd splits the GEMM's reduction into fp32 partials (few
+ * output tiles, M up to about 2048) and they would not fit, this call runs
+ * the reduction in one pass: Y then differs from qlora_linear_fwd's in the
+ * order of the fp32 sums only.
  * Every call on one GPU uses that GPU's array: calls that overlap on one GPU
  * (two streams, two threads) race and must not be issued; calls ordered on
  * one stream are safe. Arguments and errors as qlora_linear_fwd.

@@ -175,6 +175,21 @@ int main(void) {
   REJ(qlora_linear_bwd(dY, X, M, &w, A, B, r, 2.0f, dX, dA, dB, ws, 16, NULL));
   REACH(qlora_linear_bwd(dY, X, M, &w, A, B, r, 2.0f, dX, dA, dB, ws, lws, NULL));
 
+  /* forward that keeps the adapter activations, backward that takes them */
+  {
+    void *Hs = data + 393216;
+    REJ(qlora_linear_fwd_save(X, M, &w, A, B, r, 2.0f, Y, NULL, ws, lws, NULL));
+    REJ(qlora_linear_fwd_save(X, M, &w, A, B, r, 2.0f, Y, (char *)Hs + 2, ws, lws, NULL));
+    REJ(qlora_linear_fwd_save(X, M, &w, NULL, NULL, 0, 0.0f, Y, Hs, ws, lws, NULL));
+    REJ(qlora_linear_fwd_save(X, M, &w, A, B, r, 2.0f, Y, Hs, ws, lws - 1, NULL));
+    REACH(qlora_linear_fwd_save(X, M, &w, A, B, r, 2.0f, Y, Hs, ws, lws, NULL));
+    REJ(qlora_linear_bwd_saved(dY, X, NULL, M, &w, A, B, r, 2.0f, dX, dA, dB, ws, lws, NULL));
+    REJ(qlora_linear_bwd_saved(dY, X, Hs, M, &w, NULL, NULL, 0, 2.0f, dX, NULL, NULL, ws, lws, NULL));
+    REJ(qlora_linear_bwd_saved(dY, X, Hs, M, &w, A, B, r, 2.0f, dX, NULL, dB, ws, lws, NULL));
+    REJ(qlora_linear_bwd_saved(dY, X, Hs, M, &w, A, B, r, 2.0f, dX, dA, dB, ws, 16, NULL));
+    REACH(qlora_linear_bwd_saved(dY, X, Hs, M, &w, A, B, r, 2.0f, dX, dA, dB, ws, lws, NULL));
+  }
+
   /* allocation-free forward: the scratch limit, then a call that fits */
   {
     qlora_nf4_weight small = weight(64, 64, QLORA_FMT_NF4_DQ, pool);

@@ -41,11 +41,12 @@ hipError_t noalloc_scratch(void **ptr) {
   *ptr = fake;
   return hipSuccess;
 }
-hipError_t linear_fwd(const LinearArgs &, const void *, const float *, const float *, void *, void *, hipStream_t, bool) {
+hipError_t linear_fwd(const LinearArgs &, const void *, const float *, const float *, void *, void *, hipStream_t, bool,
+                      void *) {
   return reached();
 }
 hipError_t linear_bwd(const LinearArgs &, const void *, const void *, const float *, const float *, void *, float *,
-                      float *, void *, hipStream_t) {
+                      float *, void *, hipStream_t, const void *) {
   return reached();
 }
 size_t merge_ws_bytes(int64_t N, int64_t K, int r) { return static_cast<size_t>(N + K + r) * 16; }

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(qb.EXPORTED_SYMBOLS) == names
@@ -189,6 +189,18 @@ def test_linear_rejects_bad_arguments():
     assert b(FAKE, FAKE, 16, ref(w), None, None, 0, 2.0, FAKE, FAKE, None, FAKE, big, None) == -2
     assert b(None, FAKE, 16, ref(w), FAKE, FAKE, 8, 2.0, FAKE, FAKE, FAKE, FAKE, big, None) == -1
     assert "dY, X and dX" in qb.qlora_last_error()
+    fs = lib.qlora_linear_fwd_save
+    assert fs(FAKE, 16, ref(w), FAKE, FAKE, 8, 2.0, FAKE, None, FAKE, big, None) == -1
+    assert "Hs" in qb.qlora_last_error()
+    assert fs(FAKE, 16, ref(w), None, None, 0, 0.0, FAKE, FAKE, FAKE, big, None) == -2
+    assert fs(FAKE, 16, ref(w), FAKE, FAKE, 8, 2.0, FAKE, FAKE + 2, FAKE, big, None) == -6
+    assert fs(FAKE, 16, ref(w), FAKE, FAKE, 8, 2.0, FAKE, FAKE, FAKE, 10, None) == -4
+    bs = lib.qlora_linear_bwd_saved
+    assert bs(FAKE, FAKE, None, 16, ref(w), FAKE, FAKE, 8, 2.0, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    assert bs(FAKE, FAKE, FAKE, 16, ref(w), None, None, 0, 2.0, FAKE, None, None, FAKE, big, None) == -2
+    assert bs(FAKE, FAKE, FAKE + 2, 16, ref(w), FAKE, FAKE, 8, 2.0, FAKE, FAKE, FAKE, FAKE, big, None) == -6
+    assert bs(FAKE, FAKE, FAKE, 16, ref(w), FAKE, FAKE, 8, 2.0, FAKE, None, FAKE, FAKE, big, None) == -1
+    assert bs(FAKE, FAKE, FAKE, 16, ref(w), FAKE, FAKE, 8, 2.0, FAKE, FAKE, FAKE, FAKE, 16, None) == -4
 
 
 @pytest.mark.parametrize("rows,cols", [(64, (1 << 23) + 64), ((1 << 23) + 64, 64)])
@@ -218,6 +230,8 @@ def test_binding_rejects_host_tensors_before_any_call():
         qb.qlora_linear_fwd(X, W)
     with pytest.raises(TypeError):
         qb.qlora_linear_bwd(X, X, W)
+    with pytest.raises(TypeError):
+        qb.qlora_linear_fwd_save(X, W, None, None, 0.0)
     with pytest.raises(TypeError):
         qb.qlora_nf4_quantize(torch.zeros((64, 64)))
     with pytest.raises(TypeError):

@@ -1,4 +1,5 @@
-"""GPU parity of qlora_linear_fwd / qlora_linear_bwd against the fp64 oracle.
+"""GPU parity of qlora_linear_fwd / qlora_linear_bwd (and the variants that
+keep and reuse the adapter activations) against the fp64 oracle.
 
 Bar (relative Frobenius error against the oracle evaluated on the exact
 inputs: bf16 X and dY, the oracle's fp32 dequantized weight, fp32 A and B):
@@ -208,6 +209,55 @@ def test_identity_input_exact_with_split_reduction(qb, cb):
             dY = torch.eye(N, dtype=torch.bfloat16, device="cuda")
             dX, _, _ = qb.qlora_linear_bwd(dY, torch.zeros((N, K), dtype=torch.bfloat16, device="cuda"), q)
             assert np.array_equal(gu.host_bf16_bits(dX), nf4.f32_to_bf16_rne(What))
+
+
+def _saved(qb, c, label):
+    """qlora_linear_fwd_save / qlora_linear_bwd_saved: Y bit-identical to
+    qlora_linear_fwd's; Hs = bf16(s X A^T) against the oracle's fp64 down
+    projection (bf16 rounding only: regression bound); the backward from Hs
+    against the oracle like qlora_linear_bwd, and repeatable bit for bit.
+    With fewer than 64 values of H (M r < 64) dA and dB are scaled copies of
+    a few dot products, whose relative error can exceed the regression bound
+    by chance; the 2e-2 bar still holds there."""
+    wl = c.wl
+    reg = REG if wl.M * wl.r >= 64 else TOL
+    gu.announce(f"fwd_save/bwd_saved {label} M={wl.M} N={wl.N} K={wl.K} r={wl.r}")
+    Y0 = qb.qlora_linear_fwd(c.X, c.q, c.A, c.B, wl.s)
+    Y, Hs = qb.qlora_linear_fwd_save(c.X, c.q, c.A, c.B, wl.s)
+    assert np.array_equal(gu.host_bf16_bits(Y), gu.host_bf16_bits(Y0)), f"{label}: Y differs from qlora_linear_fwd"
+    Hr = wl.s * linear.lora_down(c.X32, wl.A)
+    e = gu.rel_fro(gu.host_bf16_f32(Hs), Hr)
+    assert e <= reg, f"{label}: Hs rel err {e}"
+    rX, rA, rB = linear.backward(c.dY32, c.X32, c.What, wl.A, wl.B, wl.s)
+    outs = []
+    for _ in range(2):
+        dX, dA, dB = qb.qlora_linear_bwd_saved(c.dY, c.X, Hs, c.q, c.A, c.B, wl.s)
+        outs.append((gu.host_bf16_bits(dX), gu.host(dA), gu.host(dB)))
+        for k, got, ref in (("dX", gu.host_bf16_f32(dX), rX), ("dA", gu.host(dA), rA), ("dB", gu.host(dB), rB)):
+            e = gu.rel_fro(got, ref)
+            assert e <= (REG if k == "dX" else reg), f"{label}: saved {k} rel err {e}"
+            et = gu.max_tile_rel(got, ref)
+            assert et <= TOL, f"{label}: saved {k} worst tile rel err {et}"
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{label}: saved backward not repeatable"
+
+
+@pytest.mark.parametrize("M", [1, 17, 33, 300])
+@pytest.mark.parametrize("r", [1, 8, 64, 72])
+def test_saved_activations_ragged(qb, cb, M, r):
+    """The saved-activation forward and backward with ragged M (the decode
+    path for M <= 32, the large-tile path above), ranks below, at and above
+    one 64-column adapter tile (r not a multiple of 64: the caller's [M, r]
+    is padded to the kernels' width and back)."""
+    wl = synth.make_linear_workload("saved", M=M, N=320, K=448, r=r, alpha=16.0,
+                                    seed=9000 + M * 10 + r, w_dtype="bf16")
+    _saved(qb, Case(qb, wl, cb), f"saved M={M} r={r}")
+
+
+def test_saved_activations_attn7b(qb, cb):
+    """The 7B attention projection at full size (M = 4096, r = 64: the caller's
+    Hs is used in place by the GEMMs)."""
+    _saved(qb, Case(qb, synth.workload("attn7b"), cb), "attn7b")
 
 
 def test_zero_scale_and_zero_adapter(qb, cb):
