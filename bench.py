@@ -339,12 +339,15 @@ def main():
     dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     dA = torch.empty((r, K), dtype=torch.float32, device=dev)
     dB = torch.empty((N, r), dtype=torch.float32, device=dev)
+    Hs = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
 
+    # The forward keeps the adapter activations bf16(s X A^T) for the
+    # backward, as a training step keeps its activations.
     def step():
         qb.qlora_nf4_quantize(W, out=q, ws=ws_q)
         qb.qlora_nf4_dequantize(q, torch.bfloat16, out=Wdq)
-        qb.qlora_linear_fwd(X, q, A, B, s, ws=ws_l, out=Y)
-        qb.qlora_linear_bwd(dY, X, q, A, B, s, ws=ws_l, outs=(dX, dA, dB))
+        qb.qlora_linear_fwd_save(X, q, A, B, s, ws=ws_l, out=Y, hs=Hs)
+        qb.qlora_linear_bwd_saved(dY, X, Hs, q, A, B, s, ws=ws_l, outs=(dX, dA, dB))
 
     for _ in range(args.warmup):
         step()
@@ -361,7 +364,7 @@ def main():
     t1 = time.perf_counter()
     qb.qlora_profile_enable(False)
     ms_step_eager = (t1 - t0) * 1e3 / args.steps
-    eager_out = [t.clone() for t in (q.codes, q.absmax_q, q.dq_scale, q.dq_mean, Wdq, Y, dX, dA, dB)]
+    eager_out = [t.clone() for t in (q.codes, q.absmax_q, q.dq_scale, q.dq_mean, Wdq, Y, Hs, dX, dA, dB)]
 
     # The same step captured once as a HIP graph and replayed: one launch per
     # step instead of one per kernel. Every replay must reproduce the eager
@@ -376,12 +379,12 @@ def main():
             torch.cuda.synchronize()
             graph_ok = True
             for _ in range(3):
-                for t in (Y, dX, dA, dB, Wdq):
+                for t in (Y, Hs, dX, dA, dB, Wdq):
                     t.zero_()
                 torch.cuda.synchronize()
                 graph.replay()
                 torch.cuda.synchronize()
-                outs = (q.codes, q.absmax_q, q.dq_scale, q.dq_mean, Wdq, Y, dX, dA, dB)
+                outs = (q.codes, q.absmax_q, q.dq_scale, q.dq_mean, Wdq, Y, Hs, dX, dA, dB)
                 graph_ok = graph_ok and all(torch.equal(a, b) for a, b in zip(outs, eager_out))
             if graph_ok:
                 for _ in range(args.warmup):
