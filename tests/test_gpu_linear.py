@@ -243,12 +243,13 @@ def _saved(qb, c, label):
 
 
 @pytest.mark.parametrize("M", [1, 17, 33, 300])
-@pytest.mark.parametrize("r", [1, 8, 64, 72])
+@pytest.mark.parametrize("r", [1, 8, 64, 72, 256])
 def test_saved_activations_ragged(qb, cb, M, r):
     """The saved-activation forward and backward with ragged M (the decode
     path for M <= 32, the large-tile path above), ranks below, at and above
     one 64-column adapter tile (r not a multiple of 64: the caller's [M, r]
-    is padded to the kernels' width and back)."""
+    is padded to the kernels' width and back) up to the largest accepted
+    rank."""
     wl = synth.make_linear_workload("saved", M=M, N=320, K=448, r=r, alpha=16.0,
                                     seed=9000 + M * 10 + r, w_dtype="bf16")
     _saved(qb, Case(qb, wl, cb), f"saved M={M} r={r}")
@@ -318,12 +319,15 @@ def test_mlp65b_sampled(qb, cb, name):
 
 
 @pytest.mark.parametrize("M", [16, 300])
-def test_graph_replays_match_eager(qb, cb, M):
+@pytest.mark.parametrize("saved", [False, True])
+def test_graph_replays_match_eager(qb, cb, M, saved):
     """The whole path captured as one HIP graph (quantize, dequantize, forward,
-    backward; M = 16 takes the decode kernels, M = 300 the large-tile ones) and
-    replayed three times, with the outputs cleared and eager work on the same
-    stream between replays: every replay reproduces the eager results bit for
-    bit (the library allocates and clears nothing inside a call)."""
+    backward; M = 16 takes the decode kernels, M = 300 the large-tile ones;
+    with `saved` the forward keeps the adapter activations and the backward
+    takes them) and replayed three times, with the outputs cleared and eager
+    work on the same stream between replays: every replay reproduces the eager
+    results bit for bit (the library allocates and clears nothing inside a
+    call)."""
     import torch
     wl = synth.make_linear_workload("graph", M=M, N=320, K=448, r=72, alpha=16.0, seed=4000 + M, w_dtype="bf16")
     dev = torch.device("cuda:0")
@@ -338,15 +342,20 @@ def test_graph_replays_match_eager(qb, cb, M):
     dX = torch.empty((M, wl.K), dtype=torch.bfloat16, device=dev)
     dA = torch.empty((wl.r, wl.K), dtype=torch.float32, device=dev)
     dB = torch.empty((wl.N, wl.r), dtype=torch.float32, device=dev)
+    Hs = torch.zeros((M, wl.r), dtype=torch.bfloat16, device=dev)   # untouched unless saved
 
     def step():
         qb.qlora_nf4_quantize(W, out=q, ws=ws_q)
         qb.qlora_nf4_dequantize(q, torch.bfloat16, out=Wd)
-        qb.qlora_linear_fwd(X, q, A, B, wl.s, ws=ws_l, out=Y)
-        qb.qlora_linear_bwd(dY, X, q, A, B, wl.s, ws=ws_l, outs=(dX, dA, dB))
+        if saved:
+            qb.qlora_linear_fwd_save(X, q, A, B, wl.s, ws=ws_l, out=Y, hs=Hs)
+            qb.qlora_linear_bwd_saved(dY, X, Hs, q, A, B, wl.s, ws=ws_l, outs=(dX, dA, dB))
+        else:
+            qb.qlora_linear_fwd(X, q, A, B, wl.s, ws=ws_l, out=Y)
+            qb.qlora_linear_bwd(dY, X, q, A, B, wl.s, ws=ws_l, outs=(dX, dA, dB))
 
-    gu.announce(f"graph capture M={M}")
-    outs = (q.codes, q.absmax_q, q.dq_scale, q.dq_mean, Wd, Y, dX, dA, dB)
+    gu.announce(f"graph capture M={M} saved={saved}")
+    outs = (q.codes, q.absmax_q, q.dq_scale, q.dq_mean, Wd, Y, Hs, dX, dA, dB)
     step()
     torch.cuda.synchronize()
     eager = [t.clone() for t in outs]
@@ -361,7 +370,8 @@ def test_graph_replays_match_eager(qb, cb, M):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for name, a, b in zip(("codes", "absmax_q", "dq_scale", "dq_mean", "Wd", "Y", "dX", "dA", "dB"), outs, eager):
+        for name, a, b in zip(("codes", "absmax_q", "dq_scale", "dq_mean", "Wd", "Y", "Hs", "dX", "dA", "dB"), outs,
+                              eager):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager result"
 
 
