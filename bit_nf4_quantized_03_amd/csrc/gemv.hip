@@ -648,7 +648,10 @@ constexpr int kRsMaxChunks = 64 * 8;           // K <= 16384: at most 8 waves pe
 constexpr int kRsCus = 256;                    // compute units of the GPU
 constexpr int kRsXBytes = 16384 * 2;           // X row in LDS (K <= 16384)
 constexpr int kRsMaxBlocks = 4096;             // blocks of a workgroup's rows (c_b in LDS)
-constexpr int kRsLdsTotal = kRsLds + kRsXBytes + kRsMaxBlocks * 4;   // 112 KB of dynamic LDS
+// 112 KB of LDS, declared static: the table's address is then a constant of
+// the kernel, and each lookup address goes to the LDS read as it is (with the
+// array declared extern, every lookup paid one more add of its base)
+constexpr int kRsLdsTotal = kRsLds + kRsXBytes + kRsMaxBlocks * 4;
 constexpr int kRsHword0 = 256;                 // sync word of the H slots: [Gw][r] fp32 bits, 0 = not yet published
 
 __device__ __forceinline__ float *rs_aux(char *smem, int i) {
@@ -671,7 +674,7 @@ __device__ __forceinline__ float div127(float s) {
 
 template <bool kDq>
 __global__ __launch_bounds__(kRsThreads) void k_gemv_rows(GemvParams p) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];   // kRsLdsTotal bytes
+  __shared__ __attribute__((aligned(16))) char smem[kRsLdsTotal];
   constexpr int NP = kRsPasses;   // passes per workgroup at most
   constexpr int D = 2;            // passes in flight
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1113,10 +1116,7 @@ void launch_mt(int nq, bool dq, unsigned grid, size_t lds, hipStream_t s, const 
 
 template <bool kDq>
 void launch_rows(unsigned grid, hipStream_t s, const GemvParams &p) {
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_rows<kDq>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kRsLdsTotal);
-  (void)attr;
-  hipLaunchKernelGGL((k_gemv_rows<kDq>), dim3(grid), dim3(kRsThreads), kRsLdsTotal, s, p);
+  hipLaunchKernelGGL((k_gemv_rows<kDq>), dim3(grid), dim3(kRsThreads), 0, s, p);
 }
 
 size_t part_bytes(const GemvPlan &pl, int64_t M) {
