@@ -885,7 +885,7 @@ __global__ __launch_bounds__(kRsThreads) void k_gemv_rows(GemvParams p) {
     __syncthreads();
   };
 
-  // ---- passes: 4 accumulators per pass (one per code word); after pass 1
+  // ---- passes: one accumulator per pass; after pass 1
   // the adapter columns (their X and A requests were issued before the
   // passes', so they have arrived); then the reduce-scatter of the 8 sums
   const uint32_t lane4 = 4u * static_cast<uint32_t>(lane & 31);
@@ -899,11 +899,13 @@ __global__ __launch_bounds__(kRsThreads) void k_gemv_rows(GemvParams p) {
       const uint4 c = cw[slot];
       const int rl = i * P + rs;
       const float cb = cs[jon && rl < rows ? rl * kb + (j >> 1) : 0];
-      float sq[4];
+      // one accumulator for the chunk's 16 pairs (four per code word): no
+      // zeroing or combining of partial sums, and the SIMD's other waves
+      // cover the chain's latency
+      float s = 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t wq = q == 0 ? c.x : q == 1 ? c.y : q == 2 ? c.z : c.w;
-        float s = 0.0f;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const uint32_t addr = __builtin_amdgcn_perm(wq, lane4, 0x0C0C0400u | (static_cast<uint32_t>(bb) << 8));
@@ -911,9 +913,8 @@ __global__ __launch_bounds__(kRsThreads) void k_gemv_rows(GemvParams p) {
           s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr), __builtin_bit_cast(bf16x2_t, xr[4 * q + bb]),
                                               s, false);
         }
-        sq[q] = s;
       }
-      v[i] = cb * ((sq[0] + sq[1]) + (sq[2] + sq[3]));
+      v[i] = cb * s;
     }
     issue(i + D);
     if (i == 1 && b < p.r) {   // workgroup-uniform: it owns adapter columns
