@@ -672,11 +672,14 @@ __device__ __forceinline__ float div127(float s) {
   return __builtin_fmaf(__builtin_fmaf(-q0, 127.0f, s), c, q0);
 }
 
-template <bool kDq>
+// D passes in flight: 3 without an adapter, 2 with one (where the adapter's
+// requests and columns share the start of the call, a third pass in flight
+// made the gate/up shape slower)
+template <bool kDq, int D>
 __global__ __launch_bounds__(kRsThreads) void k_gemv_rows(GemvParams p) {
   __shared__ __attribute__((aligned(16))) char smem[kRsLdsTotal];
   constexpr int NP = kRsPasses;   // passes per workgroup at most
-  constexpr int D = 2;            // passes in flight
+  static_assert(D >= 1 && D <= NP, "passes in flight");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nw = p.rs_nw, P = p.rs_P, RW = p.rs_RW, Gw = p.S;
   const int C = static_cast<int>(p.K / 32);
@@ -1117,7 +1120,8 @@ void launch_mt(int nq, bool dq, unsigned grid, size_t lds, hipStream_t s, const 
 
 template <bool kDq>
 void launch_rows(unsigned grid, hipStream_t s, const GemvParams &p) {
-  hipLaunchKernelGGL((k_gemv_rows<kDq>), dim3(grid), dim3(kRsThreads), 0, s, p);
+  if (p.r > 0) hipLaunchKernelGGL((k_gemv_rows<kDq, 2>), dim3(grid), dim3(kRsThreads), 0, s, p);
+  else hipLaunchKernelGGL((k_gemv_rows<kDq, 3>), dim3(grid), dim3(kRsThreads), 0, s, p);
 }
 
 size_t part_bytes(const GemvPlan &pl, int64_t M) {
