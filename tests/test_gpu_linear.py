@@ -255,6 +255,15 @@ def test_saved_activations_ragged(qb, cb, M, r):
     _saved(qb, Case(qb, wl, cb), f"saved M={M} r={r}")
 
 
+@pytest.mark.parametrize("M,N,K,r", [(128, 512, 2048, 72), (100, 832, 2048, 64)])
+def test_saved_activations_with_split_reduction(qb, cb, M, N, K, r):
+    """The saved pair where the forward and dX GEMMs split their reduction
+    (few output tiles): the caller's Hs feeds split 0's adapter steps."""
+    wl = synth.make_linear_workload("saved-split", M=M, N=N, K=K, r=r, alpha=16.0, seed=9500 + M + r,
+                                    w_dtype="bf16")
+    _saved(qb, Case(qb, wl, cb), f"saved split M={M} N={N} K={K} r={r}")
+
+
 def test_saved_activations_attn7b(qb, cb):
     """The 7B attention projection at full size (M = 4096, r = 64: the caller's
     Hs is used in place by the GEMMs)."""
